@@ -1,0 +1,16 @@
+"""CPU oracle for MLA paged decode.  Test infrastructure: only the tests, the
+smoke check and the benchmark's CPU-baseline leg use it."""
+from .reference import (  # noqa: F401
+    absorb_q,
+    bf16_to_f64,
+    combine_partials,
+    decode_rows,
+    e4m3fn_value,
+    e8m0_value,
+    latent_attention,
+    mla_decode,
+    out_proj,
+    row_bytes,
+    sequence_rows,
+    to_f64,
+)
