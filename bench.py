@@ -1,0 +1,198 @@
+"""Benchmark: MLA decode over a paged latent cache on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch:
+mla_absorb_q -> mla_decode_paged (plan, split-KV kernel, LSE merge) ->
+mla_out_proj, on synthetic seeded inputs already resident in HBM.
+
+The default workload is one GLM-4.7-Flash layer: batch 32, 20 heads, 4096
+cached tokens per sequence, bf16 latent cache (512 + 64 values per token),
+page block 64, permuted block table.  Its 151 MB cache would sit in the
+256 MB Infinity Cache if one buffer were reused, so the step cycles through
+several copies of the cache (as successive layers would), each at its own
+address, totalling more than the cache size.
+
+Output: one JSON line with query-tokens/s for the whole step, the achieved
+HBM bandwidth of the decode call (latent bytes read / its average duration,
+HIP events on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode query-tokens/s and achieved HBM GB/s (% of 8 TB/s) at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle (unabsorbed, float64) on whole sequences of the same
+    workload until about target_s seconds of work have run."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synth import make_inputs
+
+    inp = make_inputs(wl)
+    t0 = time.perf_counter()
+    done = 0
+    for b in range(wl.batch):
+        oracle.mla_decode(inp, seqs=[b])
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    qtok = done * wl.q_per_seq
+    return {
+        "value": qtok / dt,
+        "unit": "query-tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {wl.batch} sequences of {wl.name} ({int(np.sum(inp.seq_lens[:done]))} "
+                  f"cached tokens), unabsorbed float64 numpy oracle, {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="glm_b32_h20_ctx4096_bf16")
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="split-KV chunks per sequence (0 = balanced; default: the workload's)")
+    ap.add_argument("--kernel", choices=["auto", "simt", "mfma"], default="auto")
+    ap.add_argument("--cache-bytes", type=float, default=1.0e9,
+                    help="total bytes of rotated cache copies (>= 4x the Infinity Cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path: sequences would shard across GPUs with no exchange, see the design notes.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_amd as mla
+    from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
+    from synth import WORKLOADS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mla.lib()
+    wl = WORKLOADS[args.workload]
+    splits = wl.num_splits if args.num_splits is None else args.num_splits
+    kernel = {"auto": mla.MLA_KERNEL_AUTO, "simt": mla.MLA_KERNEL_SIMT, "mfma": mla.MLA_KERNEL_MFMA}[args.kernel]
+    qd = mla.MLA_BF16 if wl.kv_format == "fp8_e4m3_e8m0" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
+
+    log(f"[bench] generating {wl.name}")
+    inp = make_inputs(wl)
+    dev = DeviceBatch.upload(inp)
+    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel)
+    pool_bytes = dev.kv_pool.numel()
+    copies = max(1, math.ceil(args.cache_bytes / pool_bytes))
+    pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
+    log(f"[bench] {copies} cache copies of {pool_bytes / 1e6:.1f} MB")
+
+    latent_bytes = int(np.sum(inp.seq_lens.astype(np.int64))) * inp.row_bytes
+    unique_bytes = pool_bytes  # every page of the pool is referenced once or more
+    q_tokens = wl.n_tokens
+
+    def one_step(i, ev=None):
+        step.params.kv_pool = pools[i % copies].data_ptr()
+        step.absorb()
+        if ev is not None:
+            ev[0].record()
+        step.decode()
+        if ev is not None:
+            ev[1].record()
+        step.project()
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        one_step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    decode_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = total_ms / args.steps
+    decode_avg_s = sum(decode_ms) / len(decode_ms) / 1e3
+    achieved = latent_bytes / decode_avg_s / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode call "
+        f"{decode_avg_s * 1e6:.1f} us, {achieved:.0f} GB/s")
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        base = cpu_baseline(wl, args.cpu_seconds)
+
+    qtok_s = q_tokens / (ms_per_step / 1e3)
+    used = mla.mla_decode_select_kernel(step.params)
+    compute = "f32" if used == mla.MLA_KERNEL_SIMT else "bf16"
+    line = {
+        "metric": METRIC,
+        "value": qtok_s,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": compute,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_per_seq": wl.q_per_seq,
+            "context": list(wl.lens), "page_block": wl.page_block, "kv_format": wl.kv_format,
+            "d_latent": wl.d_latent, "d_rope": wl.d_rope, "num_splits": splits,
+            "kernel": {1: "simt", 2: "mfma"}[used], "cache_copies": copies,
+        },
+        "hbm_gbs": achieved,
+        "pct_of_8tbs": 100.0 * achieved / HBM_PEAK_GBS,
+        "decode_call_us": decode_avg_s * 1e6,
+        "latent_bytes": latent_bytes,
+        "unique_bytes": unique_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+        },
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

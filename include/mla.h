@@ -1,0 +1,189 @@
+/*
+ * libmla: multi-head latent attention (MLA) decode over a paged latent KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  GLM-4.7-Flash uses DeepSeek-V2 style MLA with the weights
+ * kv_a_proj_with_mqa and kv_b_proj (model record "GLM-4.7-Flash", config
+ * facts; vLLM pull request "fix: Add glm4_moe_lite to MLA detection",
+ * Summary).  Its cache holds, per token and layer, one shared low-rank latent
+ * c_t (kv_lora_rank = 512 values) followed by a decoupled RoPE key k^R_t (64
+ * values): 576 values, 1,152 bytes in bf16 (model record, "SERVICEABILITY
+ * JOIN" and the kv_cache_bytes_per_token formula).  An fp8 variant stores 512
+ * e4m3 values, RoPE dims included, plus one e8m0 scale byte per 32 values,
+ * 528 bytes per token (model record, ENGINE KERNEL CONSTRAINTS item (2));
+ * with 64 RoPE dims that leaves a 448-wide latent.  Decode kernels are built
+ * per page-block size (same list, item (1)); this library takes the page
+ * block as an argument.
+ *
+ * kv_b_proj is stored per head as [d_nope + d_v][d_latent]: rows 0..d_nope-1
+ * are W_UK^h (key half), rows d_nope..d_nope+d_v-1 are W_UV^h (value half).
+ * The query head is d_nope + d_rope = 192 + 64 and the value head d_v = 256
+ * (model record, "head_dim FILLED = 256").
+ *
+ * A decode step is three calls, in the absorbed form:
+ *   mla_absorb_q      q_abs^h = [ (W_UK^h)^T q^{N,h} , q^{R,h} ]
+ *   mla_decode_paged  o_lat^h = sum_t softmax_t(scale <q_abs^h,[c_t,k^R_t]>) c_t
+ *                     (split-KV over the token range + log-sum-exp merge)
+ *   mla_out_proj      o^h     = W_UV^h o_lat^h
+ * which equals softmax attention with K^h_t = [W_UK^h c_t, k^R_t] and
+ * V^h_t = W_UV^h c_t.
+ *
+ * Conventions for every call:
+ *  - Pointers are device pointers owned by the caller.  The library
+ *    allocates nothing, frees nothing and keeps no state between calls.
+ *  - Inputs are read only; outputs are overwritten in full.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous on it and never synchronise with the host.
+ *  - Everything checkable on the host is checked before any launch.  A
+ *    failed check returns a non-zero status and sets a thread-local message
+ *    of the form "<argument>: expected <X>, got <Y>"; nothing is launched.
+ *  - Values that live on the device (seq_lens, block_table) are trusted:
+ *    block_table entries for logical pages [0, ceil(seq_len/page_block))
+ *    must lie in [0, num_pages) and seq_lens must be in
+ *    [0, max_blocks_per_seq * page_block].  Entries past a sequence's last
+ *    page are never read.
+ */
+#ifndef LIBMLA_MLA_H
+#define LIBMLA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
+
+/* Cache row formats.  Row = [latent (d_latent) | RoPE key (d_rope)].
+ *  MLA_KV_F32            4 bytes per value   (2,304 B at 512 + 64)
+ *  MLA_KV_BF16           2 bytes per value   (1,152 B at 512 + 64)
+ *  MLA_KV_FP8_E4M3_E8M0  d_latent + d_rope e4m3fn bytes, then one e8m0 byte
+ *                        per 32 values; value = e4m3fn * 2^(E - 127)
+ *                        (528 B at 448 + 64). */
+typedef enum {
+  MLA_KV_F32 = 0,
+  MLA_KV_BF16 = 1,
+  MLA_KV_FP8_E4M3_E8M0 = 2
+} mla_kv_format_t;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_POINTER = 1,
+  MLA_ERR_INVALID_SHAPE = 2,
+  MLA_ERR_UNSUPPORTED = 3,
+  MLA_ERR_ALIGNMENT = 4,
+  MLA_ERR_WORKSPACE_TOO_SMALL = 5,
+  MLA_ERR_HIP = 6
+} mla_status_t;
+
+/* Per-layer attention dimensions.  Supported: 1 <= num_heads <= 128,
+ * d_rope = 64, d_nope and d_v multiples of 32 in [32, 512], d_latent = 512
+ * (f32 / bf16 cache) or 448 (fp8 cache). */
+typedef struct {
+  int32_t num_heads;
+  int32_t d_latent; /* kv_lora_rank, the shared latent width d_c */
+  int32_t d_rope;   /* qk_rope_head_dim */
+  int32_t d_nope;   /* qk_nope_head_dim */
+  int32_t d_v;      /* v_head_dim */
+} mla_dims_t;
+
+/* Bytes of one cached row in `format`, or 0 if dims/format are invalid. */
+size_t mla_kv_row_bytes(const mla_dims_t* dims, mla_kv_format_t format);
+
+/* Fold the no-RoPE part of the query into latent space.
+ *   q       [n_tokens][H][d_nope + d_rope]      q_dtype (F32 or BF16)
+ *   w_kv_b  [H][d_nope + d_v][d_latent]         w_dtype (F32 or BF16)
+ *   q_abs   [n_tokens][H][d_latent + d_rope]    q_abs_dtype (F32 or BF16)
+ * q_abs[n][h][c] = sum_k w_kv_b[h][k][c] * q[n][h][k] for k < d_nope
+ * (accumulated in fp32), and q_abs[n][h][d_latent + i] = q[n][h][d_nope + i].
+ * Source of the step: the key half of kv_b_proj (model record, SERVICEABILITY
+ * JOIN: kv_b_proj) applied to the query instead of to every cached token.
+ * All pointers 16-byte aligned.  n_tokens = 0 is a no-op. */
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_tokens,
+                          const void* q, mla_dtype_t q_dtype,
+                          const void* w_kv_b, mla_dtype_t w_dtype,
+                          void* q_abs, mla_dtype_t q_abs_dtype, void* stream);
+
+/* Kernel choice for mla_decode_paged. */
+typedef enum {
+  MLA_KERNEL_AUTO = 0, /* MFMA kernel where supported, else SIMT */
+  MLA_KERNEL_SIMT = 1, /* fp32 vector-ALU kernel, every format */
+  MLA_KERNEL_MFMA = 2  /* matrix-core kernel; MLA_ERR_UNSUPPORTED if not */
+} mla_kernel_t;
+
+typedef struct {
+  mla_dims_t dims;
+  int32_t batch;     /* B >= 0 sequences */
+  int32_t q_per_seq; /* Sq in [1, 8]; the Sq new tokens are the last Sq
+                        cached ones and attend causally among themselves */
+  const void* q_abs; /* [B][Sq][H][d_latent + d_rope]; F32 = full precision,
+                        BF16 = single-rounded queries */
+  mla_dtype_t q_abs_dtype;
+  const void* kv_pool; /* [num_pages][page_block][row_bytes], 16-B aligned */
+  mla_kv_format_t kv_format;
+  int64_t num_pages;
+  int32_t page_block;           /* tokens per page: 16, 32, 64 or 128 */
+  const int32_t* block_table;   /* [B][max_blocks_per_seq] physical page ids */
+  int32_t max_blocks_per_seq;
+  const int32_t* seq_lens;      /* [B] cached tokens per sequence, incl. Sq */
+  float softmax_scale;
+  int32_t num_splits;  /* >= 1: each sequence cut into num_splits equal
+                          contiguous chunks; 0: balanced, chunks of whole
+                          tiles spread evenly over a fixed worker count */
+  mla_kernel_t kernel;
+  void* workspace;     /* scratch of mla_decode_workspace_size() bytes,
+                          16-B aligned; contents need no initialisation */
+  size_t workspace_bytes;
+  void* o_latent;      /* out: [B][Sq][H][d_latent], F32 */
+  mla_dtype_t o_dtype;
+  float* lse;          /* out (optional, may be NULL): [B][Sq][H], natural
+                          log of the softmax denominator */
+} mla_decode_params_t;
+
+/* Workspace bytes mla_decode_paged needs for these parameters.  Reads only
+ * host scalars (no pointers are dereferenced, no device is touched). */
+mla_status_t mla_decode_workspace_size(const mla_decode_params_t* p, size_t* bytes);
+
+/* Which kernel mla_decode_paged would run for these parameters
+ * (MLA_KERNEL_SIMT or MLA_KERNEL_MFMA); host scalars only. */
+mla_status_t mla_decode_select_kernel(const mla_decode_params_t* p, mla_kernel_t* chosen);
+
+/* Paged MLA decode.  For sequence b (length L = seq_lens[b]) and query j in
+ * [0, Sq), row r = j*H + h attends to cached tokens t in [0, L - Sq + j]:
+ *   s_t   = softmax_scale * < q_abs[b][j][h], row_t >   (all d_latent + d_rope)
+ *   o_lat = sum_t softmax(s)_t * latent_t ,  lse = log sum_t exp(s_t)
+ * where token t is read from page block_table[b][t / page_block], slot
+ * t % page_block.  A row with no visible token gets o_lat = 0, lse = -inf.
+ * The token range is split into chunks (num_splits), each chunk's partial
+ * result is written to the workspace, and a log-sum-exp merge produces the
+ * outputs.  Source of the operation: model record "GLM-4.7-Flash",
+ * SERVICEABILITY JOIN (the required MLA decode kernel class over the latent
+ * plus RoPE-key cache) and ENGINE KERNEL CONSTRAINTS (1)-(2) (page-block
+ * size and fp8 row format).  Errors: see the conventions above. */
+mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
+
+/* Value up-projection.
+ *   o_latent [n_tokens][H][d_latent]    F32
+ *   w_kv_b   [H][d_nope + d_v][d_latent] w_dtype (F32 or BF16)
+ *   out      [n_tokens][H][d_v]         out_dtype (F32)
+ * out[n][h][v] = sum_c w_kv_b[h][d_nope + v][c] * o_latent[n][h][c], with
+ * fp32 accumulation.  Source: the value half of kv_b_proj (model record,
+ * SERVICEABILITY JOIN), applied once per query instead of per token. */
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens,
+                          const void* o_latent, mla_dtype_t o_dtype,
+                          const void* w_kv_b, mla_dtype_t w_dtype,
+                          void* out, mla_dtype_t out_dtype, void* stream);
+
+const char* mla_status_string(mla_status_t status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* mla_last_error_message(void);
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMLA_MLA_H */

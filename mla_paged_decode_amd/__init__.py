@@ -1,0 +1,203 @@
+"""Python binding of libmla (MLA decode over a paged latent KV cache, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libmla.so.  Tensors are passed by device pointer (``data_ptr()``); integers
+are taken as raw device addresses.  The stream defaults to torch's current
+stream.  A non-zero status raises :class:`MlaError` carrying the library's
+"<argument>: expected X, got Y" message.
+
+There is no fallback: if libmla.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "MlaError", "Dims", "DecodeParams", "lib", "library_path",
+    "mla_kv_row_bytes", "mla_absorb_q", "mla_decode_workspace_size",
+    "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_abi_version",
+    "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0",
+    "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
+]
+
+MLA_F32, MLA_BF16 = 0, 1
+MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0 = 0, 1, 2
+MLA_KERNEL_AUTO, MLA_KERNEL_SIMT, MLA_KERNEL_MFMA = 0, 1, 2
+KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0}
+
+STATUS = {
+    0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",
+    3: "MLA_ERR_UNSUPPORTED", 4: "MLA_ERR_ALIGNMENT",
+    5: "MLA_ERR_WORKSPACE_TOO_SMALL", 6: "MLA_ERR_HIP",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmla.so")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+                ("d_v", ctypes.c_int32)]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("dims", Dims),
+        ("batch", ctypes.c_int32),
+        ("q_per_seq", ctypes.c_int32),
+        ("q_abs", ctypes.c_void_p),
+        ("q_abs_dtype", ctypes.c_int),
+        ("kv_pool", ctypes.c_void_p),
+        ("kv_format", ctypes.c_int),
+        ("num_pages", ctypes.c_int64),
+        ("page_block", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("num_splits", ctypes.c_int32),
+        ("kernel", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("o_latent", ctypes.c_void_p),
+        ("o_dtype", ctypes.c_int),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run `python -m mla_paged_decode_amd.build`")
+        L = ctypes.CDLL(library_path)
+        vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+        L.mla_kv_row_bytes.argtypes = [ctypes.POINTER(Dims), st]
+        L.mla_kv_row_bytes.restype = ctypes.c_size_t
+        L.mla_absorb_q.argtypes = [ctypes.POINTER(Dims), i32, vp, st, vp, st, vp, st, vp]
+        L.mla_absorb_q.restype = st
+        L.mla_out_proj.argtypes = [ctypes.POINTER(Dims), i32, vp, st, vp, st, vp, st, vp]
+        L.mla_out_proj.restype = st
+        L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode_workspace_size.restype = st
+        L.mla_decode_select_kernel.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(ctypes.c_int)]
+        L.mla_decode_select_kernel.restype = st
+        L.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeParams), vp]
+        L.mla_decode_paged.restype = st
+        L.mla_status_string.argtypes = [st]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_last_error_message.argtypes = []
+        L.mla_last_error_message.restype = ctypes.c_char_p
+        L.mla_abi_version.argtypes = []
+        L.mla_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MlaError(status, lib().mla_last_error_message().decode())
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _dtype_code(x, explicit: Optional[int] = None) -> int:
+    if explicit is not None:
+        return explicit
+    import torch
+    if x.dtype == torch.float32:
+        return MLA_F32
+    if x.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MLA_BF16
+    raise TypeError(f"unsupported tensor dtype {x.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _dims(dims) -> Dims:
+    if isinstance(dims, Dims):
+        return dims
+    return Dims(*dims)
+
+
+def mla_abi_version() -> int:
+    return int(lib().mla_abi_version())
+
+
+def mla_kv_row_bytes(dims, kv_format: int) -> int:
+    return int(lib().mla_kv_row_bytes(ctypes.byref(_dims(dims)), kv_format))
+
+
+def mla_absorb_q(dims, n_tokens: int, q, w_kv_b, q_abs, *, q_dtype=None, w_dtype=None,
+                 q_abs_dtype=None, stream=None) -> None:
+    _check(lib().mla_absorb_q(ctypes.byref(_dims(dims)), n_tokens,
+                              _ptr(q), _dtype_code(q, q_dtype),
+                              _ptr(w_kv_b), _dtype_code(w_kv_b, w_dtype),
+                              _ptr(q_abs), _dtype_code(q_abs, q_abs_dtype), _stream(stream)))
+
+
+def mla_out_proj(dims, n_tokens: int, o_latent, w_kv_b, out, *, w_dtype=None, stream=None) -> None:
+    _check(lib().mla_out_proj(ctypes.byref(_dims(dims)), n_tokens,
+                              _ptr(o_latent), MLA_F32, _ptr(w_kv_b), _dtype_code(w_kv_b, w_dtype),
+                              _ptr(out), MLA_F32, _stream(stream)))
+
+
+def make_decode_params(*, dims, batch, q_per_seq, q_abs, kv_pool, kv_format, num_pages,
+                       page_block, block_table, max_blocks_per_seq, seq_lens, softmax_scale,
+                       num_splits=0, kernel=MLA_KERNEL_AUTO, workspace=None, workspace_bytes=0,
+                       o_latent=None, lse=None, q_abs_dtype=None) -> DecodeParams:
+    """Fill the C parameter struct (pointers from tensors or raw ints)."""
+    qd = q_abs_dtype if q_abs_dtype is not None else (
+        _dtype_code(q_abs) if not isinstance(q_abs, int) and q_abs is not None else MLA_F32)
+    return DecodeParams(
+        dims=_dims(dims), batch=batch, q_per_seq=q_per_seq,
+        q_abs=_ptr(q_abs), q_abs_dtype=qd,
+        kv_pool=_ptr(kv_pool), kv_format=kv_format, num_pages=num_pages,
+        page_block=page_block, block_table=_ptr(block_table),
+        max_blocks_per_seq=max_blocks_per_seq, seq_lens=_ptr(seq_lens),
+        softmax_scale=softmax_scale, num_splits=num_splits, kernel=kernel,
+        workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
+        o_latent=_ptr(o_latent), o_dtype=MLA_F32, lse=_ptr(lse))
+
+
+def mla_decode_workspace_size(params: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_decode_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_decode_select_kernel(params: DecodeParams) -> int:
+    k = ctypes.c_int(0)
+    _check(lib().mla_decode_select_kernel(ctypes.byref(params), ctypes.byref(k)))
+    return int(k.value)
+
+
+def mla_decode_paged(params: DecodeParams, stream=None) -> None:
+    _check(lib().mla_decode_paged(ctypes.byref(params), _stream(stream)))

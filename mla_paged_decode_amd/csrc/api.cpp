@@ -1,0 +1,311 @@
+// C-ABI host layer of libmla: argument validation, workspace layout, kernel
+// selection and launches.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+#include "mla.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status_t fail(mla_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+mla_status_t ok() {
+  g_last_error.clear();
+  return MLA_OK;
+}
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape checks common to all calls.  `d_latent_required` = 0 accepts any
+// multiple of 32 in [32, 512].
+mla_status_t check_dims(const mla_dims_t* d, int d_latent_required) {
+  if (!d) return fail(MLA_ERR_NULL_POINTER, "dims: expected non-null, got NULL");
+  if (d->num_heads < 1 || d->num_heads > 128)
+    return fail(MLA_ERR_INVALID_SHAPE, "num_heads: expected 1..128, got %d", d->num_heads);
+  if (d->d_rope != 64)
+    return fail(MLA_ERR_UNSUPPORTED, "d_rope: expected 64, got %d", d->d_rope);
+  if (d->d_nope < 32 || d->d_nope > 512 || d->d_nope % 32)
+    return fail(MLA_ERR_UNSUPPORTED, "d_nope: expected a multiple of 32 in [32, 512], got %d", d->d_nope);
+  if (d->d_v < 32 || d->d_v > 512 || d->d_v % 32)
+    return fail(MLA_ERR_UNSUPPORTED, "d_v: expected a multiple of 32 in [32, 512], got %d", d->d_v);
+  if (d_latent_required) {
+    if (d->d_latent != d_latent_required)
+      return fail(MLA_ERR_UNSUPPORTED, "d_latent: expected %d for this kv_format, got %d",
+                  d_latent_required, d->d_latent);
+  } else if (d->d_latent < 32 || d->d_latent > 512 || d->d_latent % 32) {
+    return fail(MLA_ERR_UNSUPPORTED, "d_latent: expected a multiple of 32 in [32, 512], got %d",
+                d->d_latent);
+  }
+  return MLA_OK;
+}
+
+bool valid_dtype(int t) { return t == MLA_F32 || t == MLA_BF16; }
+
+int latent_for_format(int fmt) { return fmt == MLA_KV_FP8_E4M3_E8M0 ? 448 : 512; }
+
+mla_status_t check_decode_scalars(const mla_decode_params_t* p) {
+  if (!p) return fail(MLA_ERR_NULL_POINTER, "params: expected non-null, got NULL");
+  if (p->kv_format != MLA_KV_F32 && p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8_E4M3_E8M0)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16) or 2 (fp8 e4m3+e8m0), got %d",
+                (int)p->kv_format);
+  mla_status_t st = check_dims(&p->dims, latent_for_format(p->kv_format));
+  if (st) return st;
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_SHAPE, "batch: expected >= 0, got %d", p->batch);
+  if (p->q_per_seq < 1 || p->q_per_seq > 8)
+    return fail(MLA_ERR_UNSUPPORTED, "q_per_seq: expected 1..8, got %d", p->q_per_seq);
+  const int P = p->page_block;
+  if (P != 16 && P != 32 && P != 64 && P != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "page_block: expected one of {16,32,64,128}, got %d", P);
+  if (p->num_pages < 1) return fail(MLA_ERR_INVALID_SHAPE, "num_pages: expected >= 1, got %lld",
+                                    (long long)p->num_pages);
+  if (p->max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_SHAPE, "max_blocks_per_seq: expected >= 1, got %d", p->max_blocks_per_seq);
+  if (p->num_splits < 0 || p->num_splits > 4096)
+    return fail(MLA_ERR_INVALID_SHAPE, "num_splits: expected 0 (balanced) or 1..4096, got %d", p->num_splits);
+  if ((int64_t)p->batch * (p->num_splits ? p->num_splits : 1) > 0x7fffffffLL)
+    return fail(MLA_ERR_INVALID_SHAPE, "batch * num_splits: expected < 2^31, got %lld",
+                (long long)p->batch * p->num_splits);
+  if (!valid_dtype(p->q_abs_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "q_abs_dtype: expected 0 (f32) or 1 (bf16), got %d", (int)p->q_abs_dtype);
+  if (p->o_dtype != MLA_F32)
+    return fail(MLA_ERR_UNSUPPORTED, "o_dtype: expected 0 (f32), got %d", (int)p->o_dtype);
+  if (p->kernel != MLA_KERNEL_AUTO && p->kernel != MLA_KERNEL_SIMT && p->kernel != MLA_KERNEL_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED, "kernel: expected 0 (auto), 1 (simt) or 2 (mfma), got %d", (int)p->kernel);
+  if (!std::isfinite(p->softmax_scale))
+    return fail(MLA_ERR_INVALID_SHAPE, "softmax_scale: expected a finite value, got %g", (double)p->softmax_scale);
+  return MLA_OK;
+}
+
+// Kernel choice for validated scalars.
+mla_status_t select_kernel(const mla_decode_params_t* p, mla_kernel_t* chosen) {
+  const int R = p->q_per_seq * p->dims.num_heads;
+  const bool mfma_ok = mla::decode_mfma_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope, R,
+                                                  p->q_abs_dtype == MLA_F32);
+  if (p->kernel == MLA_KERNEL_MFMA && !mfma_ok)
+    return fail(MLA_ERR_UNSUPPORTED, "kernel: MFMA path does not support kv_format %d with %d query rows",
+                (int)p->kv_format, R);
+  *chosen = (p->kernel == MLA_KERNEL_SIMT || !mfma_ok) ? MLA_KERNEL_SIMT : MLA_KERNEL_MFMA;
+  return MLA_OK;
+}
+
+mla_status_t hip_fail(const char* what, hipError_t e) {
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+namespace mla {
+
+WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
+  WorkspaceLayout w{};
+  w.slots = num_splits > 0 ? (int64_t)B * num_splits : (int64_t)kBalancedWorkers + B;
+  w.tile_start_off = 0;
+  size_t off = round_up(sizeof(int32_t) * ((size_t)B + 1), 256);
+  w.part_lse_off = off;
+  off = round_up(off + sizeof(float) * (size_t)w.slots * R, 256);
+  w.part_o_off = off;
+  off = round_up(off + sizeof(float) * (size_t)w.slots * R * dc, 256);
+  w.total = off;
+  return w;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL_POINTER: return "MLA_ERR_NULL_POINTER";
+    case MLA_ERR_INVALID_SHAPE: return "MLA_ERR_INVALID_SHAPE";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t mla_kv_row_bytes(const mla_dims_t* dims, mla_kv_format_t format) {
+  if (!dims || dims->d_latent < 1 || dims->d_rope < 0) return 0;
+  const size_t n = (size_t)dims->d_latent + dims->d_rope;
+  switch (format) {
+    case MLA_KV_F32: return 4 * n;
+    case MLA_KV_BF16: return 2 * n;
+    case MLA_KV_FP8_E4M3_E8M0: return n % 32 ? 0 : n + n / 32;
+  }
+  return 0;
+}
+
+mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t n_tokens, const void* q, mla_dtype_t q_dtype,
+                          const void* w_kv_b, mla_dtype_t w_dtype, void* q_abs, mla_dtype_t q_abs_dtype,
+                          void* stream) {
+  mla_status_t st = check_dims(dims, 0);
+  if (st) return st;
+  if (n_tokens < 0) return fail(MLA_ERR_INVALID_SHAPE, "n_tokens: expected >= 0, got %d", n_tokens);
+  if (!valid_dtype(q_dtype)) return fail(MLA_ERR_UNSUPPORTED, "q_dtype: expected 0 or 1, got %d", (int)q_dtype);
+  if (!valid_dtype(w_dtype)) return fail(MLA_ERR_UNSUPPORTED, "w_dtype: expected 0 or 1, got %d", (int)w_dtype);
+  if (!valid_dtype(q_abs_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "q_abs_dtype: expected 0 or 1, got %d", (int)q_abs_dtype);
+  if (n_tokens == 0) return ok();
+  if (!q) return fail(MLA_ERR_NULL_POINTER, "q: expected non-null, got NULL");
+  if (!w_kv_b) return fail(MLA_ERR_NULL_POINTER, "w_kv_b: expected non-null, got NULL");
+  if (!q_abs) return fail(MLA_ERR_NULL_POINTER, "q_abs: expected non-null, got NULL");
+  if (!aligned(q, 16) || !aligned(w_kv_b, 16) || !aligned(q_abs, 16))
+    return fail(MLA_ERR_ALIGNMENT, "q/w_kv_b/q_abs: expected 16-byte aligned pointers, got %p/%p/%p", q,
+                w_kv_b, q_abs);
+  mla::ProjArgs a{};
+  a.N = n_tokens;
+  a.H = dims->num_heads;
+  a.dn = dims->d_nope;
+  a.dr = dims->d_rope;
+  a.dv = dims->d_v;
+  a.dc = dims->d_latent;
+  a.in = q;
+  a.in_f32 = q_dtype == MLA_F32;
+  a.w = w_kv_b;
+  a.w_f32 = w_dtype == MLA_F32;
+  a.out = q_abs;
+  a.out_f32 = q_abs_dtype == MLA_F32;
+  hipError_t e = mla::launch_absorb_q(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mla_absorb_q launch", e);
+  return ok();
+}
+
+mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens, const void* o_latent, mla_dtype_t o_dtype,
+                          const void* w_kv_b, mla_dtype_t w_dtype, void* out, mla_dtype_t out_dtype,
+                          void* stream) {
+  mla_status_t st = check_dims(dims, 0);
+  if (st) return st;
+  if (n_tokens < 0) return fail(MLA_ERR_INVALID_SHAPE, "n_tokens: expected >= 0, got %d", n_tokens);
+  if (o_dtype != MLA_F32) return fail(MLA_ERR_UNSUPPORTED, "o_dtype: expected 0 (f32), got %d", (int)o_dtype);
+  if (!valid_dtype(w_dtype)) return fail(MLA_ERR_UNSUPPORTED, "w_dtype: expected 0 or 1, got %d", (int)w_dtype);
+  if (out_dtype != MLA_F32)
+    return fail(MLA_ERR_UNSUPPORTED, "out_dtype: expected 0 (f32), got %d", (int)out_dtype);
+  if (n_tokens == 0) return ok();
+  if (!o_latent) return fail(MLA_ERR_NULL_POINTER, "o_latent: expected non-null, got NULL");
+  if (!w_kv_b) return fail(MLA_ERR_NULL_POINTER, "w_kv_b: expected non-null, got NULL");
+  if (!out) return fail(MLA_ERR_NULL_POINTER, "out: expected non-null, got NULL");
+  if (!aligned(o_latent, 16) || !aligned(w_kv_b, 16) || !aligned(out, 16))
+    return fail(MLA_ERR_ALIGNMENT, "o_latent/w_kv_b/out: expected 16-byte aligned pointers, got %p/%p/%p",
+                o_latent, w_kv_b, out);
+  mla::ProjArgs a{};
+  a.N = n_tokens;
+  a.H = dims->num_heads;
+  a.dn = dims->d_nope;
+  a.dr = dims->d_rope;
+  a.dv = dims->d_v;
+  a.dc = dims->d_latent;
+  a.in = o_latent;
+  a.in_f32 = 1;
+  a.w = w_kv_b;
+  a.w_f32 = w_dtype == MLA_F32;
+  a.out = out;
+  a.out_f32 = 1;
+  hipError_t e = mla::launch_out_proj(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mla_out_proj launch", e);
+  return ok();
+}
+
+mla_status_t mla_decode_workspace_size(const mla_decode_params_t* p, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
+  mla_status_t st = check_decode_scalars(p);
+  if (st) return st;
+  const int R = p->q_per_seq * p->dims.num_heads;
+  *bytes = mla::workspace_layout(p->batch, R, p->dims.d_latent, p->num_splits).total;
+  return ok();
+}
+
+mla_status_t mla_decode_select_kernel(const mla_decode_params_t* p, mla_kernel_t* chosen) {
+  if (!chosen) return fail(MLA_ERR_NULL_POINTER, "chosen: expected non-null, got NULL");
+  mla_status_t st = check_decode_scalars(p);
+  if (st) return st;
+  if ((st = select_kernel(p, chosen)) != MLA_OK) return st;
+  return ok();
+}
+
+mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
+  mla_status_t st = check_decode_scalars(p);
+  if (st) return st;
+  const int B = p->batch, H = p->dims.num_heads, R = p->q_per_seq * H;
+  const int dc = p->dims.d_latent, dr = p->dims.d_rope;
+  const int fmt = p->kv_format;
+  const int q_f32 = p->q_abs_dtype == MLA_F32;
+  mla_kernel_t chosen;
+  if ((st = select_kernel(p, &chosen)) != MLA_OK) return st;
+  const bool use_mfma = chosen == MLA_KERNEL_MFMA;
+  if (B == 0) return ok();
+  const struct {
+    const void* ptr;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{p->q_abs, "q_abs", 16},           {p->kv_pool, "kv_pool", 16},
+              {p->block_table, "block_table", 4}, {p->seq_lens, "seq_lens", 4},
+              {p->workspace, "workspace", 16},    {p->o_latent, "o_latent", 16}};
+  for (const auto& x : ptrs) {
+    if (!x.ptr) return fail(MLA_ERR_NULL_POINTER, "%s: expected non-null, got NULL", x.name);
+    if (!aligned(x.ptr, x.align))
+      return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
+  }
+  if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
+  const mla::WorkspaceLayout w = mla::workspace_layout(B, R, dc, p->num_splits);
+  if (p->workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
+                p->workspace_bytes);
+
+  mla::DecodeArgs a{};
+  a.B = B;
+  a.Sq = p->q_per_seq;
+  a.H = H;
+  a.R = R;
+  a.dc = dc;
+  a.dr = dr;
+  a.q_abs = p->q_abs;
+  a.q_f32 = q_f32;
+  a.pool = static_cast<const uint8_t*>(p->kv_pool);
+  a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
+  a.P = p->page_block;
+  a.block_table = p->block_table;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.seq_lens = p->seq_lens;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.num_splits = p->num_splits;
+  a.workers = mla::kBalancedWorkers;
+  char* ws = static_cast<char*>(p->workspace);
+  a.tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start_off);
+  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse_off);
+  a.part_o = reinterpret_cast<float*>(ws + w.part_o_off);
+  a.o = static_cast<float*>(p->o_latent);
+  a.lse = p->lse;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (a.num_splits == 0 && (e = mla::launch_plan(a, s)) != hipSuccess) return hip_fail("plan launch", e);
+  e = use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
+  if (e != hipSuccess) return hip_fail("decode launch", e);
+  if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);
+  return ok();
+}
+
+}  // extern "C"

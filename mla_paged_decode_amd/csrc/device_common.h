@@ -1,0 +1,40 @@
+// Device helpers: storage-format conversions used by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mla {
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// OCP e4m3fn byte -> float: 1 sign, 4 exponent bits (bias 7), 3 mantissa
+// bits, exponent 0 subnormal, S.1111.111 NaN, no infinities.
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 24;
+  const uint32_t e = (b >> 3) & 0xfu;
+  const uint32_t m = b & 0x7u;
+  if (e == 0xfu && m == 0x7u) return __uint_as_float(0x7fc00000u);
+  if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 0x1p-9f));
+  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// OCP e8m0 scale byte -> 2^(E - 127); 0xff is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  if (e == 0xffu) return __uint_as_float(0x7fc00000u);
+  if (e == 0) return 0x1p-127f;
+  return __uint_as_float(e << 23);
+}
+
+}  // namespace mla

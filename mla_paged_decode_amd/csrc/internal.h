@@ -1,0 +1,67 @@
+// Internal launch interface between the C-ABI host layer (api.cpp) and the
+// HIP kernels.  Everything here is validated by the host layer first.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace mla {
+
+// Tokens per planning tile: balanced split-KV cuts every sequence into tiles
+// of this many tokens and hands each worker a contiguous run of tiles.
+constexpr int kPlanTile = 32;
+// Worker count of balanced mode: two workgroups per compute unit on a
+// 256-CU MI355X, which fills the chip in one pass.
+constexpr int kBalancedWorkers = 512;
+
+enum KvFormat : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+struct DecodeArgs {
+  int B, Sq, H, R;        // R = Sq * H query rows per sequence
+  int dc, dr;             // latent and RoPE widths
+  const void* q_abs;      // [B][R][dc + dr]
+  int q_f32;              // 1: fp32 queries, 0: bf16
+  const uint8_t* pool;    // [pages][P][row_bytes]
+  int64_t row_bytes;
+  int P;
+  const int32_t* block_table;
+  int max_blocks;
+  const int32_t* seq_lens;
+  float scale_log2;       // softmax_scale * log2(e): scores kept in base 2
+  int num_splits;         // >= 1 uniform, 0 balanced
+  int workers;            // balanced: worker count G
+  float* part_o;          // [slots][R][dc]
+  float* part_lse;        // [slots][R], natural log
+  int32_t* tile_start;    // balanced: [B + 1] exclusive prefix of tiles
+  float* o;               // [B][R][dc]
+  float* lse;             // [B][R] or null
+};
+
+// Workspace layout shared by the size query and the launch.
+struct WorkspaceLayout {
+  size_t tile_start_off, part_lse_off, part_o_off, total;
+  int64_t slots;
+};
+WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits);
+
+hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s);
+bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+
+struct ProjArgs {
+  int N, H, dn, dr, dv, dc;
+  const void* in;  // absorb: q [N][H][dn+dr]; out_proj: o [N][H][dc] (f32)
+  int in_f32;
+  const void* w;   // [H][dn+dv][dc]
+  int w_f32;
+  void* out;       // absorb: q_abs [N][H][dc+dr]; out_proj: [N][H][dv] (f32)
+  int out_f32;
+};
+hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t s);
+hipError_t launch_out_proj(const ProjArgs& a, hipStream_t s);
+
+}  // namespace mla

@@ -11,6 +11,8 @@ from .gen import (  # noqa: F401
     Workload,
     bf16_bits_from_f32,
     make_inputs,
+    make_o_latent,
+    make_q_abs,
     quantize_e4m3_e8m0,
     stored_row_bytes,
 )

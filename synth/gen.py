@@ -325,3 +325,23 @@ def make_inputs(
         block_table=table,
         seq_lens=lens,
     )
+
+
+def make_q_abs(wl: Workload, *, seed: Optional[int] = None) -> np.ndarray:
+    """Absorbed queries [B*Sq, H, d_latent + d_rope] float32 for exercising
+    the decode step on its own: the latent part is N(0, d_nope/512) (the
+    spread of W_UK^T q for the weights above), the RoPE part N(0, 1)."""
+    g = _rng(wl.seed if seed is None else seed, 6)
+    N = wl.batch * wl.q_per_seq
+    lat = g.standard_normal((N, wl.heads, wl.d_latent), dtype=np.float32)
+    lat *= np.float32(math.sqrt(wl.d_nope / 512.0))
+    rope = g.standard_normal((N, wl.heads, wl.d_rope), dtype=np.float32)
+    return np.ascontiguousarray(np.concatenate([lat, rope], axis=-1))
+
+
+def make_o_latent(wl: Workload, *, seed: Optional[int] = None) -> np.ndarray:
+    """Latent attention outputs [B*Sq, H, d_latent] float32, N(0, 1/64), for
+    exercising the value up-projection on its own."""
+    g = _rng(wl.seed if seed is None else seed, 7)
+    N = wl.batch * wl.q_per_seq
+    return g.standard_normal((N, wl.heads, wl.d_latent), dtype=np.float32) * np.float32(0.125)

@@ -1,0 +1,130 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+declared entry point, reports row sizes, and rejects every invalid argument
+with its status code and message before touching a device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import mla_paged_decode_amd as mla
+from mla_paged_decode_amd import (MLA_BF16, MLA_F32, MLA_KERNEL_MFMA, MLA_KV_BF16, MLA_KV_F32,
+                                  MLA_KV_FP8_E4M3_E8M0, Dims, MlaError, make_decode_params)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GLM = Dims(20, 512, 64, 192, 256)
+FP8 = Dims(20, 448, 64, 192, 256)
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(mla_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = mla.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert mla.mla_abi_version() == 1
+
+
+def test_row_bytes_match_page_figures(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "page_invariants.json")))
+    assert mla.mla_kv_row_bytes(GLM, MLA_KV_BF16) * g["num_layers"] == g["bf16_bytes_per_token_all_layers"]
+    assert mla.mla_kv_row_bytes(FP8, MLA_KV_FP8_E4M3_E8M0) == g["fp8_row_bytes"]
+    assert mla.mla_kv_row_bytes(GLM, MLA_KV_F32) == 2304
+    assert mla.mla_kv_row_bytes(GLM, 7) == 0
+
+
+def params(**kw):
+    base = dict(dims=GLM, batch=4, q_per_seq=1, q_abs=FAKE, kv_pool=FAKE, kv_format=MLA_KV_BF16,
+                num_pages=100, page_block=64, block_table=FAKE, max_blocks_per_seq=32,
+                seq_lens=FAKE, softmax_scale=0.0625, num_splits=0, workspace=FAKE,
+                workspace_bytes=1 << 40, o_latent=FAKE, lse=None, q_abs_dtype=MLA_F32)
+    base.update(kw)
+    return make_decode_params(**base)
+
+
+def expect_error(fn, status, fragment):
+    with pytest.raises(MlaError) as ei:
+        fn()
+    assert ei.value.status == status, ei.value
+    assert fragment in ei.value.message, ei.value.message
+
+
+@pytest.mark.parametrize("kw,status,fragment", [
+    (dict(page_block=96), 3, "page_block: expected one of {16,32,64,128}, got 96"),
+    (dict(q_per_seq=9), 3, "q_per_seq: expected 1..8, got 9"),
+    (dict(q_per_seq=0), 3, "q_per_seq: expected 1..8, got 0"),
+    (dict(dims=Dims(20, 448, 64, 192, 256)), 3, "d_latent: expected 512 for this kv_format, got 448"),
+    (dict(dims=GLM, kv_format=MLA_KV_FP8_E4M3_E8M0), 3, "d_latent: expected 448 for this kv_format, got 512"),
+    (dict(dims=Dims(20, 512, 32, 192, 256)), 3, "d_rope: expected 64, got 32"),
+    (dict(dims=Dims(129, 512, 64, 192, 256)), 2, "num_heads: expected 1..128, got 129"),
+    (dict(dims=Dims(0, 512, 64, 192, 256)), 2, "num_heads: expected 1..128, got 0"),
+    (dict(dims=Dims(20, 512, 64, 100, 256)), 3, "d_nope: expected a multiple of 32"),
+    (dict(kv_format=5), 3, "kv_format: expected 0 (f32), 1 (bf16) or 2"),
+    (dict(batch=-1), 2, "batch: expected >= 0, got -1"),
+    (dict(num_pages=0), 2, "num_pages: expected >= 1, got 0"),
+    (dict(max_blocks_per_seq=0), 2, "max_blocks_per_seq: expected >= 1, got 0"),
+    (dict(num_splits=-2), 2, "num_splits: expected 0 (balanced) or 1..4096, got -2"),
+    (dict(q_abs_dtype=3), 3, "q_abs_dtype: expected 0 (f32) or 1 (bf16), got 3"),
+    (dict(kernel=9), 3, "kernel: expected 0 (auto), 1 (simt) or 2 (mfma), got 9"),
+    (dict(softmax_scale=float("nan")), 2, "softmax_scale: expected a finite value"),
+    (dict(q_abs=None), 1, "q_abs: expected non-null, got NULL"),
+    (dict(kv_pool=None), 1, "kv_pool: expected non-null, got NULL"),
+    (dict(block_table=None), 1, "block_table: expected non-null, got NULL"),
+    (dict(seq_lens=None), 1, "seq_lens: expected non-null, got NULL"),
+    (dict(workspace=None), 1, "workspace: expected non-null, got NULL"),
+    (dict(o_latent=None), 1, "o_latent: expected non-null, got NULL"),
+    (dict(kv_pool=FAKE + 8), 4, "kv_pool: expected 16-byte alignment"),
+    (dict(q_abs=FAKE + 4), 4, "q_abs: expected 16-byte alignment"),
+    (dict(seq_lens=FAKE + 2), 4, "seq_lens: expected 4-byte alignment"),
+    (dict(lse=FAKE + 1), 4, "lse: expected 4-byte alignment"),
+    (dict(workspace_bytes=100), 5, "workspace_bytes: expected >= "),
+])
+def test_decode_rejects_before_launch(kw, status, fragment):
+    p = params(**kw)
+    expect_error(lambda: mla.mla_decode_paged(p, stream=0), status, fragment)
+
+
+def test_mfma_request_rejected_where_unsupported():
+    p = params(kv_format=MLA_KV_F32, kernel=MLA_KERNEL_MFMA)
+    expect_error(lambda: mla.mla_decode_paged(p, stream=0), 3, "MFMA path does not support")
+    expect_error(lambda: mla.mla_decode_select_kernel(p), 3, "MFMA path does not support")
+    assert mla.mla_decode_select_kernel(params(kv_format=MLA_KV_F32)) == mla.MLA_KERNEL_SIMT
+
+
+def test_workspace_size_is_host_only_and_monotone():
+    small = mla.mla_decode_workspace_size(params(batch=4, num_splits=32))
+    big = mla.mla_decode_workspace_size(params(batch=4, num_splits=64))
+    bal = mla.mla_decode_workspace_size(params(batch=4, num_splits=0))
+    assert 0 < small < big
+    # 4 * 32 partial slots of 20 rows x (512 + 1) floats, plus the plan
+    assert small >= 4 * 32 * 20 * 513 * 4
+    assert bal >= (512 + 4) * 20 * 513 * 4
+    expect_error(lambda: mla.mla_decode_workspace_size(params(page_block=8)), 3, "page_block")
+
+
+def test_empty_batch_and_zero_tokens_are_no_ops():
+    mla.mla_decode_paged(params(batch=0, q_abs=None, kv_pool=None, block_table=None,
+                                seq_lens=None, workspace=None, o_latent=None), stream=0)
+    mla.mla_absorb_q(GLM, 0, 0, 0, 0, q_dtype=MLA_BF16, w_dtype=MLA_BF16, q_abs_dtype=MLA_F32, stream=0)
+    mla.mla_out_proj(GLM, 0, 0, 0, 0, w_dtype=MLA_BF16, stream=0)
+
+
+@pytest.mark.parametrize("call", ["absorb", "out_proj"])
+def test_projection_argument_checks(call):
+    if call == "absorb":
+        f = lambda dims, n, a, b, c, dt=MLA_BF16: mla.mla_absorb_q(dims, n, a, b, c, q_dtype=dt, w_dtype=MLA_BF16,
+                                                                 q_abs_dtype=MLA_F32, stream=0)
+    else:
+        f = lambda dims, n, a, b, c, dt=MLA_BF16: mla.mla_out_proj(dims, n, a, b, c, w_dtype=dt, stream=0)
+    expect_error(lambda: f(GLM, -1, FAKE, FAKE, FAKE), 2, "n_tokens: expected >= 0, got -1")
+    expect_error(lambda: f(GLM, 4, 0, FAKE, FAKE), 1, "expected non-null, got NULL")
+    expect_error(lambda: f(GLM, 4, FAKE + 8, FAKE, FAKE), 4, "expected 16-byte aligned pointers")
+    expect_error(lambda: f(GLM, 4, FAKE, FAKE, FAKE, 7), 3, "expected 0 or 1, got 7")
+    expect_error(lambda: f(Dims(20, 500, 64, 192, 256), 4, FAKE, FAKE, FAKE), 3, "d_latent: expected a multiple of 32")

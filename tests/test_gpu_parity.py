@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Criterion (written here, used everywhere below): with `ref` the oracle's
+float64 result over the compared entries,
+
+    max |gpu - ref| <= tau * RMS(ref)
+
+tau = 1e-2 for bf16 caches and 5e-2 for the fp8 cache on the matrix-core
+path (measured against the oracle on the same dequantised values).  The
+vector-ALU kernels compute in fp32 throughout, so their bound is tighter:
+tau = 1e-4 (fp32 unit roundoff 6e-8 grown by sums of at most ~2e5 terms
+and a 576-term dot product, with margin).  Rows without a visible token must
+give exactly o = 0 and lse = -inf.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, make_inputs, make_o_latent, make_q_abs
+
+pytestmark = pytest.mark.gpu
+
+TAU_BF16, TAU_FP8, TAU_F32 = 1e-2, 5e-2, 1e-4
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_decode_amd as mla
+    mla.lib()  # fail loudly if the library is not built
+
+
+def rel_err(gpu, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    gpu = np.asarray(gpu, dtype=np.float64)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    return float(np.max(np.abs(gpu - ref))) / rms
+
+
+def kernels():
+    from mla_paged_decode_amd import MLA_KERNEL_SIMT
+    return [MLA_KERNEL_SIMT]
+
+
+def run_step(inp, *, kernel, num_splits=0, q_abs_dtype=None, q_abs=None):
+    from mla_paged_decode_amd import MLA_F32
+    from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
+    dev = DeviceBatch.upload(inp)
+    step = DecodeStep(dev, kernel=kernel, num_splits=num_splits,
+                      q_abs_dtype=MLA_F32 if q_abs_dtype is None else q_abs_dtype)
+    step.o_latent.fill_(float("nan"))
+    step.lse.fill_(float("nan"))
+    step.out.fill_(float("nan"))
+    if q_abs is None:
+        step.run()
+    else:
+        step.q_abs.copy_(torch.from_numpy(q_abs))
+        step.decode()
+    torch.cuda.synchronize()
+    return step
+
+
+def check_empty_rows(inp, o, lse):
+    wl = inp.wl
+    for b in range(wl.batch):
+        for j in range(wl.q_per_seq):
+            if int(inp.seq_lens[b]) - wl.q_per_seq + 1 + j <= 0:
+                n = b * wl.q_per_seq + j
+                assert (o[n] == 0).all(), (b, j)
+                assert np.isneginf(lse[n]).all(), (b, j)
+
+
+# ------------------------------------------------------- single steps --
+
+@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16"])
+@pytest.mark.parametrize("out_f32", [True, False])
+def test_absorb_q(name, out_f32):
+    import mla_paged_decode_amd as mla
+    wl = WORKLOADS[name].with_(batch=min(WORKLOADS[name].batch, 8), lens=("const", 16))
+    say(f"[absorb] {name} out_f32={out_f32}")
+    inp = make_inputs(wl)
+    from mla_paged_decode_amd.step import DeviceBatch
+    dev = DeviceBatch.upload(inp)
+    N, H = wl.n_tokens, wl.heads
+    q_abs = torch.full((N, H, wl.d_latent + wl.d_rope), float("nan"),
+                       dtype=torch.float32 if out_f32 else torch.bfloat16, device="cuda")
+    mla.mla_absorb_q(dev.dims, N, dev.q, dev.w_kv_b, q_abs)
+    torch.cuda.synchronize()
+    ref = oracle.absorb_q(oracle.to_f64(inp.q, wl.q_dtype), oracle.to_f64(inp.w_kv_b, wl.w_dtype), wl.d_nope)
+    got = q_abs.float().cpu().numpy()
+    err = rel_err(got, ref)
+    say(f"  rel err {err:.3e}")
+    if out_f32:
+        assert err <= 1e-5
+    else:
+        # one bf16 rounding of the fp32 result: half an ulp, at most 2^-8 relative per
+        # element, plus the fp32 accumulation error
+        rms = math.sqrt(float(np.mean(ref ** 2)))
+        assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms).all()
+
+
+@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16", "fp8_mtp4_b64_h20_ctx16k"])
+def test_out_proj(name):
+    import mla_paged_decode_amd as mla
+    wl = WORKLOADS[name].with_(batch=min(WORKLOADS[name].batch, 8), lens=("const", 16))
+    say(f"[out_proj] {name}")
+    inp = make_inputs(wl)
+    o_lat = make_o_latent(wl)
+    from mla_paged_decode_amd.step import DeviceBatch
+    dev = DeviceBatch.upload(inp)
+    N, H = wl.n_tokens, wl.heads
+    out = torch.full((N, H, wl.d_v), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_out_proj(dev.dims, N, torch.from_numpy(o_lat).cuda(), dev.w_kv_b, out)
+    torch.cuda.synchronize()
+    ref = oracle.out_proj(o_lat.astype(np.float64), oracle.to_f64(inp.w_kv_b, wl.w_dtype), wl.d_nope)
+    err = rel_err(out.cpu().numpy(), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("kernel", kernels())
+@pytest.mark.parametrize("name,lens", [
+    ("tiny_b2_h4_f32", (37, 64)),
+    ("glm_b32_h20_ctx4096_bf16", (1, 31, 32, 33, 100, 700)),
+    ("fp8_mtp4_b64_h20_ctx16k", (4, 3, 66, 300)),
+])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_decode_latent_attention(kernel, name, lens, num_splits):
+    wl = WORKLOADS[name].with_(batch=len(lens), lens=("fixed", lens))
+    say(f"[decode] {name} lens={lens} splits={num_splits} kernel={kernel}")
+    inp = make_inputs(wl, poison_tail=True)
+    q_abs = make_q_abs(wl)
+    step = run_step(inp, kernel=kernel, num_splits=num_splits, q_abs=q_abs)
+    o = step.o_latent.cpu().numpy()
+    lse = step.lse.cpu().numpy()
+    ref_o, ref_lse = oracle.latent_attention(q_abs.astype(np.float64), inp)
+    check_empty_rows(inp, o, lse)
+    fin = np.isfinite(ref_lse)
+    err = rel_err(o[fin], ref_o[fin])
+    lse_err = float(np.max(np.abs(lse[fin] - ref_lse[fin])))
+    say(f"  o rel err {err:.3e}  lse abs err {lse_err:.3e}")
+    assert err <= TAU_F32
+    assert lse_err <= 1e-4
+
+
+# ---------------------------------------------------------- end to end --
+
+@pytest.mark.parametrize("kernel", kernels())
+def test_tiny_end_to_end(kernel):
+    wl = WORKLOADS["tiny_b2_h4_f32"]
+    say(f"[e2e] tiny kernel={kernel}")
+    inp = make_inputs(wl)
+    step = run_step(inp, kernel=kernel)
+    ref, ref_lse = oracle.mla_decode(inp)
+    err = rel_err(step.out.cpu().numpy(), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TAU_F32
+    assert np.max(np.abs(step.lse.cpu().numpy() - ref_lse)) <= 1e-4
+
+
+@pytest.mark.parametrize("kernel", kernels())
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 7, 32])
+def test_split_modes_agree(kernel, num_splits):
+    """Every split count gives the oracle's result (split-KV + LSE merge)."""
+    lens = (1, 5, 64, 129, 1000, 2049)
+    wl = WORKLOADS["ragged_b256_h20_ctx512_8k_bf16"].with_(batch=len(lens), lens=("fixed", lens))
+    say(f"[splits] {num_splits} kernel={kernel}")
+    inp = make_inputs(wl, poison_tail=True)
+    step = run_step(inp, kernel=kernel, num_splits=num_splits)
+    ref, _ = oracle.mla_decode(inp)
+    err = rel_err(step.out.cpu().numpy(), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TAU_F32
+
+
+@pytest.mark.parametrize("kernel", kernels())
+def test_mtp_and_short_sequences(kernel):
+    """Sq = 4 with lengths below, at and just above Sq, and L = 0."""
+    lens = (0, 1, 3, 4, 5, 17, 64, 65)
+    wl = WORKLOADS["fp8_mtp4_b64_h20_ctx16k"].with_(batch=len(lens), lens=("fixed", lens), heads=5)
+    say(f"[mtp-short] kernel={kernel}")
+    inp = make_inputs(wl, poison_tail=True)
+    step = run_step(inp, kernel=kernel)
+    ref, ref_lse = oracle.mla_decode(inp)
+    out, lse = step.out.cpu().numpy(), step.lse.cpu().numpy()
+    check_empty_rows(inp, step.o_latent.cpu().numpy(), lse)
+    assert np.isfinite(out).all()
+    err = rel_err(out, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TAU_F32
+
+
+@pytest.mark.parametrize("kernel", kernels())
+def test_page_layout_invariance_and_determinism(kernel):
+    """Two physical layouts of the same logical cache give identical bits,
+    and rerunning gives identical bits."""
+    lens = (300, 77, 1024)
+    wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=3, lens=("fixed", lens))
+    a = make_inputs(wl)
+    b = make_inputs(wl.with_(permute_pages=False))
+    # b has the same pages in identity order; a's block table permutes them.
+    # Rebuild a's pool so that its permuted tables address b's logical data.
+    pool = np.empty_like(b.kv_pool)
+    for s in range(3):
+        n = (lens[s] + 63) // 64
+        pool[a.block_table[s, :n]] = b.kv_pool[b.block_table[s, :n]]
+    a.kv_pool = pool
+    say(f"[layout] kernel={kernel}")
+    sa = run_step(a, kernel=kernel)
+    sb = run_step(b, kernel=kernel)
+    assert torch.equal(sa.out, sb.out)
+    again = run_step(a, kernel=kernel)
+    assert torch.equal(sa.out, again.out)
+
+
+# ---------------------------------------------- full-size workloads --
+
+FULL = [
+    # (workload, sequences checked against the oracle, heads checked)
+    ("glm_b32_h20_ctx4096_bf16", [0, 17, 31], None),
+    ("long_b4_h20_ctx65k_203k_bf16", [1], [0, 7, 19]),
+    ("ragged_b256_h20_ctx512_8k_bf16", [0, 3, 100, 255], None),
+    ("fp8_mtp4_b64_h20_ctx16k", [0, 63], None),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kernel", kernels())
+@pytest.mark.parametrize("name,seqs,heads", FULL)
+def test_full_size_sampled(kernel, name, seqs, heads):
+    from mla_paged_decode_amd import MLA_BF16, MLA_F32, MLA_KERNEL_SIMT
+    wl = WORKLOADS[name]
+    say(f"[full] {name} kernel={kernel} splits={wl.num_splits}")
+    inp = make_inputs(wl)
+    qd = MLA_F32 if (kernel == MLA_KERNEL_SIMT or wl.kv_format != "fp8_e4m3_e8m0") else MLA_BF16
+    step = run_step(inp, kernel=kernel, num_splits=wl.num_splits, q_abs_dtype=qd)
+    out = step.out.cpu().numpy()
+    assert np.isfinite(out).all()
+    ref, ref_lse = oracle.mla_decode(inp, seqs=seqs, heads=heads)
+    rows = [b * wl.q_per_seq + j for b in seqs for j in range(wl.q_per_seq)]
+    hs = list(range(wl.heads)) if heads is None else heads
+    sel = np.ix_(rows, hs)
+    err = rel_err(out[sel], ref[sel])
+    tau = TAU_F32 if kernel == MLA_KERNEL_SIMT else (TAU_FP8 if wl.kv_format.startswith("fp8") else TAU_BF16)
+    say(f"  rel err {err:.3e} (tau {tau})")
+    assert err <= tau
+    lse = step.lse.cpu().numpy()
+    assert np.max(np.abs(lse[sel] - ref_lse[sel])) <= 1e-3
