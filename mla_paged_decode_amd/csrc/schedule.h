@@ -36,33 +36,67 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* ts, int B, int64_t t) 
   return lo;
 }
 
-// Calls f(b, L, t0, t1, slot) for each unit of this workgroup, uniformly
-// across the workgroup.
+// One work unit: tokens [t0, t1) of sequence b (length L), partial -> slot.
+struct Unit {
+  int b, L, t0, t1;
+  int64_t slot;
+};
+
+// Walks this workgroup's units with a single loop body at the call site:
+//   UnitIter it(a); Unit u; while (it.next(a, u)) { ... }
+// All lanes of the workgroup see the same sequence of units.
+struct UnitIter {
+  int b;          // next sequence to consider (balanced) / done flag (uniform)
+  int64_t tb, te; // this worker's tile range (balanced)
+
+  __device__ __forceinline__ explicit UnitIter(const DecodeArgs& a) {
+    if (a.num_splits > 0) {
+      b = 0;
+      tb = te = 0;
+    } else {
+      const int64_t G = a.workers, N = a.tile_start[a.B], g = blockIdx.x;
+      tb = worker_tile_begin(g, N, G);
+      te = worker_tile_begin(g + 1, N, G);
+      b = tb < te ? seq_of_tile(a.tile_start, a.B, tb) : a.B;
+    }
+  }
+
+  __device__ __forceinline__ bool next(const DecodeArgs& a, Unit& u) {
+    if (a.num_splits > 0) {
+      if (b) return false;
+      b = 1;
+      const int S = a.num_splits;
+      u.b = blockIdx.x / S;
+      const int s = blockIdx.x % S;
+      u.L = max(a.seq_lens[u.b], 0);
+      const int chunk = (u.L + S - 1) / S;
+      u.t0 = min(u.L, s * chunk);
+      u.t1 = min(u.L, u.t0 + chunk);
+      u.slot = blockIdx.x;
+      return true;
+    }
+    for (; b < a.B && a.tile_start[b] < te; ++b) {
+      const int64_t s0 = max(tb, (int64_t)a.tile_start[b]);
+      const int64_t s1 = min(te, (int64_t)a.tile_start[b + 1]);
+      if (s0 >= s1) continue;
+      u.b = b;
+      u.L = max(a.seq_lens[b], 0);
+      u.t0 = (int)((s0 - a.tile_start[b]) * kPlanTile);
+      u.t1 = (int)min((int64_t)u.L, (s1 - a.tile_start[b]) * kPlanTile);
+      u.slot = (int64_t)blockIdx.x + b;
+      ++b;
+      return true;
+    }
+    return false;
+  }
+};
+
+// Calls f(b, L, t0, t1, slot) for each unit of this workgroup.
 template <class F>
 __device__ __forceinline__ void for_each_unit(const DecodeArgs& a, F&& f) {
-  if (a.num_splits > 0) {
-    const int S = a.num_splits;
-    const int b = blockIdx.x / S, s = blockIdx.x % S;
-    const int L = max(a.seq_lens[b], 0);
-    const int chunk = (L + S - 1) / S;
-    const int t0 = min(L, s * chunk);
-    const int t1 = min(L, t0 + chunk);
-    f(b, L, t0, t1, (int64_t)blockIdx.x);
-    return;
-  }
-  const int64_t G = a.workers, N = a.tile_start[a.B];
-  const int64_t g = blockIdx.x;
-  const int64_t tb = worker_tile_begin(g, N, G), te = worker_tile_begin(g + 1, N, G);
-  if (tb >= te) return;
-  for (int b = seq_of_tile(a.tile_start, a.B, tb); b < a.B && a.tile_start[b] < te; ++b) {
-    const int64_t s0 = max(tb, (int64_t)a.tile_start[b]);
-    const int64_t s1 = min(te, (int64_t)a.tile_start[b + 1]);
-    if (s0 >= s1) continue;
-    const int L = max(a.seq_lens[b], 0);
-    const int t0 = (int)((s0 - a.tile_start[b]) * kPlanTile);
-    const int t1 = (int)min((int64_t)L, (s1 - a.tile_start[b]) * kPlanTile);
-    f(b, L, t0, t1, g + b);
-  }
+  UnitIter it(a);
+  Unit u;
+  while (it.next(a, u)) f(u.b, u.L, u.t0, u.t1, u.slot);
 }
 
 }  // namespace mla
