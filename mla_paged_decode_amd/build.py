@@ -27,11 +27,14 @@ SOURCES = [
     "decode_simt.hip",
     "decode_mfma.hip",
     "proj_simt.hip",
+    "proj_mfma.hip",
 ]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # LDS is laid out by hand in every kernel; do not move private arrays there
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -286,6 +286,7 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
   a.pool = static_cast<const uint8_t*>(p->kv_pool);
   a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
   a.P = p->page_block;
+  a.P_log2 = __builtin_ctz((unsigned)p->page_block);
   a.block_table = p->block_table;
   a.max_blocks = p->max_blocks_per_seq;
   a.seq_lens = p->seq_lens;
@@ -299,9 +300,13 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
   a.o = static_cast<float*>(p->o_latent);
   a.lse = p->lse;
 
+  a.plan_in_kernel = use_mfma && B <= mla::kMaxInKernelPlan;
+  if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (a.num_splits == 0 && (e = mla::launch_plan(a, s)) != hipSuccess) return hip_fail("plan launch", e);
+  if (a.num_splits == 0 && !a.plan_in_kernel && (e = mla::launch_plan(a, s)) != hipSuccess)
+    return hip_fail("plan launch", e);
   e = use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
   if (e != hipSuccess) return hip_fail("decode launch", e);
   if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);

@@ -89,34 +89,109 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Physical pages of one 32-token tile: tokens [tt0, tt1) of the current
+// sequence lie in logical pages p0 .. p0+2 at most (page_block >= 16).
+// Loaded with scalar loads, so the vector-memory counter only tracks the
+// tile data itself.
+struct TilePages {
+  int tt0, tt1, p0, pg0, pg1, pg2;
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// The block table is read-only during the call: reading it through the
+// constant address space lets the compiler use scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const_i32_ptr bt, int tt0, int t1) {
+  TilePages r;
+  r.tt0 = tt0;
+  r.tt1 = min(tt0 + kTile, t1);
+  r.p0 = tt0 >> a.P_log2;
+  const int p1 = (r.tt1 - 1) >> a.P_log2;
+  r.pg0 = uniform(bt[r.p0]);
+  r.pg1 = uniform(bt[min(r.p0 + 1, p1)]);
+  r.pg2 = uniform(bt[min(r.p0 + 2, p1)]);
+  // Pin the fields in scalar registers so the struct never lives in memory
+  // (a dynamically indexed copy would add waits on the transfer counter).
+  asm volatile("" : "+s"(r.tt0), "+s"(r.tt1), "+s"(r.p0), "+s"(r.pg0), "+s"(r.pg1), "+s"(r.pg2));
+  return r;
+}
+
+// Row index (page * P + slot) of tile token k; tokens past the end repeat
+// the last valid one.
+__device__ __forceinline__ int64_t tile_row(const DecodeArgs& a, TilePages tp, int k) {
+  const int t = min(tp.tt0 + k, tp.tt1 - 1);
+  const int pi = (t >> a.P_log2) - tp.p0;  // 0, 1 or 2
+  const int page = tp.pg0 + (pi >= 1 ? tp.pg1 - tp.pg0 : 0) + (pi >= 2 ? tp.pg2 - tp.pg1 : 0);
+  return (int64_t)page * a.P + (t & (a.P - 1));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier for LDS hand-off only.  The caller has already waited
+// for its own LDS operations and tile transfers; unlike __syncthreads() this
+// does not drain the tile transfers still in flight for later tiles.  The
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One 16-byte direct-to-LDS load per lane: the wave's 64 chunks land at
+// lds + 16 * lane.  Issued as inline assembly so that the compiler does not
+// treat the pending LDS write as aliasing every LDS read (which would make
+// it drain all transfers before reading the current tile); completion is
+// tracked explicitly with wait_vmcnt_lgkm0.
+__device__ __forceinline__ void dma16(const void* src, const char* lds) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+  uint32_t saved;
+  // m0 holds the LDS destination of the transfer; its previous value is
+  // restored afterwards.
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
 // bf16 tiles go straight from HBM to LDS with 16-byte direct-to-LDS loads.
 // A wave instruction fills 64 consecutive 16-B LDS chunks from per-lane
 // sources: instruction k < 32 is token k's latent row (lane = swizzled
 // chunk, 1 KB contiguous in HBM); the 4 instructions after it carry the
-// RoPE parts of 8 tokens each.
+// RoPE parts of 8 tokens each.  Wave w issues latent rows w, w+NW, ... and
+// RoPE groups w, w+NW, ...; every wave issues at least kMinOps of them.
 template <int NW>
 struct DmaStaging {
   using G = Geo<kBF16>;
-  static constexpr int kInst = kTile + kTile * 8 / 64;  // 32 latent + 4 RoPE
+  static constexpr int kRopeInst = kTile * 8 / 64;  // 4
+  static constexpr int kMinOps = kTile / NW + kRopeInst / NW;
 
-  // `rid` holds in lanes 0..31 the row index of the tile's 32 tokens.
-  // Wave w issues latent rows w, w+NW, ... and RoPE groups w, w+NW, ...
-  __device__ __forceinline__ static void load(const DecodeArgs& a, int rid, char* buf) {
-    typedef __attribute__((address_space(3))) void lds_void;
+  __device__ __forceinline__ static void load(const DecodeArgs& a, TilePages tp, char* buf) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll 1
     for (int k = wave; k < kTile; k += NW) {
-      const int64_t row = __builtin_amdgcn_readlane(rid, k);
-      const uint8_t* src = a.pool + row * a.row_bytes + 16 * (lane ^ swz(k));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + G::kLatRow * k), 16, 0, 0);
+      const uint8_t* src = a.pool + tile_row(a, tp, k) * a.row_bytes + 16 * (lane ^ swz(k));
+      dma16(src, buf + G::kLatRow * k);
     }
 #pragma unroll 1
-    for (int r = wave; r < kInst - kTile; r += NW) {
+    for (int r = wave; r < kRopeInst; r += NW) {
       const int tok = 8 * r + (lane >> 3);
-      const int64_t row = __shfl(rid, tok);
-      const uint8_t* src = a.pool + row * a.row_bytes + 2 * G::kDc + 16 * ((lane & 7) ^ swz(tok));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + G::kRopeBase + 1024 * r), 16, 0, 0);
+      const uint8_t* src = a.pool + tile_row(a, tp, tok) * a.row_bytes + 2 * G::kDc + 16 * ((lane & 7) ^ swz(tok));
+      dma16(src, buf + G::kRopeBase + 1024 * r);
     }
   }
 };
@@ -131,14 +206,13 @@ struct Fp8Staging {
   uint4 v[kPer];
   uint32_t s[kPer];
 
-  __device__ __forceinline__ void load(const DecodeArgs& a, int rid) {
+  __device__ __forceinline__ void load(const DecodeArgs& a, TilePages tp) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = j * kThreads + threadIdx.x;
       const int tok = min(q / G::kSrcChunks, kTile - 1);
       const int c = q % G::kSrcChunks;
-      const int64_t row = __shfl(rid, tok);
-      const uint8_t* p = a.pool + row * a.row_bytes;
+      const uint8_t* p = a.pool + tile_row(a, tp, tok) * a.row_bytes;
       if (q < kSrc) {
         v[j] = *reinterpret_cast<const uint4*>(p + 16 * c);
         s[j] = p[G::kVals + c / 2];
@@ -175,27 +249,45 @@ struct Fp8Staging {
   }
 };
 
-// Uniform staging interface over the two formats.
-template <int FMT, int NW>
+// Staging interface over the two formats.  kDepth tiles are in flight ahead
+// of the one being computed: issue(x) starts tile x's transfer into its ring
+// buffer, finish(x) completes it from registers (fp8), wait(n) blocks until
+// this wave's part of the oldest outstanding tile has landed when n younger
+// tiles have been issued after it.
+template <int FMT, int NW, int NBUF>
 struct Staging;
 
-template <int NW>
-struct Staging<kBF16, NW> {
-  __device__ __forceinline__ void issue(const DecodeArgs& a, int rid, char* buf) { DmaStaging<NW>::load(a, rid, buf); }
+template <int NW, int NBUF>
+struct Staging<kBF16, NW, NBUF> {
+  static constexpr int kDepth = NBUF - 1;
+  __device__ __forceinline__ void issue(const DecodeArgs& a, TilePages tp, char* buf) {
+    DmaStaging<NW>::load(a, tp, buf);
+  }
   __device__ __forceinline__ void finish(char*) {}
+  __device__ __forceinline__ void wait(int younger) {
+    constexpr int M = DmaStaging<NW>::kMinOps;
+    if (younger >= 2) wait_vmcnt_lgkm0<(NBUF >= 4 ? 2 * M : 0)>();
+    else if (younger == 1) wait_vmcnt_lgkm0<(NBUF >= 3 ? M : 0)>();
+    else wait_vmcnt_lgkm0<0>();
+  }
 };
 
-template <int NW>
-struct Staging<kFP8, NW> {
+template <int NW, int NBUF>
+struct Staging<kFP8, NW, NBUF> {
+  static_assert(NBUF == 2, "fp8 tiles are staged through registers, one ahead");
+  static constexpr int kDepth = 1;
   Fp8Staging<NW> f;
-  __device__ __forceinline__ void issue(const DecodeArgs& a, int rid, char*) { f.load(a, rid); }
+  __device__ __forceinline__ void issue(const DecodeArgs& a, TilePages tp, char*) { f.load(a, tp); }
   __device__ __forceinline__ void finish(char* buf) { f.store(buf); }
+  __device__ __forceinline__ void wait(int) { wait_vmcnt_lgkm0<0>(); }
 };
 
-template <int FMT, bool HILO, int NW>
+template <int FMT, bool HILO, int NW, int NBUF>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   using G = Geo<FMT>;
-  __shared__ __attribute__((aligned(16))) char tiles[2][G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char tiles[NBUF][G::kTileBytes];
+  __shared__ int32_t s_ts[kMaxInKernelPlan + 1];
+  __shared__ int32_t s_scan[64 * NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -204,7 +296,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int row = wave * 16 + li;   // this lane's query row (B / P side)
   const bool row_ok = row < a.R;
 
-  for_each_unit(a, [&](int b, int L, int t0, int t1, int64_t slot) {
+  const int32_t* ts = a.tile_start;
+  if (a.num_splits == 0 && a.plan_in_kernel) {
+    block_plan(a.seq_lens, a.B, s_ts, s_scan);
+    if (blockIdx.x == 0)  // publish the plan for the merge kernel
+      for (int i = threadIdx.x; i <= a.B; i += 64 * NW) a.tile_start[i] = s_ts[i];
+    ts = s_ts;
+  }
+  UnitIter unit_it(a, ts);
+  Unit unit;
+  while (unit_it.next(a, unit)) {
+    // The unit is the same for the whole workgroup: keep it in scalar
+    // registers so page lookups below are scalar loads.
+    const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
+    const int64_t slot = a.num_splits > 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x + b;
     // ---- queries in the B-operand layout: column = row, k = 8g..8g+7 ----
     bf16x8 qh[G::kKs], ql[HILO ? G::kKs : 1];
     {
@@ -246,35 +351,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     float m = -INFINITY, lsum = 0.f;
 
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    // Lanes 0..31 own token tile*32 + lane (tokens past t1 stand in for t0,
-    // a valid row).  The page id is loaded one tile early and combined with
-    // the slot only when used, so that no wait on the load is needed before.
-    auto tok_of = [&](int tile) -> int {
-      const int t = t0 + tile * kTile + (lane & 31);
-      return t < t1 ? t : t0;
-    };
-    auto page_of = [&](int tile) -> int {
-      return a.block_table[(int64_t)b * a.max_blocks + tok_of(tile) / a.P];
-    };
-    Staging<FMT, NW> st;
-    int page_next = 0;
+    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+    using St = Staging<FMT, NW, NBUF>;
+    constexpr int D = St::kDepth;
+    St st;
+    TilePages tp_next;  // pages of the next tile to issue, loaded one tile early
     if (ntiles > 0) {
-      const int rid0 = page_of(0) * a.P + tok_of(0) % a.P;
-      if (ntiles > 1) page_next = page_of(1);
-      __syncthreads();  // previous unit's readers of tiles[0] are done
-      st.issue(a, rid0, tiles[0]);
+      wait_vmcnt_lgkm0<0>();
+      lds_barrier();  // the previous unit's readers of the ring are done
+#pragma unroll
+      for (int x = 0; x < D; ++x)
+        if (x < ntiles) st.issue(a, tile_pages(a, bt, t0 + x * kTile, t1), tiles[x]);
+      if (D < ntiles) tp_next = tile_pages(a, bt, t0 + D * kTile, t1);
       st.finish(tiles[0]);
     }
 
     for (int it = 0; it < ntiles; ++it) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into tile `it` landed
-      __syncthreads();                // everyone's did; everyone finished tile it-1
-      const bool more = it + 1 < ntiles;
-      if (more) {
-        st.issue(a, page_next * a.P + tok_of(it + 1) % a.P, tiles[(it + 1) & 1]);
-        if (it + 2 < ntiles) page_next = page_of(it + 2);
+      st.wait(min(D - 1, ntiles - 1 - it));  // this wave's part of tile `it` landed
+      lds_barrier();                          // everyone's did; everyone finished tile it-1
+      const int x = it + D;                   // goes into the buffer tile it-1 used
+      if (x < ntiles) {
+        st.issue(a, tp_next, tiles[x % NBUF]);
+        if (x + 1 < ntiles) tp_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
       }
-      const char* buf = tiles[it & 1];
+      const char* buf = tiles[it % NBUF];
       const int tt0 = t0 + it * kTile;
 
       // ---- S^T = Tile . Q^T for two 16-token blocks ----
@@ -405,7 +505,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      if (more) st.finish(tiles[(it + 1) & 1]);
+      if (D == 1 && it + 1 < ntiles) st.finish(tiles[(it + 1) % NBUF]);
     }
 
     // ---- normalise and write this unit's partial ----
@@ -424,15 +524,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         for (int d = 0; d < G::kDb; ++d) dst[16 * d] = acc[d][i] * inv_r[i];
       }
     }
-  });
+  }
 }
 
 template <int FMT, bool HILO>
 hipError_t launch_nw(const DecodeArgs& a, int nw, hipStream_t s) {
   const unsigned units = a.num_splits > 0 ? (unsigned)(a.B * a.num_splits) : (unsigned)a.workers;
+  constexpr int NBUF = FMT == kBF16 ? kRingBf16 : 2;
   switch (nw) {
 #define MLA_CASE(N) \
-  case N: decode_mfma_kernel<FMT, HILO, N><<<units, 64 * N, 0, s>>>(a); break;
+  case N: decode_mfma_kernel<FMT, HILO, N, NBUF><<<units, 64 * N, 0, s>>>(a); break;
     MLA_CASE(2) MLA_CASE(3) MLA_CASE(4)
     MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
 #undef MLA_CASE

@@ -15,6 +15,13 @@ constexpr int kPlanTile = 32;
 // Worker count of balanced mode: two workgroups per compute unit on a
 // 256-CU MI355X, which fills the chip in one pass.
 constexpr int kBalancedWorkers = 512;
+// LDS ring depth (tile buffers) of the bf16 matrix-core decode kernel and the
+// balanced worker count it runs with (at most kBalancedWorkers).
+constexpr int kRingBf16 = 2;
+constexpr int kMfmaWorkersBf16 = 512;
+// Batches up to this size are planned inside the matrix-core decode kernel
+// (each workgroup scans seq_lens itself); larger ones use the plan kernel.
+constexpr int kMaxInKernelPlan = 512;
 
 enum KvFormat : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
@@ -26,6 +33,7 @@ struct DecodeArgs {
   const uint8_t* pool;    // [pages][P][row_bytes]
   int64_t row_bytes;
   int P;
+  int P_log2;             // page_block = 1 << P_log2
   const int32_t* block_table;
   int max_blocks;
   const int32_t* seq_lens;
@@ -35,6 +43,7 @@ struct DecodeArgs {
   float* part_o;          // [slots][R][dc]
   float* part_lse;        // [slots][R], natural log
   int32_t* tile_start;    // balanced: [B + 1] exclusive prefix of tiles
+  int plan_in_kernel;     // balanced: the decode kernel computes tile_start
   float* o;               // [B][R][dc]
   float* lse;             // [B][R] or null
 };
@@ -61,7 +70,13 @@ struct ProjArgs {
   void* out;       // absorb: q_abs [N][H][dc+dr]; out_proj: [N][H][dv] (f32)
   int out_f32;
 };
+// Dispatchers: matrix-core kernels where the dtypes and shapes allow,
+// vector-ALU kernels otherwise.
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_proj(const ProjArgs& a, hipStream_t s);
+bool absorb_mfma_supported(const ProjArgs& a);
+bool out_proj_mfma_supported(const ProjArgs& a);
+hipError_t launch_absorb_mfma(const ProjArgs& a, hipStream_t s);
+hipError_t launch_out_proj_mfma(const ProjArgs& a, hipStream_t s);
 
 }  // namespace mla

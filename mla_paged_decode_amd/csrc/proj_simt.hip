@@ -107,6 +107,7 @@ __global__ __launch_bounds__(kThreads) void out_proj_simt_kernel(ProjArgs a) {
 
 hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
+  if (absorb_mfma_supported(a)) return launch_absorb_mfma(a, s);
   const dim3 grid((a.N + kTokBlk - 1) / kTokBlk, a.H);
   const int key = (a.in_f32 ? 4 : 0) | (a.w_f32 ? 2 : 0) | (a.out_f32 ? 1 : 0);
   switch (key) {
@@ -124,6 +125,7 @@ hipError_t launch_absorb_q(const ProjArgs& a, hipStream_t s) {
 
 hipError_t launch_out_proj(const ProjArgs& a, hipStream_t s) {
   if (a.N == 0) return hipSuccess;
+  if (out_proj_mfma_supported(a)) return launch_out_proj_mfma(a, s);
   const dim3 grid((a.N + kTokBlk - 1) / kTokBlk, a.H);
   if (a.w_f32) out_proj_simt_kernel<true><<<grid, kThreads, 0, s>>>(a);
   else out_proj_simt_kernel<false><<<grid, kThreads, 0, s>>>(a);

@@ -36,6 +36,33 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* ts, int B, int64_t t) 
   return lo;
 }
 
+// Balanced-mode plan computed by one workgroup: ts[b] = sum over b' < b of
+// ceil(max(L_b', 0) / kPlanTile), ts[B] = total, written to `ts` (LDS or
+// global).  `scan` is LDS scratch of blockDim.x ints.  Contains barriers:
+// every thread of the workgroup must call it.
+__device__ __forceinline__ void block_plan(const int32_t* lens, int B, int32_t* ts, int32_t* scan) {
+  const int nt = blockDim.x, tid = threadIdx.x;
+  const int per = (B + nt - 1) / nt;
+  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
+  int32_t sum = 0;
+  for (int b = b0; b < b1; ++b) sum += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
+  scan[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    const int32_t v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = scan[tid] - sum;
+  for (int b = b0; b < b1; ++b) {
+    ts[b] = run;
+    run += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
+  }
+  if (tid == nt - 1) ts[B] = scan[tid];
+  __syncthreads();
+}
+
 // One work unit: tokens [t0, t1) of sequence b (length L), partial -> slot.
 struct Unit {
   int b, L, t0, t1;
@@ -46,18 +73,19 @@ struct Unit {
 //   UnitIter it(a); Unit u; while (it.next(a, u)) { ... }
 // All lanes of the workgroup see the same sequence of units.
 struct UnitIter {
-  int b;          // next sequence to consider (balanced) / done flag (uniform)
-  int64_t tb, te; // this worker's tile range (balanced)
+  const int32_t* ts;  // tile_start[0..B] (global memory or LDS)
+  int b;              // next sequence to consider (balanced) / done flag (uniform)
+  int64_t tb, te;     // this worker's tile range (balanced)
 
-  __device__ __forceinline__ explicit UnitIter(const DecodeArgs& a) {
+  __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start) : ts(tile_start) {
     if (a.num_splits > 0) {
       b = 0;
       tb = te = 0;
     } else {
-      const int64_t G = a.workers, N = a.tile_start[a.B], g = blockIdx.x;
+      const int64_t G = a.workers, N = ts[a.B], g = blockIdx.x;
       tb = worker_tile_begin(g, N, G);
       te = worker_tile_begin(g + 1, N, G);
-      b = tb < te ? seq_of_tile(a.tile_start, a.B, tb) : a.B;
+      b = tb < te ? seq_of_tile(ts, a.B, tb) : a.B;
     }
   }
 
@@ -75,14 +103,14 @@ struct UnitIter {
       u.slot = blockIdx.x;
       return true;
     }
-    for (; b < a.B && a.tile_start[b] < te; ++b) {
-      const int64_t s0 = max(tb, (int64_t)a.tile_start[b]);
-      const int64_t s1 = min(te, (int64_t)a.tile_start[b + 1]);
+    for (; b < a.B && ts[b] < te; ++b) {
+      const int64_t s0 = max(tb, (int64_t)ts[b]);
+      const int64_t s1 = min(te, (int64_t)ts[b + 1]);
       if (s0 >= s1) continue;
       u.b = b;
       u.L = max(a.seq_lens[b], 0);
-      u.t0 = (int)((s0 - a.tile_start[b]) * kPlanTile);
-      u.t1 = (int)min((int64_t)u.L, (s1 - a.tile_start[b]) * kPlanTile);
+      u.t0 = (int)((s0 - ts[b]) * kPlanTile);
+      u.t1 = (int)min((int64_t)u.L, (s1 - ts[b]) * kPlanTile);
       u.slot = (int64_t)blockIdx.x + b;
       ++b;
       return true;
@@ -94,7 +122,7 @@ struct UnitIter {
 // Calls f(b, L, t0, t1, slot) for each unit of this workgroup.
 template <class F>
 __device__ __forceinline__ void for_each_unit(const DecodeArgs& a, F&& f) {
-  UnitIter it(a);
+  UnitIter it(a, a.tile_start);
   Unit u;
   while (it.next(a, u)) f(u.b, u.L, u.t0, u.t1, u.slot);
 }

@@ -143,7 +143,9 @@ def test_out_proj(name):
     ref = oracle.out_proj(o_lat.astype(np.float64), oracle.to_f64(inp.w_kv_b, wl.w_dtype), wl.d_nope)
     err = rel_err(out.cpu().numpy(), ref)
     say(f"  rel err {err:.3e}")
-    assert err <= 1e-5
+    # matrix-core path: the fp32 input is split into two bf16 parts, which
+    # leaves ~2^-17 relative per product; fp32 path: accumulation only
+    assert err <= (1e-5 if wl.w_dtype == "f32" else 1e-4)
 
 
 @pytest.mark.parametrize("kernel", kernels())
