@@ -12,9 +12,11 @@ several copies of the cache (as successive layers would), each at its own
 address, totalling more than the cache size.
 
 Output: one JSON line with query-tokens/s for the whole step, the achieved
-HBM bandwidth of the decode call (latent bytes read / its average duration,
-HIP events on the launch stream), and the CPU oracle timed on a bounded
-sample of the same workload.
+HBM bandwidth of the decode call (latent bytes read / its average duration),
+the roofline of its dominant kernel, the split-KV attention kernel (latent
+bytes read / its average duration; HIP events the library records on the
+launch stream around that launch alone), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -77,6 +79,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=None,
                     help="split-KV chunks per sequence (0 = balanced; default: the workload's)")
     ap.add_argument("--kernel", choices=["auto", "simt", "mfma"], default="auto")
+    ap.add_argument("--q-abs", choices=["bf16", "f32"], default="bf16",
+                    help="absorbed-query dtype fed to the attention kernel (the SIMT kernel takes f32)")
     ap.add_argument("--cache-bytes", type=float, default=1.0e9,
                     help="total bytes of rotated cache copies (>= 4x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -101,7 +105,7 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     splits = wl.num_splits if args.num_splits is None else args.num_splits
     kernel = {"auto": mla.MLA_KERNEL_AUTO, "simt": mla.MLA_KERNEL_SIMT, "mfma": mla.MLA_KERNEL_MFMA}[args.kernel]
-    qd = mla.MLA_BF16 if wl.kv_format == "fp8_e4m3_e8m0" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
+    qd = mla.MLA_BF16 if args.q_abs == "bf16" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
 
     log(f"[bench] generating {wl.name}")
     inp = make_inputs(wl)
@@ -121,9 +125,13 @@ def main() -> int:
         step.absorb()
         if ev is not None:
             ev[0].record()
+            step.params.kernel_start_event = ev[2].cuda_event
+            step.params.kernel_stop_event = ev[3].cuda_event
         step.decode()
         if ev is not None:
             ev[1].record()
+            step.params.kernel_start_event = None
+            step.params.kernel_stop_event = None
         step.project()
 
     for i in range(args.warmup):
@@ -131,8 +139,12 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # Per step: the decode call (plan + attention + merge) and, recorded by
+    # the library on the launch stream, the attention kernel alone.
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
+    for e in evs:
+        for x in e:
+            x.record()  # creates the underlying HIP event
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -141,12 +153,16 @@ def main() -> int:
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    decode_ms = [a.elapsed_time(b) for a, b in evs]
+    decode_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    kernel_ms = [e[2].elapsed_time(e[3]) for e in evs]
     ms_per_step = total_ms / args.steps
     decode_avg_s = sum(decode_ms) / len(decode_ms) / 1e3
-    achieved = latent_bytes / decode_avg_s / 1e9
+    kernel_avg_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    achieved_call = latent_bytes / decode_avg_s / 1e9
+    achieved = latent_bytes / kernel_avg_s / 1e9
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, decode call "
-        f"{decode_avg_s * 1e6:.1f} us, {achieved:.0f} GB/s")
+        f"{decode_avg_s * 1e6:.1f} us ({achieved_call:.0f} GB/s), attention kernel "
+        f"{kernel_avg_s * 1e6:.1f} us ({achieved:.0f} GB/s)")
 
     base = None
     if not args.no_cpu_baseline:
@@ -173,11 +189,13 @@ def main() -> int:
             "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_per_seq": wl.q_per_seq,
             "context": list(wl.lens), "page_block": wl.page_block, "kv_format": wl.kv_format,
             "d_latent": wl.d_latent, "d_rope": wl.d_rope, "num_splits": splits,
-            "kernel": {1: "simt", 2: "mfma"}[used], "cache_copies": copies,
+            "kernel": {1: "simt", 2: "mfma"}[used], "q_abs": "f32" if qd == mla.MLA_F32 else "bf16",
+            "cache_copies": copies,
         },
-        "hbm_gbs": achieved,
-        "pct_of_8tbs": 100.0 * achieved / HBM_PEAK_GBS,
+        "hbm_gbs": achieved_call,
+        "pct_of_8tbs": 100.0 * achieved_call / HBM_PEAK_GBS,
         "decode_call_us": decode_avg_s * 1e6,
+        "attention_kernel_us": kernel_avg_s * 1e6,
         "latent_bytes": latent_bytes,
         "unique_bytes": unique_bytes,
         "roofline": {

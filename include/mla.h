@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
 
@@ -141,6 +141,13 @@ typedef struct {
   mla_dtype_t o_dtype;
   float* lse;          /* out (optional, may be NULL): [B][Sq][H], natural
                           log of the softmax denominator */
+  void* kernel_start_event; /* optional hipEvent_t (NULL = none): recorded on
+                               the stream right before the split-KV attention
+                               kernel is launched */
+  void* kernel_stop_event;  /* optional hipEvent_t (NULL = none): recorded right
+                               after it, before the merge kernel.  Both are
+                               caller-owned; they time the dominant kernel
+                               alone. */
 } mla_decode_params_t;
 
 /* Workspace bytes mla_decode_paged needs for these parameters.  Reads only

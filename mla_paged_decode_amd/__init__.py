@@ -72,8 +72,13 @@ class DecodeParams(ctypes.Structure):
         ("o_latent", ctypes.c_void_p),
         ("o_dtype", ctypes.c_int),
         ("lse", ctypes.c_void_p),
+        ("kernel_start_event", ctypes.c_void_p),
+        ("kernel_stop_event", ctypes.c_void_p),
     ]
 
+
+# Must equal MLA_ABI_VERSION of include/mla.h (the parameter struct layout).
+ABI_VERSION = 2
 
 _lib = None
 
@@ -104,6 +109,9 @@ def lib() -> ctypes.CDLL:
         L.mla_last_error_message.restype = ctypes.c_char_p
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = i32
+        if L.mla_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{library_path} has ABI version {L.mla_abi_version()}, this binding expects "
+                               f"{ABI_VERSION}; rebuild with `python -m mla_paged_decode_amd.build`")
         _lib = L
     return _lib
 

@@ -307,8 +307,12 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
   hipError_t e;
   if (a.num_splits == 0 && !a.plan_in_kernel && (e = mla::launch_plan(a, s)) != hipSuccess)
     return hip_fail("plan launch", e);
+  if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
+    return hip_fail("kernel_start_event record", e);
   e = use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
   if (e != hipSuccess) return hip_fail("decode launch", e);
+  if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
+    return hip_fail("kernel_stop_event record", e);
   if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);
   return ok();
 }

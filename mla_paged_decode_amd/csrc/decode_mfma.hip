@@ -23,13 +23,20 @@
 // keeps the scores at ~16 significant bits; P is rounded once to bf16; all
 // accumulation is fp32.  bf16 queries take a single pass.
 //
-// Tile staging: the next tile's rows are loaded into registers (16-byte,
-// coalesced along each row) while the current tile is computed, then stored
-// to the other LDS buffer.  fp8 rows (e4m3 + e8m0 per 32 values) are decoded
-// to bf16 on the way; both conversions are exact.  Rows of the LDS tile are
-// 16-byte-chunk XOR-swizzled so that the 16-token b128 reads of QK^T and the
-// 4-token transposed reads of PV hit distinct banks.
+// Tile staging.  bf16 rows go from HBM straight into LDS with 16-byte
+// direct-to-LDS loads, NBUF-1 tiles ahead of the one being computed; their
+// completion is tracked with explicit vmcnt waits and the hand-off between
+// waves uses an LDS-only barrier, so later tiles stay in flight.  fp8 rows
+// (e4m3 + e8m0 per 32 values) are loaded into registers one tile ahead and
+// decoded to bf16 on the way into LDS (both conversions are exact).
+//
+// LDS tile layout: the latent part of the 32 rows (region A) and the RoPE
+// part (region B) are stored separately, so that a region-A row is exactly
+// one direct-to-LDS instruction (64 lanes x 16 B).  16-byte chunks within a
+// row are XOR-swizzled by the token index so that the 16-token b128 reads of
+// QK^T and the 4-token transposed reads of PV hit distinct banks.
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -42,16 +49,19 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+// The block table is read-only during a call: reading it through the
+// constant address space lets the compiler use scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 constexpr int kTile = 32;      // tokens per tile
 constexpr int kDr = 64;        // RoPE dims
 constexpr float kLn2 = 0.693147180559945309f;
 
-// LDS tile: the latent part of the 32 rows (region A, d_c values per row)
-// and the RoPE part (region B, 64 values per row) are stored separately, so
-// that region A rows are a whole number of 1 KB / 896 B and a direct-to-LDS
-// instruction moves exactly one token's latent row.
 template <int FMT>
 struct Geo {
   static constexpr int kDc = FMT == kBF16 ? 512 : 448;      // latent width
@@ -78,53 +88,51 @@ __device__ __forceinline__ int lds_off(int tok, int chunk, int row_bytes) {
   return tok * row_bytes + 16 * (chunk ^ swz(tok));
 }
 
-// Hide a value from loop-invariant code motion: address arithmetic is
-// recomputed where it is used instead of being held in registers.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// Physical pages of one 32-token tile: tokens [tt0, tt1) of the current
-// sequence lie in logical pages p0 .. p0+2 at most (page_block >= 16).
-// Loaded with scalar loads, so the vector-memory counter only tracks the
-// tile data itself.
-struct TilePages {
-  int tt0, tt1, p0, pg0, pg1, pg2;
-};
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// The block table is read-only during the call: reading it through the
-// constant address space lets the compiler use scalar loads.
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+// Source of one tile: tokens [tt0, tt0 + n) of the current sequence.  Work
+// units start at multiples of kTile tokens and page_block is a power of two
+// >= 16, so the tile lies in one page (page_block >= 32) or two (16).  Tile
+// token k is read from row kk = min(k, n - 1) (tokens past the end repeat the
+// last valid one, so every row read holds finite values), at
+//   (kk < kb ? base0 : base1) + kk * row_bytes.
+// All fields are wave-uniform and live in scalar registers.
+struct TileSrc {
+  int n, kb;
+  uint64_t base0, base1;
+};
+
+// Physical pages of one tile, looked up (scalar loads) one tile before they
+// are used, so that the lookup latency overlaps the wait for the tile before.
+struct TilePages {
+  int tt0, pg0, pg1;
+};
 
 __device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const_i32_ptr bt, int tt0, int t1) {
-  TilePages r;
-  r.tt0 = tt0;
-  r.tt1 = min(tt0 + kTile, t1);
-  r.p0 = tt0 >> a.P_log2;
-  const int p1 = (r.tt1 - 1) >> a.P_log2;
-  r.pg0 = uniform(bt[r.p0]);
-  r.pg1 = uniform(bt[min(r.p0 + 1, p1)]);
-  r.pg2 = uniform(bt[min(r.p0 + 2, p1)]);
-  // Pin the fields in scalar registers so the struct never lives in memory
-  // (a dynamically indexed copy would add waits on the transfer counter).
-  asm volatile("" : "+s"(r.tt0), "+s"(r.tt1), "+s"(r.p0), "+s"(r.pg0), "+s"(r.pg1), "+s"(r.pg2));
+  const int n = min(kTile, t1 - tt0);
+  return TilePages{tt0, bt[tt0 >> a.P_log2], bt[(tt0 + n - 1) >> a.P_log2]};
+}
+
+__device__ __forceinline__ TileSrc tile_src(const DecodeArgs& a, const TilePages& tp, int t1) {
+  TileSrc r;
+  r.n = min(kTile, t1 - tp.tt0);
+  const int s0 = tp.tt0 & (a.P - 1);
+  r.kb = a.P - s0;
+  const uint64_t pool = (uint64_t)(uintptr_t)a.pool;
+  r.base0 = pool + (uint64_t)((int64_t)uniform(tp.pg0) * a.P + s0) * (uint64_t)a.row_bytes;
+  r.base1 = pool + (uint64_t)((int64_t)uniform(tp.pg1) * a.P - r.kb) * (uint64_t)a.row_bytes;
+  asm volatile("" : "+s"(r.n), "+s"(r.kb), "+s"(r.base0), "+s"(r.base1));
   return r;
 }
 
-// Row index (page * P + slot) of tile token k; tokens past the end repeat
-// the last valid one.
-__device__ __forceinline__ int64_t tile_row(const DecodeArgs& a, TilePages tp, int k) {
-  const int t = min(tp.tt0 + k, tp.tt1 - 1);
-  const int pi = (t >> a.P_log2) - tp.p0;  // 0, 1 or 2
-  const int page = tp.pg0 + (pi >= 1 ? tp.pg1 - tp.pg0 : 0) + (pi >= 2 ? tp.pg2 - tp.pg1 : 0);
-  return (int64_t)page * a.P + (t & (a.P - 1));
+// Address of the row holding tile token k (wave-uniform k).
+__device__ __forceinline__ const uint8_t* tile_row_ptr(const TileSrc& ts, int k, int64_t row_bytes) {
+  const int kk = min(k, ts.n - 1);
+  return (const uint8_t*)(uintptr_t)((kk < ts.kb ? ts.base0 : ts.base1) + (uint64_t)(kk * (int)row_bytes));
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
@@ -134,6 +142,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
 }
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
 
 // Workgroup barrier for LDS hand-off only.  The caller has already waited
 // for its own LDS operations and tile transfers; unlike __syncthreads() this
@@ -145,53 +156,139 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// One 16-byte direct-to-LDS load per lane: the wave's 64 chunks land at
-// lds + 16 * lane.  Issued as inline assembly so that the compiler does not
-// treat the pending LDS write as aliasing every LDS read (which would make
-// it drain all transfers before reading the current tile); completion is
-// tracked explicitly with wait_vmcnt_lgkm0.
-__device__ __forceinline__ void dma16(const void* src, const char* lds) {
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+// One 16-byte direct-to-LDS load per lane from sbase + voff: the wave's 64
+// chunks land at lds + 16 * lane.  Issued as inline assembly so that the
+// compiler does not treat the pending LDS write as aliasing every LDS read
+// (which would make it drain all transfers before reading the current
+// tile); completion is tracked explicitly with wait_vmcnt_lgkm0.  m0 holds
+// the LDS destination during the instruction and is restored afterwards.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const lds_char* lds) {
+  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)lds);
   uint32_t saved;
-  // m0 holds the LDS destination of the transfer; its previous value is
-  // restored afterwards.
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds_addr)
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
       : "memory");
 }
 
-// bf16 tiles go straight from HBM to LDS with 16-byte direct-to-LDS loads.
-// A wave instruction fills 64 consecutive 16-B LDS chunks from per-lane
-// sources: instruction k < 32 is token k's latent row (lane = swizzled
-// chunk, 1 KB contiguous in HBM); the 4 instructions after it carry the
-// RoPE parts of 8 tokens each.  Wave w issues latent rows w, w+NW, ... and
-// RoPE groups w, w+NW, ...; every wave issues at least kMinOps of them.
+// Eight direct-to-LDS loads of one wave: lane l loads 16 B from
+// sbase + voff[j] into lds + 1024 * j + 16 * l, for j = 0..7.
+__device__ __forceinline__ void dma16x8(const void* sbase, const uint32_t (&voff)[8], const lds_char* lds) {
+  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %10\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, %9\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, %9\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
+        "v"(voff[7]), "s"(sbase), "s"(lds_addr)
+      : "memory", "scc");
+}
+
+// bf16 tiles go straight from HBM to LDS.  A wave instruction fills 64
+// consecutive 16-B LDS chunks: one token's latent row (lane = swizzled
+// chunk, 1 KB contiguous in HBM), or the RoPE parts of 8 tokens.  Latent rows
+// are handed out in groups of 8 tokens (group i = tokens 8i..8i+7, so that a
+// row's swizzle only depends on its place in the group): wave w issues groups
+// w, w+NW, ... and RoPE instructions w, w+NW, ...
 template <int NW>
 struct DmaStaging {
   using G = Geo<kBF16>;
-  static constexpr int kRopeInst = kTile * 8 / 64;  // 4
-  static constexpr int kMinOps = kTile / NW + kRopeInst / NW;
+  static constexpr int kRowBytes = 2 * G::kVals;
+  static constexpr int kGroups = kTile / 8;
+  static constexpr int kRopeInst = kTile * 8 / 64;
+  // Fewest transfer instructions any wave issues per tile.
+  static constexpr int kMinOps = 8 * (kGroups / NW) + kRopeInst / NW;
 
-  __device__ __forceinline__ static void load(const DecodeArgs& a, TilePages tp, char* buf) {
+  // Per-lane source offsets for a whole tile in one page, relative to the
+  // row of the group's first token: row j's swizzled latent chunk, and the
+  // RoPE chunk of token lane/8.
+  uint32_t lat_off[8];
+  uint32_t rope_off;
+
+  __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll 1
-    for (int k = wave; k < kTile; k += NW) {
-      const uint8_t* src = a.pool + tile_row(a, tp, k) * a.row_bytes + 16 * (lane ^ swz(k));
-      dma16(src, buf + G::kLatRow * k);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lat_off[j] = j * kRowBytes + 16 * (lane ^ swz(j));
+    const int t = lane >> 3;
+    rope_off = t * kRowBytes + 2 * G::kDc + 16 * ((lane & 7) ^ swz(t));
+  }
+
+  __device__ __forceinline__ void load(const TileSrc& ts, lds_char* buf) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    if (ts.n == kTile && ts.kb >= kTile) {  // whole tile, one page: rows are consecutive
+#pragma unroll
+      for (int i = 0; i < (kGroups + NW - 1) / NW; ++i) {
+        const int grp = wave + NW * i;
+        if (NW * i + NW <= kGroups || grp < kGroups)
+          dma16x8((const void*)(uintptr_t)(ts.base0 + (uint64_t)(8 * kRowBytes) * grp), lat_off,
+                  buf + G::kLatRow * 8 * grp);
+      }
+#pragma unroll
+      for (int i = 0; i < (kRopeInst + NW - 1) / NW; ++i) {
+        const int r = wave + NW * i;
+        if (NW * i + NW <= kRopeInst || r < kRopeInst)
+          dma16((const void*)(uintptr_t)(ts.base0 + (uint64_t)(8 * kRowBytes) * r), rope_off,
+                buf + G::kRopeBase + 1024 * r);
+      }
+      return;
     }
-#pragma unroll 1
-    for (int r = wave; r < kRopeInst; r += NW) {
-      const int tok = 8 * r + (lane >> 3);
-      const uint8_t* src = a.pool + tile_row(a, tp, tok) * a.row_bytes + 2 * G::kDc + 16 * ((lane & 7) ^ swz(tok));
-      dma16(src, buf + G::kRopeBase + 1024 * r);
+    // Last tile of a unit, or a tile across two pages of 16 tokens.
+#pragma unroll
+    for (int i = 0; i < (kGroups + NW - 1) / NW; ++i) {
+      const int grp = wave + NW * i;
+      if (NW * i + NW <= kGroups || grp < kGroups) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = 8 * grp + j;
+          dma16(tile_row_ptr(ts, k, kRowBytes), 16u * (lane ^ swz(j)), buf + G::kLatRow * k);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < (kRopeInst + NW - 1) / NW; ++i) {
+      const int r = wave + NW * i;
+      if (NW * i + NW <= kRopeInst || r < kRopeInst) {
+        // Tokens 8r..8r+7 share a page: the 16-token page boundary of
+        // page_block 16 falls between groups, and clamping to n - 1 moves
+        // a whole group below it.
+        const int t = lane >> 3;
+        const int kk = min(8 * r + t, ts.n - 1);
+        const int kk_hi = min(8 * r + 7, ts.n - 1);
+        const uint64_t base = kk_hi < ts.kb ? ts.base0 : ts.base1;
+        const uint32_t off = (uint32_t)(kk * kRowBytes) + 2 * G::kDc + 16 * ((lane & 7) ^ swz(t));
+        dma16((const void*)(uintptr_t)base, off, buf + G::kRopeBase + 1024 * r);
+      }
     }
   }
 };
@@ -206,13 +303,14 @@ struct Fp8Staging {
   uint4 v[kPer];
   uint32_t s[kPer];
 
-  __device__ __forceinline__ void load(const DecodeArgs& a, TilePages tp) {
+  __device__ __forceinline__ void load(const DecodeArgs& a, const TileSrc& ts) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = j * kThreads + threadIdx.x;
       const int tok = min(q / G::kSrcChunks, kTile - 1);
       const int c = q % G::kSrcChunks;
-      const uint8_t* p = a.pool + tile_row(a, tp, tok) * a.row_bytes;
+      const int kk = min(tok, ts.n - 1);
+      const uint8_t* p = (const uint8_t*)(uintptr_t)((kk < ts.kb ? ts.base0 : ts.base1) + (uint64_t)(kk * (int)a.row_bytes));
       if (q < kSrc) {
         v[j] = *reinterpret_cast<const uint4*>(p + 16 * c);
         s[j] = p[G::kVals + c / 2];
@@ -220,7 +318,7 @@ struct Fp8Staging {
     }
   }
 
-  __device__ __forceinline__ void store(char* buf) const {
+  __device__ __forceinline__ void store(lds_char* buf) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = j * kThreads + threadIdx.x;
@@ -239,35 +337,42 @@ struct Fp8Staging {
         o[2 * i + 1] = pack_bf16(hi[0] * scale, hi[1] * scale);
       }
       const int c0 = 2 * c;  // first bf16 chunk of these 16 values
-      char* d0 = c0 < G::kLatChunks ? buf + lds_off(tok, c0, G::kLatRow)
-                                    : buf + G::kRopeBase + lds_off(tok, c0 - G::kLatChunks, G::kRopeRow);
-      char* d1 = c0 < G::kLatChunks ? buf + lds_off(tok, c0 + 1, G::kLatRow)
-                                    : buf + G::kRopeBase + lds_off(tok, c0 + 1 - G::kLatChunks, G::kRopeRow);
-      *reinterpret_cast<uint4*>(d0) = make_uint4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<uint4*>(d1) = make_uint4(o[4], o[5], o[6], o[7]);
+      lds_char* d0 = c0 < G::kLatChunks ? buf + lds_off(tok, c0, G::kLatRow)
+                                        : buf + G::kRopeBase + lds_off(tok, c0 - G::kLatChunks, G::kRopeRow);
+      lds_char* d1 = c0 < G::kLatChunks ? buf + lds_off(tok, c0 + 1, G::kLatRow)
+                                        : buf + G::kRopeBase + lds_off(tok, c0 + 1 - G::kLatChunks, G::kRopeRow);
+      *(lds_u32x4*)d0 = u32x4{o[0], o[1], o[2], o[3]};
+      *(lds_u32x4*)d1 = u32x4{o[4], o[5], o[6], o[7]};
     }
   }
 };
 
 // Staging interface over the two formats.  kDepth tiles are in flight ahead
-// of the one being computed: issue(x) starts tile x's transfer into its ring
-// buffer, finish(x) completes it from registers (fp8), wait(n) blocks until
+// of the one being computed: issue() starts a tile's transfer into its ring
+// buffer, finish() completes it from registers (fp8), wait(n) blocks until
 // this wave's part of the oldest outstanding tile has landed when n younger
-// tiles have been issued after it.
+// tiles have been issued after it (and all its LDS operations are done).
 template <int FMT, int NW, int NBUF>
 struct Staging;
 
+// bf16: a tile's transfer is issued as soon as its ring buffer is free
+// (kEarlyIssue), before waiting for the tile about to be computed, so that
+// up to NBUF - 1 tiles per workgroup are in flight while it waits.
 template <int NW, int NBUF>
 struct Staging<kBF16, NW, NBUF> {
   static constexpr int kDepth = NBUF - 1;
-  __device__ __forceinline__ void issue(const DecodeArgs& a, TilePages tp, char* buf) {
-    DmaStaging<NW>::load(a, tp, buf);
-  }
-  __device__ __forceinline__ void finish(char*) {}
+  static constexpr bool kEarlyIssue = true;
+  DmaStaging<NW> dma;
+  __device__ __forceinline__ void init() { dma.init(); }
+  __device__ __forceinline__ void issue(const DecodeArgs&, const TileSrc& ts, lds_char* buf) { dma.load(ts, buf); }
+  __device__ __forceinline__ void finish(lds_char*) {}
+  // Every wave issues at least kMinOps transfers per tile, so allowing
+  // younger * kMinOps outstanding leaves only younger tiles in flight.
   __device__ __forceinline__ void wait(int younger) {
     constexpr int M = DmaStaging<NW>::kMinOps;
-    if (younger >= 2) wait_vmcnt_lgkm0<(NBUF >= 4 ? 2 * M : 0)>();
-    else if (younger == 1) wait_vmcnt_lgkm0<(NBUF >= 3 ? M : 0)>();
+    if (younger >= 3) wait_vmcnt_lgkm0<(3 * M < 64 ? 3 * M : 0)>();
+    else if (younger == 2) wait_vmcnt_lgkm0<(2 * M < 64 ? 2 * M : 0)>();
+    else if (younger == 1) wait_vmcnt_lgkm0<M>();
     else wait_vmcnt_lgkm0<0>();
   }
 };
@@ -276,18 +381,22 @@ template <int NW, int NBUF>
 struct Staging<kFP8, NW, NBUF> {
   static_assert(NBUF == 2, "fp8 tiles are staged through registers, one ahead");
   static constexpr int kDepth = 1;
+  static constexpr bool kEarlyIssue = false;
   Fp8Staging<NW> f;
-  __device__ __forceinline__ void issue(const DecodeArgs& a, TilePages tp, char*) { f.load(a, tp); }
-  __device__ __forceinline__ void finish(char* buf) { f.store(buf); }
+  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void issue(const DecodeArgs& a, const TileSrc& ts, lds_char*) { f.load(a, ts); }
+  __device__ __forceinline__ void finish(lds_char* buf) { f.store(buf); }
   __device__ __forceinline__ void wait(int) { wait_vmcnt_lgkm0<0>(); }
 };
 
 template <int FMT, bool HILO, int NW, int NBUF>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   using G = Geo<FMT>;
-  __shared__ __attribute__((aligned(16))) char tiles[NBUF][G::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char tiles_mem[NBUF * G::kTileBytes];
   __shared__ int32_t s_ts[kMaxInKernelPlan + 1];
   __shared__ int32_t s_scan[64 * NW];
+  __shared__ int32_t s_lens[kMaxInKernelPlan];
+  lds_char* const tiles = (lds_char*)tiles_mem;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -298,18 +407,37 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
-    block_plan(a.seq_lens, a.B, s_ts, s_scan);
+    block_plan(a.seq_lens, a.B, s_ts, s_scan, s_lens);
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
       for (int i = threadIdx.x; i <= a.B; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
   }
-  UnitIter unit_it(a, ts);
+  using St = Staging<FMT, NW, NBUF>;
+  constexpr int D = St::kDepth;
+  St st;
+  st.init();
+  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens);
   Unit unit;
   while (unit_it.next(a, unit)) {
     // The unit is the same for the whole workgroup: keep it in scalar
     // registers so page lookups below are scalar loads.
     const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
     const int64_t slot = a.num_splits > 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x + b;
+
+    // The first tile transfers start before the queries are loaded, so that
+    // the two latencies overlap.
+    const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
+    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+    TilePages pages_next;  // pages of the next tile to issue, looked up one tile early
+    if (ntiles > 0) {
+      wait_vmcnt_lgkm0<0>();
+      lds_barrier();  // the previous unit's readers of the ring are done
+#pragma unroll
+      for (int x = 0; x < D; ++x)
+        if (x < ntiles) st.issue(a, tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), tiles + x * G::kTileBytes);
+      if (D < ntiles) pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
+    }
+
     // ---- queries in the B-operand layout: column = row, k = 8g..8g+7 ----
     bf16x8 qh[G::kKs], ql[HILO ? G::kKs : 1];
     {
@@ -342,6 +470,13 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
+    // The queries are only ever read as the MFMA B operand, which may come
+    // from AGPRs: keeping them there leaves the VGPRs to tile operands.
+#pragma unroll
+    for (int ks = 0; ks < G::kKs; ++ks) {
+      asm volatile("" : "+a"(qh[ks]));
+      if constexpr (HILO) asm volatile("" : "+a"(ql[ks]));
+    }
     const int j_q = row_ok ? row / a.H : 0;
     const int last_visible = L - a.Sq + j_q;
 
@@ -350,84 +485,111 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     for (int d = 0; d < G::kDb; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
 
-    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
-    using St = Staging<FMT, NW, NBUF>;
-    constexpr int D = St::kDepth;
-    St st;
-    TilePages tp_next;  // pages of the next tile to issue, loaded one tile early
-    if (ntiles > 0) {
-      wait_vmcnt_lgkm0<0>();
-      lds_barrier();  // the previous unit's readers of the ring are done
-#pragma unroll
-      for (int x = 0; x < D; ++x)
-        if (x < ntiles) st.issue(a, tile_pages(a, bt, t0 + x * kTile, t1), tiles[x]);
-      if (D < ntiles) tp_next = tile_pages(a, bt, t0 + D * kTile, t1);
-      st.finish(tiles[0]);
-    }
+    if (ntiles > 0) st.finish(tiles);  // fp8: first tile from registers to LDS
 
-    for (int it = 0; it < ntiles; ++it) {
-      st.wait(min(D - 1, ntiles - 1 - it));  // this wave's part of tile `it` landed
-      lds_barrier();                          // everyone's did; everyone finished tile it-1
-      const int x = it + D;                   // goes into the buffer tile it-1 used
-      if (x < ntiles) {
-        st.issue(a, tp_next, tiles[x % NBUF]);
-        if (x + 1 < ntiles) tp_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+    // One pipeline step before computing tile `it`.  Early issue: once every
+    // wave is done with tile it-1, start tile it+D into its buffer, then wait
+    // for tile it.  Otherwise (fp8, staged through registers one tile ahead):
+    // wait for tile it, then start loading tile it+1 into registers.
+    auto sync_issue = [&](int it) __attribute__((always_inline)) {
+      const int x = it + D;
+      if constexpr (St::kEarlyIssue) {
+        wait_lgkm0();
+        lds_barrier();  // everyone finished tile it-1: its buffer is free
+        if (x < ntiles) {
+          st.issue(a, tile_src(a, pages_next, t1), tiles + (x % NBUF) * G::kTileBytes);
+          if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+        }
+        st.wait(min(D, ntiles - 1 - it));  // this wave's part of tile `it` landed
+        lds_barrier();                     // everyone's did
+      } else {
+        st.wait(min(D - 1, ntiles - 1 - it));
+        lds_barrier();  // everyone's part of tile `it` landed; everyone finished tile it-1
+        if (x < ntiles) {
+          st.issue(a, tile_src(a, pages_next, t1), tiles + (x % NBUF) * G::kTileBytes);
+          if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+        }
       }
-      const char* buf = tiles[it % NBUF];
+    };
+    auto finish_next = [&](int it) __attribute__((always_inline)) {
+      if (D == 1 && it + 1 < ntiles) st.finish(tiles + ((it + 1) % NBUF) * G::kTileBytes);
+    };
+
+    // Online softmax with a reference maximum m per row (base-2 domain).
+    // m is set by the first tile with a visible token and then kept while
+    // the scores stay below m + kHeadroom: P = 2^(s - m) < 2^kHeadroom is
+    // far from overflowing bf16 / fp32, and P, the denominator and the
+    // accumulator all use the same m, so the result does not depend on it.
+    // The accumulator is zero while m = -inf, so setting m then needs no
+    // rescale.  A tile whose scores exceed m + kHeadroom (rare: a score
+    // ~44 nats above every earlier one) sends the wave to the loop below,
+    // which rescales the accumulator; keeping that out of the main loop
+    // lets the accumulators stay in the matrix-core registers.
+    constexpr float kHeadroom = 64.f;
+    // Returns false (having changed nothing) if tile `it` needs a rescale
+    // and kRescale is false.
+    auto tile = [&](int it, auto rescale_tag) __attribute__((always_inline)) -> bool {
+      constexpr bool kRescale = decltype(rescale_tag)::value;
+      const lds_char* buf = tiles + (it % NBUF) * G::kTileBytes;
       const int tt0 = t0 + it * kTile;
 
       // ---- S^T = Tile . Q^T for two 16-token blocks ----
       // Lane reads chunk 4ks+g of token tb*16+li.  With x = swz(token),
       // (4ks+g)^x = 4(ks ^ (x>>2)) + (g ^ (x&3)), so the address is a per-lane
       // base (one for even, one for odd ks) plus the immediate 64*ks.
-      // Operands are prefetched one k-step ahead; the scheduling fences keep
-      // the compiler from hoisting every LDS read of the unrolled loop.
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      const char* lat_base[2][2];
-      const char* rope_base[2][2];
+      // Operands are prefetched kQkAhead k-steps ahead (LDS latency is several
+      // MFMA issue slots); the scheduling fences keep the compiler from
+      // hoisting every LDS read of the unrolled loop.  Even and odd k-steps
+      // accumulate separately, so four independent MFMA chains are in flight.
+      constexpr int kQkAhead = HILO ? 2 : 3;
+      f32x4 sc[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) sc[tb][0] = sc[tb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const lds_char* lat_base[2][2];
+      const lds_char* rope_base[2][2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int tok = tb * 16 + li;
-        const int x = swz(tok);
-        const int flip = 64 * (x >> 2);
-        const char* bl = buf + tok * G::kLatRow + 16 * (g ^ (x & 3));
-        const char* br = buf + G::kRopeBase + tok * G::kRopeRow + 16 * (g ^ (x & 3));
+        const int xs = swz(tok);
+        const int flip = 64 * (xs >> 2);
+        const lds_char* bl = buf + tok * G::kLatRow + 16 * (g ^ (xs & 3));
+        const lds_char* br = buf + G::kRopeBase + tok * G::kRopeRow + 16 * (g ^ (xs & 3));
         lat_base[tb][0] = bl + flip;
         lat_base[tb][1] = bl - flip;
         rope_base[tb][0] = br + flip;
         rope_base[tb][1] = br - flip;
       }
       auto tile_a = [&](int ks, int tb) {
-        const char* p = ks < G::kKsLat ? lat_base[tb][ks & 1] + 64 * ks
-                                       : rope_base[tb][ks & 1] + 64 * (ks - G::kKsLat);
-        return *reinterpret_cast<const bf16x8*>(p);
+        const lds_char* p = ks < G::kKsLat ? lat_base[tb][ks & 1] + 64 * ks
+                                           : rope_base[tb][ks & 1] + 64 * (ks - G::kKsLat);
+        return *(const lds_bf16x8*)p;
       };
-      bf16x8 ta0 = tile_a(0, 0), ta1 = tile_a(0, 1);
+      bf16x8 ta[kQkAhead][2];
+#pragma unroll
+      for (int k = 0; k < kQkAhead; ++k) {
+        ta[k][0] = tile_a(k, 0);
+        ta[k][1] = tile_a(k, 1);
+      }
 #pragma unroll
       for (int ks = 0; ks < G::kKs; ++ks) {
-        bf16x8 tn0 = ta0, tn1 = ta1;
-        if (ks + 1 < G::kKs) {
-          tn0 = tile_a(ks + 1, 0);
-          tn1 = tile_a(ks + 1, 1);
+        const bf16x8 a0 = ta[ks % kQkAhead][0], a1 = ta[ks % kQkAhead][1];
+        if (ks + kQkAhead < G::kKs) {
+          ta[ks % kQkAhead][0] = tile_a(ks + kQkAhead, 0);
+          ta[ks % kQkAhead][1] = tile_a(ks + kQkAhead, 1);
         }
-        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta0, qh[ks], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta1, qh[ks], s[1], 0, 0, 0);
+        f32x4& c0 = sc[0][ks & 1];
+        f32x4& c1 = sc[1][ks & 1];
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qh[ks], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qh[ks], c1, 0, 0, 0);
         if constexpr (HILO) {
-          s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta0, ql[ks], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ta1, ql[ks], s[1], 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ql[ks], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ql[ks], c1, 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        ta0 = tn0;
-        ta1 = tn1;
       }
+      const f32x4 s[2] = {sc[0][0] + sc[0][1], sc[1][0] + sc[1][1]};
 
-      // ---- online softmax for row `row` over tokens tt0 + {4g+i, 16+4g+i} ----
-      // m is a reference maximum that is only raised when a row's scores
-      // exceed it by more than 2^8 (base-2 domain): P = 2^(s - m) then stays
-      // below 256, and P, the denominator and the accumulator all use the
-      // same m, so the result is unchanged while the rescale of the
-      // accumulator is skipped on almost every tile.
+
       float sv[2][4];
       float mx = -INFINITY;
 #pragma unroll
@@ -441,21 +603,24 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool raise = mx > m + 8.f;  // also true when m = -inf < mx
-      if (__any(raise)) {
-        const float m_new = raise ? mx : m;
-        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m - m_new);
-        lsum *= alpha;
-        m = m_new;
-        float al[4];
+      if constexpr (kRescale) {
+        const bool raise = mx > m + 8.f;  // also true when m = -inf < mx
+        if (__any(raise)) {
+          const float m_new = raise ? mx : m;
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+          lsum *= alpha;
+          m = m_new;
+          float al[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+          for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
 #pragma unroll
-        for (int d = 0; d < G::kDb; ++d) {
+          for (int d = 0; d < G::kDb; ++d)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
-          __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 4; ++i) acc[d][i] *= al[i];
         }
+      } else {
+        if (__any(m != -INFINITY && mx > m + kHeadroom)) return false;
+        m = m == -INFINITY ? mx : m;
       }
       float psum = 0.f;
       uint32_t pk[4];
@@ -463,8 +628,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; i += 2) {
-          const float e0 = m == -INFINITY ? 0.f : exp2f(sv[tb][i] - m);
-          const float e1 = m == -INFINITY ? 0.f : exp2f(sv[tb][i + 1] - m);
+          const float e0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i] - m);
+          const float e1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i + 1] - m);
           psum += e0 + e1;
           pk[2 * tb + i / 2] = pack_bf16(e0, e1);
         }
@@ -478,22 +643,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       // of bf16 chunk 2d + h (h = (li&3)>>1), byte 8*(li&1).  With x =
       // swz(token), (2d+h)^x = 2(4(d>>2) + ((d&3) ^ (x>>1))) + (h ^ (x&1)):
       // one per-lane base per (d&3, half) plus the immediate 128*(d>>2).
-      const char* vbase[2][4];
+      const lds_char* vbase[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int tok = 16 * half + 4 * g + (li >> 2);
-        const int x = swz(tok);
+        const int xs = swz(tok);
         const int h = (li & 3) >> 1;
-        const char* b0 = buf + tok * G::kLatRow + 16 * (h ^ (x & 1)) + 8 * (li & 1);
+        const lds_char* b0 = buf + tok * G::kLatRow + 16 * (h ^ (xs & 1)) + 8 * (li & 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vbase[half][r] = b0 + 32 * (r ^ (x >> 1));
+        for (int r = 0; r < 4; ++r) vbase[half][r] = b0 + 32 * (r ^ (xs >> 1));
       }
       auto tile_v = [&](int d) {
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[0][d & 3] + 128 * (d >> 2)));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[1][d & 3] + 128 * (d >> 2)));
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      constexpr int kPrefetch = 4;
+      constexpr int kPrefetch = HILO ? 4 : 8;
       bf16x8 vq[kPrefetch];
 #pragma unroll
       for (int d = 0; d < kPrefetch; ++d) vq[d] = tile_v(d);
@@ -505,7 +670,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      if (D == 1 && it + 1 < ntiles) st.finish(tiles[(it + 1) % NBUF]);
+      return true;
+    };
+
+    int it = 0;
+    for (; it < ntiles; ++it) {
+      sync_issue(it);
+      if (!tile(it, std::false_type{})) break;
+      finish_next(it);
+    }
+    if (it < ntiles) {  // tile `it` is synchronised but not yet computed
+      tile(it, std::true_type{});
+      finish_next(it);
+      for (++it; it < ntiles; ++it) {
+        sync_issue(it);
+        tile(it, std::true_type{});
+        finish_next(it);
+      }
     }
 
     // ---- normalise and write this unit's partial ----
@@ -548,8 +729,8 @@ int waves_for(int R) { return max(2, (R + 15) / 16); }
 
 }  // namespace
 
-// Query rows per workgroup: one wave per 16 rows; fp32 (hi + lo) queries
-// need twice the query registers, which limits them to four waves.
+// fp32 (hi + lo) queries need twice the query registers, which limits them
+// to four waves.
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32) {
   if (dr != kDr) return false;
   if (!((fmt == kBF16 && dc == 512) || (fmt == kFP8 && dc == 448))) return false;

@@ -3,8 +3,11 @@
 //
 // Uniform mode (num_splits = S >= 1): grid.x = B * S; workgroup x handles
 // chunk s = x % S of sequence b = x / S, tokens [s*c, min((s+1)*c, L)) with
-// c = ceil(L / S); its partial goes to slot x.  Every slot is written, empty
+// c = ceil(L / S) rounded up to a multiple of kPlanTile; its partial goes to
+// slot x.  Every slot is written, empty
 // chunks included (lse = -inf).
+//
+// In both modes a unit starts at a multiple of kPlanTile tokens.
 //
 // Balanced mode (num_splits = 0): every sequence is cut into tiles of
 // kPlanTile tokens; tile_start[b] is the exclusive prefix sum of tile counts
@@ -38,14 +41,20 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* ts, int B, int64_t t) 
 
 // Balanced-mode plan computed by one workgroup: ts[b] = sum over b' < b of
 // ceil(max(L_b', 0) / kPlanTile), ts[B] = total, written to `ts` (LDS or
-// global).  `scan` is LDS scratch of blockDim.x ints.  Contains barriers:
-// every thread of the workgroup must call it.
-__device__ __forceinline__ void block_plan(const int32_t* lens, int B, int32_t* ts, int32_t* scan) {
+// global).  `scan` is LDS scratch of blockDim.x ints.  If lens_out is not
+// null, max(lens[b], 0) is also stored there.  Contains barriers: every
+// thread of the workgroup must call it.
+__device__ __forceinline__ void block_plan(const int32_t* lens, int B, int32_t* ts, int32_t* scan,
+                                           int32_t* lens_out = nullptr) {
   const int nt = blockDim.x, tid = threadIdx.x;
   const int per = (B + nt - 1) / nt;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
   int32_t sum = 0;
-  for (int b = b0; b < b1; ++b) sum += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
+  for (int b = b0; b < b1; ++b) {
+    const int32_t L = max(lens[b], 0);
+    if (lens_out) lens_out[b] = L;
+    sum += (L + kPlanTile - 1) / kPlanTile;
+  }
   scan[tid] = sum;
   __syncthreads();
   for (int off = 1; off < nt; off <<= 1) {
@@ -73,11 +82,13 @@ struct Unit {
 //   UnitIter it(a); Unit u; while (it.next(a, u)) { ... }
 // All lanes of the workgroup see the same sequence of units.
 struct UnitIter {
-  const int32_t* ts;  // tile_start[0..B] (global memory or LDS)
-  int b;              // next sequence to consider (balanced) / done flag (uniform)
-  int64_t tb, te;     // this worker's tile range (balanced)
+  const int32_t* ts;    // tile_start[0..B] (global memory or LDS)
+  const int32_t* lens;  // sequence lengths (global memory, or clamped copies in LDS)
+  int b;                // next sequence to consider (balanced) / done flag (uniform)
+  int64_t tb, te;       // this worker's tile range (balanced)
 
-  __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start) : ts(tile_start) {
+  __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start, const int32_t* seq_lens)
+      : ts(tile_start), lens(seq_lens) {
     if (a.num_splits > 0) {
       b = 0;
       tb = te = 0;
@@ -96,8 +107,8 @@ struct UnitIter {
       const int S = a.num_splits;
       u.b = blockIdx.x / S;
       const int s = blockIdx.x % S;
-      u.L = max(a.seq_lens[u.b], 0);
-      const int chunk = (u.L + S - 1) / S;
+      u.L = max(lens[u.b], 0);
+      const int chunk = ((u.L + S - 1) / S + kPlanTile - 1) / kPlanTile * kPlanTile;
       u.t0 = min(u.L, s * chunk);
       u.t1 = min(u.L, u.t0 + chunk);
       u.slot = blockIdx.x;
@@ -108,7 +119,7 @@ struct UnitIter {
       const int64_t s1 = min(te, (int64_t)ts[b + 1]);
       if (s0 >= s1) continue;
       u.b = b;
-      u.L = max(a.seq_lens[b], 0);
+      u.L = max(lens[b], 0);
       u.t0 = (int)((s0 - ts[b]) * kPlanTile);
       u.t1 = (int)min((int64_t)u.L, (s1 - ts[b]) * kPlanTile);
       u.slot = (int64_t)blockIdx.x + b;
@@ -122,7 +133,7 @@ struct UnitIter {
 // Calls f(b, L, t0, t1, slot) for each unit of this workgroup.
 template <class F>
 __device__ __forceinline__ void for_each_unit(const DecodeArgs& a, F&& f) {
-  UnitIter it(a, a.tile_start);
+  UnitIter it(a, a.tile_start, a.seq_lens);
   Unit u;
   while (it.next(a, u)) f(u.b, u.L, u.t0, u.t1, u.slot);
 }

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert mla.mla_abi_version() == 1
+    assert mla.mla_abi_version() == 2
 
 
 def test_row_bytes_match_page_figures(golden_dir):
