@@ -40,8 +40,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   if (tid == kPlanThreads - 1) tile_start[B] = s[tid];
 }
 
-constexpr int kCombineThreads = 256;
-constexpr int kMaxParts = 4096;  // partial slots one sequence can have
+constexpr int kCombineThreads = 128;  // x 4 values = one 512-wide latent row per pass
+constexpr int kMaxParts = 4096;       // partial slots one sequence can have
+constexpr int kUnroll = 16;           // partial rows in flight per thread
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   for (int o = 32; o >= 1; o >>= 1) {
@@ -58,8 +59,9 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 
 // One workgroup per (sequence, query row).  The slots' log-sum-exps are
-// read in parallel, reduced in LDS, and the partial rows are then summed
-// with independent loads.
+// read in parallel and reduced in LDS; then each thread sums 4 consecutive
+// values of the partial rows with kUnroll independent 16-byte loads in
+// flight.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {
   __shared__ float s_w[kMaxParts];
   __shared__ int32_t s_slot[kMaxParts];
@@ -82,7 +84,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
       n = worker_of_tile(te - 1, N, G) - g0 + 1;
     }
   }
-  float m = -INFINITY;
   for (int64_t i = tid; i < n; i += kCombineThreads) {
     int64_t slot;
     bool ok = true;
@@ -93,9 +94,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
       ok = worker_tile_begin(g, N, G) < worker_tile_begin(g + 1, N, G);
       slot = g + b;
     }
-    const float l = ok ? a.part_lse[slot * a.R + row] : -INFINITY;
+    s_slot[i] = ok ? (int32_t)slot : -1;
+  }
+  __syncthreads();
+
+  // The first kUnroll partial rows are requested before their weights are
+  // known; the log-sum-exps are read meanwhile.
+  const float* po = a.part_o + (int64_t)row * a.dc;
+  const int64_t slot_stride = (int64_t)a.R * a.dc;
+  const int d4 = tid;  // this thread's 4 values (first pass)
+  const bool d_ok = d4 < a.dc / 4;
+  float4 pre[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const int32_t sl = j < n ? s_slot[j] : -1;
+    pre[j] = d_ok && sl >= 0 ? reinterpret_cast<const float4*>(po + sl * slot_stride)[d4]
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float m = -INFINITY;
+  for (int64_t i = tid; i < n; i += kCombineThreads) {
+    const int32_t sl = s_slot[i];
+    const float l = sl >= 0 ? a.part_lse[(int64_t)sl * a.R + row] : -INFINITY;
     s_w[i] = l;
-    s_slot[i] = (int32_t)slot;
     m = fmaxf(m, l);
   }
   m = block_reduce(m, red, true);
@@ -113,27 +133,36 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
   }
   z = block_reduce(z, red, false);  // also orders the s_w writes before the reads below
   const float inv = 1.f / z;
-  for (int d = tid; d < a.dc; d += kCombineThreads) {
-    // Partial values are loaded without waiting for the weights; slots of
-    // workers that had no tiles may hold stale data and are selected away.
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int64_t i = 0;
-    for (; i + 4 <= n; i += 4) {
-      float p[4];
+  // Rows with zero weight (no visible token in that part, or a worker
+  // without tiles) are selected away, never multiplied.
+  auto accumulate = [&](float4& c, float w, const float4& p) {
+    const bool use = w != 0.f;
+    c.x = fmaf(w, use ? p.x : 0.f, c.x);
+    c.y = fmaf(w, use ? p.y : 0.f, c.y);
+    c.z = fmaf(w, use ? p.z : 0.f, c.z);
+    c.w = fmaf(w, use ? p.w : 0.f, c.w);
+  };
+  for (int dd = d4; dd < a.dc / 4; dd += kCombineThreads) {
+    float4 acc[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    int64_t i0 = 0;
+    if (dd == d4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = a.part_o[((int64_t)s_slot[i + j] * a.R + row) * a.dc + d];
-      const float w0 = s_w[i], w1 = s_w[i + 1], w2 = s_w[i + 2], w3 = s_w[i + 3];
-      acc0 = fmaf(w0, w0 != 0.f ? p[0] : 0.f, acc0);
-      acc1 = fmaf(w1, w1 != 0.f ? p[1] : 0.f, acc1);
-      acc2 = fmaf(w2, w2 != 0.f ? p[2] : 0.f, acc2);
-      acc3 = fmaf(w3, w3 != 0.f ? p[3] : 0.f, acc3);
+      for (int j = 0; j < kUnroll; ++j) accumulate(acc[j & 1], j < n ? s_w[j] : 0.f, pre[j]);
+      i0 = kUnroll;
     }
-    for (; i < n; ++i) {
-      const float p = a.part_o[((int64_t)s_slot[i] * a.R + row) * a.dc + d];
-      const float w = s_w[i];
-      acc0 = fmaf(w, w != 0.f ? p : 0.f, acc0);
+    for (; i0 < n; i0 += kUnroll) {
+      float4 p[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int32_t sl = i0 + j < n ? s_slot[i0 + j] : -1;
+        p[j] = sl >= 0 ? reinterpret_cast<const float4*>(po + sl * slot_stride)[dd] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) accumulate(acc[j & 1], i0 + j < n ? s_w[i0 + j] : 0.f, p[j]);
     }
-    a.o[out_row * a.dc + d] = ((acc0 + acc1) + (acc2 + acc3)) * inv;
+    reinterpret_cast<float4*>(a.o + out_row * a.dc)[dd] =
+        make_float4((acc[0].x + acc[1].x) * inv, (acc[0].y + acc[1].y) * inv,
+                    (acc[0].z + acc[1].z) * inv, (acc[0].w + acc[1].w) * inv);
   }
   if (a.lse && tid == 0) a.lse[out_row] = m + logf(z);
 }

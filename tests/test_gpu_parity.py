@@ -321,3 +321,34 @@ def test_full_size_sampled(kernel, q_abs, name, seqs, heads):
     assert err <= tau
     lse = step.lse.cpu().numpy()
     assert np.max(np.abs(lse[sel] - ref_lse[sel])) <= 2e-3
+
+
+def test_graph_replay_matches_eager():
+    """A whole step captured into a HIP graph gives the eager result on
+    every replay, with eager work and synchronisations between replays."""
+    from mla_paged_decode_amd import MLA_BF16
+    from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
+    wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=4, lens=("const", 1000))
+    inp = make_inputs(wl)
+    dev = DeviceBatch.upload(inp)
+    step = DecodeStep(dev, q_abs_dtype=MLA_BF16)
+    eager = step.run().clone()
+    lse_eager = step.lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step.run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step.run()
+    for rep in range(3):
+        step.out.fill_(float("nan"))
+        step.lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager), rep
+        assert torch.equal(step.lse, lse_eager), rep
+        other = DecodeStep(dev, q_abs_dtype=MLA_BF16)  # eager work between replays
+        assert torch.equal(other.run(), eager)
+        torch.cuda.synchronize()
