@@ -72,6 +72,41 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
+COUNTER_SOURCES = ["decode_mfma.hip", "schedule.h", "internal.h", "device_common.h"]
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the attention kernel's sources (counters go stale when it changes)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in COUNTER_SOURCES:
+        with open(os.path.join(ROOT, "mla_paged_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per attention-kernel launch from the committed counter
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    same counter's reading for a plain copy of known size), or None if there
+    is none or the kernel has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -81,12 +116,16 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=None,
                     help="split-KV chunks per sequence (0 = balanced; default: the workload's)")
     ap.add_argument("--kernel", choices=["auto", "simt", "mfma"], default="auto")
-    ap.add_argument("--q-abs", choices=["bf16", "f32"], default="bf16",
-                    help="absorbed-query dtype fed to the attention kernel (the SIMT kernel takes f32)")
+    ap.add_argument("--q-abs", choices=["auto", "bf16", "f32"], default="auto",
+                    help="absorbed-query dtype fed to the attention kernel; auto: f32 (hi + lo bf16 "
+                         "products) for bf16 and f32 caches, bf16 for the fp8 cache")
     ap.add_argument("--cache-bytes", type=float, default=1.0e9,
                     help="total bytes of rotated cache copies (>= 4x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB before the timed "
+                         "region, as the reference kernel for scaling byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -107,7 +146,8 @@ def main() -> int:
     wl = WORKLOADS[args.workload]
     splits = wl.num_splits if args.num_splits is None else args.num_splits
     kernel = {"auto": mla.MLA_KERNEL_AUTO, "simt": mla.MLA_KERNEL_SIMT, "mfma": mla.MLA_KERNEL_MFMA}[args.kernel]
-    qd = mla.MLA_BF16 if args.q_abs == "bf16" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
+    q_abs = args.q_abs if args.q_abs != "auto" else ("bf16" if wl.kv_format == "fp8_e4m3_e8m0" else "f32")
+    qd = mla.MLA_BF16 if q_abs == "bf16" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
 
     log(f"[bench] generating {wl.name}")
     inp = make_inputs(wl)
@@ -117,6 +157,15 @@ def main() -> int:
     copies = max(1, math.ceil(args.cache_bytes / pool_bytes))
     pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
     log(f"[bench] {copies} cache copies of {pool_bytes / 1e6:.1f} MB")
+
+    if args.calibrate_copy_mib > 0:
+        src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
 
     latent_bytes = int(np.sum(inp.seq_lens.astype(np.int64))) * inp.row_bytes
     unique_bytes = pool_bytes  # every page of the pool is referenced once or more
@@ -229,7 +278,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": counter_traffic(wl.name),
         },
         "cpu_baseline": base,
     }

@@ -287,10 +287,10 @@ def test_page_layout_invariance_and_determinism(kernel):
 
 FULL = [
     # (workload, sequences checked against the oracle, heads checked)
-    ("glm_b32_h20_ctx4096_bf16", [0, 17, 31], None),
-    ("long_b4_h20_ctx65k_203k_bf16", [1], [0, 7, 19]),
-    ("ragged_b256_h20_ctx512_8k_bf16", [0, 3, 100, 255], None),
-    ("fp8_mtp4_b64_h20_ctx16k", [0, 63], None),
+    ("glm_b32_h20_ctx4096_bf16", list(range(32)), None),
+    ("long_b4_h20_ctx65k_203k_bf16", [0, 1, 2, 3], [0, 7, 19]),
+    ("ragged_b256_h20_ctx512_8k_bf16", list(range(0, 256, 8)) + [255], None),
+    ("fp8_mtp4_b64_h20_ctx16k", list(range(0, 64, 8)) + [63], None),
 ]
 
 
@@ -299,8 +299,9 @@ FULL = [
 @pytest.mark.parametrize("name,seqs,heads", FULL)
 def test_full_size_sampled(kernel, q_abs, name, seqs, heads):
     """The whole step at full size, in the launch configuration the benchmark
-    times (matrix-core kernel, bf16 absorbed queries, the workload's split
-    mode), plus the fp32-query and vector-ALU variants."""
+    times (matrix-core kernel, the workload's split mode, fp32 absorbed
+    queries for bf16 caches and bf16 ones for the fp8 cache), plus the
+    vector-ALU kernel and the single-bf16-query mode on bf16 caches."""
     from mla_paged_decode_amd import MLA_BF16, MLA_F32
     wl = WORKLOADS[name]
     if kernel == MFMA and q_abs == "f32" and wl.heads * wl.q_per_seq > 64:
