@@ -121,7 +121,8 @@ WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
   w.part_lse_off = off;
   off = round_up(off + sizeof(float) * (size_t)w.slots * R, 256);
   w.part_o_off = off;
-  off = round_up(off + sizeof(float) * (size_t)w.slots * R * dc, 256);
+  const size_t R16 = ((size_t)R + 15) / 16 * 16;
+  off = round_up(off + sizeof(float) * (size_t)w.slots * R16 * dc, 256);
   w.total = off;
   return w;
 }
@@ -301,6 +302,7 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
   a.lse = p->lse;
 
   a.plan_in_kernel = use_mfma && B <= mla::kMaxInKernelPlan;
+  a.part_tiled = use_mfma ? 1 : 0;
   if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

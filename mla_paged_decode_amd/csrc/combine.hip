@@ -167,6 +167,137 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
   if (a.lse && tid == 0) a.lse[out_row] = m + logf(z);
 }
 
+// Merge for the tiled partial layout of the matrix-core kernel.  One
+// workgroup per (sequence, 16-row block, 4 column blocks of 16): thread t
+// owns column block 4*blockIdx.z + t/64 and lane l = t%64, i.e. column
+// 16d + l%16 of rows 16w + 4(l/16) + i, i = 0..3, which are one float4 of
+// every partial.  Per-row maxima and sums over the parts are reduced in LDS;
+// weights are computed in LDS for chunks of kChunk parts.
+constexpr int kTiledThreads = 256;
+constexpr int kChunk = 128;
+
+__global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs a) {
+  __shared__ int32_t s_slot[kMaxParts];
+  __shared__ float s_red[kTiledThreads];
+  __shared__ float s_m[16], s_z[16];
+  __shared__ float s_wt[kChunk][16];
+  const int b = blockIdx.x, w = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int row_blocks = (a.R + 15) / 16;
+  const int kdb = a.dc / 16;
+  const int d = 4 * blockIdx.z + tid / 64;
+  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+
+  int64_t g0 = 0, n = 0;
+  int64_t N = 0, G = a.workers;
+  if (a.num_splits > 0) {
+    n = a.num_splits;
+  } else {
+    const int64_t ts = a.tile_start[b], te = a.tile_start[b + 1];
+    N = a.tile_start[a.B];
+    if (ts < te) {
+      g0 = worker_of_tile(ts, N, G);
+      n = worker_of_tile(te - 1, N, G) - g0 + 1;
+    }
+  }
+  for (int64_t i = tid; i < n; i += kTiledThreads) {
+    int64_t slot;
+    bool ok = true;
+    if (a.num_splits > 0) {
+      slot = (int64_t)b * a.num_splits + i;
+    } else {
+      const int64_t gg = g0 + i;
+      ok = worker_tile_begin(gg, N, G) < worker_tile_begin(gg + 1, N, G);
+      slot = gg + b;
+    }
+    s_slot[i] = ok ? (int32_t)slot : -1;
+  }
+  __syncthreads();
+
+  // Per-row maximum and sum: thread t covers row t%16 and parts t/16, +16, ...
+  const int rr = tid & 15, r_glob = 16 * w + rr;
+  float pm = -INFINITY;
+  for (int64_t i = tid >> 4; i < n; i += kTiledThreads / 16) {
+    const int32_t sl = s_slot[i];
+    if (sl >= 0 && r_glob < a.R) pm = fmaxf(pm, a.part_lse[(int64_t)sl * a.R + r_glob]);
+  }
+  s_red[tid] = pm;
+  __syncthreads();
+  if (tid < 16) {
+    float m = -INFINITY;
+    for (int k = 0; k < kTiledThreads / 16; ++k) m = fmaxf(m, s_red[tid + 16 * k]);
+    s_m[tid] = m;
+  }
+  __syncthreads();
+  float pz = 0.f;
+  const float mr = s_m[rr];
+  if (mr != -INFINITY)
+    for (int64_t i = tid >> 4; i < n; i += kTiledThreads / 16) {
+      const int32_t sl = s_slot[i];
+      if (sl >= 0 && r_glob < a.R) {
+        const float l = a.part_lse[(int64_t)sl * a.R + r_glob];
+        pz += l == -INFINITY ? 0.f : expf(l - mr);
+      }
+    }
+  s_red[tid] = pz;
+  __syncthreads();
+  if (tid < 16) {
+    float z = 0.f;
+    for (int k = 0; k < kTiledThreads / 16; ++k) z += s_red[tid + 16 * k];
+    s_z[tid] = z;
+    const int r = 16 * w + tid;
+    if (a.lse && blockIdx.z == 0 && r < a.R)
+      a.lse[(int64_t)b * a.R + r] = s_m[tid] == -INFINITY ? -INFINITY : s_m[tid] + logf(z);
+  }
+  __syncthreads();
+
+  const float* po = a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4;
+  const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
+    const int64_t cn = min((int64_t)kChunk, n - c0);
+    // Weights of this chunk: e^(lse - m) / z, zero for empty parts.
+    for (int k = tid; k < kChunk * 16; k += kTiledThreads) {
+      const int i = k >> 4, r = k & 15, rg = 16 * w + r;
+      float wt = 0.f;
+      if (i < cn && rg < a.R) {
+        const int32_t sl = s_slot[c0 + i];
+        if (sl >= 0 && s_m[r] != -INFINITY) {
+          const float l = a.part_lse[(int64_t)sl * a.R + rg];
+          wt = l == -INFINITY ? 0.f : expf(l - s_m[r]) / s_z[r];
+        }
+      }
+      s_wt[i][r] = wt;
+    }
+    __syncthreads();
+    for (int i0 = 0; i0 < cn; i0 += kUnroll) {
+      float4 p[kUnroll];
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        const int32_t sl = i0 + j < cn ? s_slot[c0 + i0 + j] : -1;
+        p[j] = sl >= 0 ? *reinterpret_cast<const float4*>(po + sl * slot_stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kUnroll; ++j) {
+        if (i0 + j >= cn) break;
+        const float* wt = s_wt[i0 + j] + 4 * g;
+        // zero-weight parts may hold stale data: select, never multiply
+        acc.x = fmaf(wt[0], wt[0] != 0.f ? p[j].x : 0.f, acc.x);
+        acc.y = fmaf(wt[1], wt[1] != 0.f ? p[j].y : 0.f, acc.y);
+        acc.z = fmaf(wt[2], wt[2] != 0.f ? p[j].z : 0.f, acc.z);
+        acc.w = fmaf(wt[3], wt[3] != 0.f ? p[j].w : 0.f, acc.w);
+      }
+    }
+    __syncthreads();  // s_wt is rewritten by the next chunk
+  }
+  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * g + i;
+    if (r < a.R) a.o[((int64_t)b * a.R + r) * a.dc + 16 * d + li] = v[i];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
@@ -175,9 +306,14 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.B * a.R;
-  if (blocks == 0) return hipSuccess;
-  combine_kernel<<<dim3((unsigned)blocks), kCombineThreads, 0, s>>>(a);
+  if ((int64_t)a.B * a.R == 0) return hipSuccess;
+  if (a.part_tiled) {
+    if (a.dc % 64) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(a.dc / 64));
+    combine_tiled_kernel<<<grid, kTiledThreads, 0, s>>>(a);
+  } else {
+    combine_kernel<<<dim3((unsigned)((int64_t)a.B * a.R)), kCombineThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

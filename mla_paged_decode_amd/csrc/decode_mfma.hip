@@ -20,8 +20,9 @@
 //
 // Precision: with fp32 queries each query is split q = hi + lo into two bf16
 // numbers and QK^T runs twice (the cache operand is exact in bf16), which
-// keeps the scores at ~16 significant bits; P is rounded once to bf16; all
-// accumulation is fp32.  bf16 queries take a single pass.
+// keeps the scores at ~16 significant bits; P is split the same way and PV
+// also runs twice; all accumulation is fp32.  bf16 queries take a single pass
+// with P rounded once to bf16.
 //
 // Tile staging.  bf16 rows go from HBM straight into LDS with 16-byte
 // direct-to-LDS loads, NBUF-1 tiles ahead of the one being computed; their
@@ -444,8 +445,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       const int64_t qoff = ((int64_t)b * a.R + (row_ok ? row : 0)) * G::kVals + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < G::kKs; ++ks) {
-        float x[8];
-        if (a.q_f32) {
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (!row_ok) {
+          // padding rows load nothing
+        } else if (a.q_f32) {
           const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q_abs) + qoff + 32 * ks);
           const float4 u = p[0], w = p[1];
           x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
@@ -622,8 +625,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         if (__any(m != -INFINITY && mx > m + kHeadroom)) return false;
         m = m == -INFINITY ? mx : m;
       }
+      // With fp32 queries P is also split into hi + lo bf16 parts, so PV keeps
+      // ~16 significant bits of the weights; otherwise P is rounded once.
       float psum = 0.f;
-      uint32_t pk[4];
+      uint32_t pk[4], pl[4];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -631,12 +636,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           const float e0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i] - m);
           const float e1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i + 1] - m);
           psum += e0 + e1;
-          pk[2 * tb + i / 2] = pack_bf16(e0, e1);
+          const uint32_t h0 = f32_to_bf16_bits(e0), h1 = f32_to_bf16_bits(e1);
+          pk[2 * tb + i / 2] = h0 | (h1 << 16);
+          if constexpr (HILO)
+            pl[2 * tb + i / 2] = pack_bf16(e0 - bf16_bits_to_f32(h0), e1 - bf16_bits_to_f32(h1));
         }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
       lsum += psum;
       const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      bf16x8 pa_lo = pa;
+      if constexpr (HILO) pa_lo = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
 
       // ---- O += P . V, V read transposed from the tile ----
       // Column block d needs two transposed reads (tokens 4g+li/4 and 16 more)
@@ -667,6 +677,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         const bf16x8 vb = vq[d % kPrefetch];
         if (d + kPrefetch < G::kDb) vq[d % kPrefetch] = tile_v(d + kPrefetch);
         acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, acc[d], 0, 0, 0);
+        if constexpr (HILO) acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[d], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -696,14 +707,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) inv_r[i] = __shfl(inv, 4 * g + i);
     if (g == 0 && row_ok)
       a.part_lse[slot * a.R + row] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+    // Tiled partial layout: the lane's four rows of column block d are one
+    // 16-byte store, and a wave's store instruction writes 1 KB contiguously.
+    const int row_blocks = (a.R + 15) / 16;
+    if (wave < row_blocks) {
+      float* dst = a.part_o + ((slot * row_blocks + wave) * G::kDb * 64 + lane) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 16 + 4 * g + i;
-      if (r < a.R) {
-        float* dst = a.part_o + (slot * a.R + r) * G::kDc + li;
-#pragma unroll
-        for (int d = 0; d < G::kDb; ++d) dst[16 * d] = acc[d][i] * inv_r[i];
-      }
+      for (int d = 0; d < G::kDb; ++d)
+        *reinterpret_cast<float4*>(dst + 256 * d) =
+            make_float4(acc[d][0] * inv_r[0], acc[d][1] * inv_r[1], acc[d][2] * inv_r[2], acc[d][3] * inv_r[3]);
     }
   }
 }

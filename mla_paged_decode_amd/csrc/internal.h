@@ -40,7 +40,9 @@ struct DecodeArgs {
   float scale_log2;       // softmax_scale * log2(e): scores kept in base 2
   int num_splits;         // >= 1 uniform, 0 balanced
   int workers;            // balanced: worker count G
-  float* part_o;          // [slots][R][dc]
+  float* part_o;          // part_tiled ? see below : [slots][R][dc]
+  int part_tiled;         // 1: matrix-core layout [slots][ceil(R/16)][dc/16][64 lanes][4]:
+                          //    row 16w + 4(l/16) + i, column 16d + l%16 at [slot][w][d][l][i]
   float* part_lse;        // [slots][R], natural log
   int32_t* tile_start;    // balanced: [B + 1] exclusive prefix of tiles
   int plan_in_kernel;     // balanced: the decode kernel computes tile_start
@@ -53,6 +55,7 @@ struct WorkspaceLayout {
   size_t tile_start_off, part_lse_off, part_o_off, total;
   int64_t slots;
 };
+// Partial rows are padded to a multiple of 16 (the tiled layout's row blocks).
 WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits);
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
