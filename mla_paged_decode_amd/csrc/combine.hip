@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 constexpr int kCombineThreads = 128;  // x 4 values = one 512-wide latent row per pass
 constexpr int kMaxParts = 4096;       // partial slots one sequence can have
-constexpr int kUnroll = 16;           // partial rows in flight per thread
+constexpr int kUnroll = 8;            // partial rows in flight per thread
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
   for (int o = 32; o >= 1; o >>= 1) {
@@ -168,25 +168,39 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
 }
 
 // Merge for the tiled partial layout of the matrix-core kernel.  One
-// workgroup per (sequence, 16-row block, 4 column blocks of 16): thread t
-// owns column block 4*blockIdx.z + t/64 and lane l = t%64, i.e. column
-// 16d + l%16 of rows 16w + 4(l/16) + i, i = 0..3, which are one float4 of
-// every partial.  Per-row maxima and sums over the parts are reduced in LDS;
-// weights are computed in LDS for chunks of kChunk parts.
+// workgroup per (sequence, 16-row block, DPW column blocks of 16); its four
+// waves take column block 4/DPW-way interleaved shares of the parts, and
+// lane l owns column 16d + l%16 of rows 16w + 4(l/16) + i, i = 0..3, which
+// are one float4 of every partial.  Parts are processed in chunks of kChunk:
+// a first pass over the chunks' log-sum-exps gives each row's maximum and
+// sum (merged online across chunks), a second pass weights and sums the
+// partial rows.  With one chunk (the usual case) the second pass reuses the
+// slots and log-sum-exps already in LDS, and the first partial rows are
+// requested before the first pass starts.
 constexpr int kTiledThreads = 256;
-constexpr int kChunk = 128;
+constexpr int kTiledWaves = kTiledThreads / 64;
+constexpr int kChunk = 64;
 
+// 32-bit forms of the balanced-split worker ranges (tile counts < 2^22).
+__device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) {
+  return N < (1 << 22) ? (int64_t)((uint32_t)(g * N) / (uint32_t)G) : worker_tile_begin(g, N, G);
+}
+
+template <int DPW>
 __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs a) {
-  __shared__ int32_t s_slot[kMaxParts];
+  constexpr int kShare = kTiledWaves / DPW;  // waves sharing one column block
+  __shared__ int32_t s_slot[kChunk];
+  __shared__ float s_lse[kChunk][16];
   __shared__ float s_red[kTiledThreads];
   __shared__ float s_m[16], s_z[16];
-  __shared__ float s_wt[kChunk][16];
+  __shared__ float4 s_acc[kTiledWaves][64];
   const int b = blockIdx.x, w = blockIdx.y;
   const int tid = threadIdx.x;
   const int row_blocks = (a.R + 15) / 16;
   const int kdb = a.dc / 16;
-  const int d = 4 * blockIdx.z + tid / 64;
-  const int lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
+  const int d = DPW * blockIdx.z + wave / kShare;  // this wave's column block
+  const int share = wave % kShare;                 // ... and its share of the parts
 
   int64_t g0 = 0, n = 0;
   int64_t N = 0, G = a.workers;
@@ -200,95 +214,131 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
       n = worker_of_tile(te - 1, N, G) - g0 + 1;
     }
   }
-  for (int64_t i = tid; i < n; i += kTiledThreads) {
-    int64_t slot;
-    bool ok = true;
-    if (a.num_splits > 0) {
-      slot = (int64_t)b * a.num_splits + i;
-    } else {
-      const int64_t gg = g0 + i;
-      ok = worker_tile_begin(gg, N, G) < worker_tile_begin(gg + 1, N, G);
-      slot = gg + b;
-    }
-    s_slot[i] = ok ? (int32_t)slot : -1;
-  }
-  __syncthreads();
-
-  // Per-row maximum and sum: thread t covers row t%16 and parts t/16, +16, ...
-  const int rr = tid & 15, r_glob = 16 * w + rr;
-  float pm = -INFINITY;
-  for (int64_t i = tid >> 4; i < n; i += kTiledThreads / 16) {
-    const int32_t sl = s_slot[i];
-    if (sl >= 0 && r_glob < a.R) pm = fmaxf(pm, a.part_lse[(int64_t)sl * a.R + r_glob]);
-  }
-  s_red[tid] = pm;
-  __syncthreads();
-  if (tid < 16) {
-    float m = -INFINITY;
-    for (int k = 0; k < kTiledThreads / 16; ++k) m = fmaxf(m, s_red[tid + 16 * k]);
-    s_m[tid] = m;
-  }
-  __syncthreads();
-  float pz = 0.f;
-  const float mr = s_m[rr];
-  if (mr != -INFINITY)
-    for (int64_t i = tid >> 4; i < n; i += kTiledThreads / 16) {
-      const int32_t sl = s_slot[i];
-      if (sl >= 0 && r_glob < a.R) {
-        const float l = a.part_lse[(int64_t)sl * a.R + r_glob];
-        pz += l == -INFINITY ? 0.f : expf(l - mr);
+  // Slots and log-sum-exps of parts [c0, c0 + kChunk) into LDS; `between`
+  // runs once the slots are known, before the log-sum-exps are read.
+  auto load_chunk = [&](int64_t c0, auto&& between) {
+    __syncthreads();  // previous chunk's readers are done
+    if (tid < kChunk) {
+      const int64_t i = c0 + tid;
+      int32_t slot = -1;
+      if (i < n) {
+        if (a.num_splits > 0) {
+          slot = (int32_t)((int64_t)b * a.num_splits + i);
+        } else {
+          const int64_t gg = g0 + i;
+          if (tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = (int32_t)(gg + b);
+        }
       }
+      s_slot[tid] = slot;
     }
-  s_red[tid] = pz;
-  __syncthreads();
-  if (tid < 16) {
-    float z = 0.f;
-    for (int k = 0; k < kTiledThreads / 16; ++k) z += s_red[tid + 16 * k];
-    s_z[tid] = z;
-    const int r = 16 * w + tid;
-    if (a.lse && blockIdx.z == 0 && r < a.R)
-      a.lse[(int64_t)b * a.R + r] = s_m[tid] == -INFINITY ? -INFINITY : s_m[tid] + logf(z);
-  }
-  __syncthreads();
+    __syncthreads();
+    between();
+    for (int k = tid; k < kChunk * 16; k += kTiledThreads) {
+      const int i = k >> 4, r = k & 15, rg = 16 * w + r;
+      const int32_t sl = s_slot[i];
+      s_lse[i][r] = sl >= 0 && rg < a.R ? a.part_lse[(int64_t)sl * a.R + rg] : -INFINITY;
+    }
+    __syncthreads();
+  };
 
   const float* po = a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4;
   const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool lane_rows = 16 * w + 4 * g < a.R;  // lanes holding only padding rows load nothing
+  // Parts of a chunk handled by this wave: share, share + kShare, ...,
+  // loaded kBatch at a time.
+  constexpr int kPer = kChunk / kShare;
+  constexpr int kBatch = kPer < 8 ? kPer : 8;
+  float4 p[kBatch];
+  auto load_parts = [&](int64_t c0, int j0) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = share + kShare * (j0 + j);
+      const int32_t sl = c0 + i < n && lane_rows ? s_slot[i] : -1;
+      p[j] = sl >= 0 ? *reinterpret_cast<const float4*>(po + sl * slot_stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  // Pass 1: per-row maximum and sum (thread t: row t%16, parts t/16, +16, ...).
+  const int rr = tid & 15;
+  float m_run = -INFINITY, z_run = 0.f;
   for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
-    const int64_t cn = min((int64_t)kChunk, n - c0);
-    // Weights of this chunk: e^(lse - m) / z, zero for empty parts.
-    for (int k = tid; k < kChunk * 16; k += kTiledThreads) {
-      const int i = k >> 4, r = k & 15, rg = 16 * w + r;
-      float wt = 0.f;
-      if (i < cn && rg < a.R) {
-        const int32_t sl = s_slot[c0 + i];
-        if (sl >= 0 && s_m[r] != -INFINITY) {
-          const float l = a.part_lse[(int64_t)sl * a.R + rg];
-          wt = l == -INFINITY ? 0.f : expf(l - s_m[r]) / s_z[r];
-        }
-      }
-      s_wt[i][r] = wt;
+    // The first partial rows are requested with the first log-sum-exps.
+    load_chunk(c0, [&] { if (c0 == 0) load_parts(0, 0); });
+    float pm = -INFINITY;
+    for (int i = tid >> 4; i < kChunk; i += kTiledThreads / 16) pm = fmaxf(pm, s_lse[i][rr]);
+    s_red[tid] = pm;
+    __syncthreads();
+    if (tid < 16) {
+      float m = -INFINITY;
+      for (int k = 0; k < kTiledThreads / 16; ++k) m = fmaxf(m, s_red[tid + 16 * k]);
+      s_m[tid] = m;
     }
     __syncthreads();
-    for (int i0 = 0; i0 < cn; i0 += kUnroll) {
-      float4 p[kUnroll];
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int32_t sl = i0 + j < cn ? s_slot[c0 + i0 + j] : -1;
-        p[j] = sl >= 0 ? *reinterpret_cast<const float4*>(po + sl * slot_stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float mc = s_m[rr];
+    float pz = 0.f;
+    if (mc != -INFINITY)
+      for (int i = tid >> 4; i < kChunk; i += kTiledThreads / 16) {
+        const float l = s_lse[i][rr];
+        pz += l == -INFINITY ? 0.f : __expf(l - mc);
       }
+    __syncthreads();  // s_m read above
+    s_red[tid] = pz;
+    __syncthreads();
+    if (tid < 16) {
+      float z = 0.f;
+      for (int k = 0; k < kTiledThreads / 16; ++k) z += s_red[tid + 16 * k];
+      const float m_new = fmaxf(m_run, mc);
+      z_run = (m_run == -INFINITY ? 0.f : z_run * __expf(m_run - m_new)) + (mc == -INFINITY ? 0.f : z * __expf(mc - m_new));
+      m_run = m_new;
+    }
+  }
+  __syncthreads();
+  if (tid < 16) {
+    s_m[tid] = m_run;
+    s_z[tid] = z_run;
+    const int r = 16 * w + tid;
+    if (a.lse && blockIdx.z == 0 && r < a.R) a.lse[(int64_t)b * a.R + r] = m_run == -INFINITY ? -INFINITY : m_run + logf(z_run);
+  }
+  __syncthreads();
+
+  // Pass 2: weights e^(lse - m) / z, zero for empty parts; zero-weight parts
+  // may hold stale data and are selected away, never multiplied.
+  float m4[4], iz4[4];
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        if (i0 + j >= cn) break;
-        const float* wt = s_wt[i0 + j] + 4 * g;
-        // zero-weight parts may hold stale data: select, never multiply
-        acc.x = fmaf(wt[0], wt[0] != 0.f ? p[j].x : 0.f, acc.x);
-        acc.y = fmaf(wt[1], wt[1] != 0.f ? p[j].y : 0.f, acc.y);
-        acc.z = fmaf(wt[2], wt[2] != 0.f ? p[j].z : 0.f, acc.z);
-        acc.w = fmaf(wt[3], wt[3] != 0.f ? p[j].w : 0.f, acc.w);
+  for (int k = 0; k < 4; ++k) {
+    m4[k] = s_m[4 * g + k];
+    iz4[k] = s_z[4 * g + k] > 0.f ? 1.f / s_z[4 * g + k] : 0.f;
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
+    if (c0 > 0 || n > kChunk) load_chunk(c0, [] {});  // pass 1 left the last chunk in LDS
+    for (int j0 = 0; j0 < kPer && c0 + share + kShare * j0 < n; j0 += kBatch) {
+      if (c0 > 0 || j0 > 0) load_parts(c0, j0);
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = share + kShare * (j0 + j);
+        const bool valid = c0 + i < n;
+        const float pv[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+        float r[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float l = valid ? s_lse[i][4 * g + k] : -INFINITY;
+          const float wt = l == -INFINITY || m4[k] == -INFINITY ? 0.f : __expf(l - m4[k]) * iz4[k];
+          r[k] = wt != 0.f ? wt * pv[k] : 0.f;
+        }
+        acc.x += r[0]; acc.y += r[1]; acc.z += r[2]; acc.w += r[3];
       }
     }
-    __syncthreads();  // s_wt is rewritten by the next chunk
+  }
+  if constexpr (kShare > 1) {
+    s_acc[wave][lane] = acc;
+    __syncthreads();
+    if (share != 0) return;
+#pragma unroll
+    for (int k = 1; k < kShare; ++k) {
+      const float4 o = s_acc[wave + k][lane];
+      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+    }
   }
   const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
@@ -308,9 +358,14 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   if ((int64_t)a.B * a.R == 0) return hipSuccess;
   if (a.part_tiled) {
-    if (a.dc % 64) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(a.dc / 64));
-    combine_tiled_kernel<<<grid, kTiledThreads, 0, s>>>(a);
+    // Few parts per sequence: each wave takes its own column block (DPW = 4);
+    // many parts: the four waves share one column block and split the parts.
+    const int64_t parts = a.num_splits > 0 ? a.num_splits : (a.workers + a.B - 1) / a.B + 1;
+    const int dpw = parts > 32 ? 1 : 4;
+    if (a.dc % (16 * dpw)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(a.dc / (16 * dpw)));
+    if (dpw == 1) combine_tiled_kernel<1><<<grid, kTiledThreads, 0, s>>>(a);
+    else combine_tiled_kernel<4><<<grid, kTiledThreads, 0, s>>>(a);
   } else {
     combine_kernel<<<dim3((unsigned)((int64_t)a.B * a.R)), kCombineThreads, 0, s>>>(a);
   }

@@ -710,7 +710,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     // Tiled partial layout: the lane's four rows of column block d are one
     // 16-byte store, and a wave's store instruction writes 1 KB contiguously.
     const int row_blocks = (a.R + 15) / 16;
-    if (wave < row_blocks) {
+    if (wave < row_blocks && wave * 16 + 4 * g < a.R) {  // lanes with only padding rows skip
       float* dst = a.part_o + ((slot * row_blocks + wave) * G::kDb * 64 + lane) * 4;
 #pragma unroll
       for (int d = 0; d < G::kDb; ++d)

@@ -71,7 +71,10 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   bf16x8 qa[NKS];
   const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qa[ks] = n_ok ? load_bf16x8(q + 32 * ks + 8 * g) : zero;
+  for (int ks = 0; ks < NKS; ++ks) {
+    qa[ks] = load_bf16x8(q + 32 * ks + 8 * g);  // padding tokens read token 0 ...
+    if (!n_ok) qa[ks] = zero;                   // ... and use zeros
+  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = j * 64 * kWaves + threadIdx.x;
@@ -136,12 +139,10 @@ __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) 
     float4 raw[kStep][2];
 #pragma unroll
     for (int j = 0; j < kStep && k0 + j < NKS; ++j) {
-      if (n_ok) {
-        raw[j][0] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g);
-        raw[j][1] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g + 4);
-      } else {
-        raw[j][0] = raw[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      // Padding tokens read token 0 (no branch around the loads) and use zeros.
+      raw[j][0] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g);
+      raw[j][1] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g + 4);
+      if (!n_ok) raw[j][0] = raw[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int j = 0; j < kStep && k0 + j < NKS; ++j) {
