@@ -168,18 +168,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
 }
 
 // Merge for the tiled partial layout of the matrix-core kernel.  One
-// workgroup per (sequence, 16-row block, DPW column blocks of 16); its four
-// waves take column block 4/DPW-way interleaved shares of the parts, and
-// lane l owns column 16d + l%16 of rows 16w + 4(l/16) + i, i = 0..3, which
-// are one float4 of every partial.  Parts are processed in chunks of kChunk:
-// a first pass over the chunks' log-sum-exps gives each row's maximum and
-// sum (merged online across chunks), a second pass weights and sums the
-// partial rows.  With one chunk (the usual case) the second pass reuses the
-// slots and log-sum-exps already in LDS, and the first partial rows are
-// requested before the first pass starts.
+// workgroup per (sequence, 16-row block, DPW column blocks of 16).  Lane l of
+// a wave owns column 16d + l%16 of rows 16w + 4(l/16) + i, i = 0..3, which
+// are one float4 of every partial.  With DPW >= 4 each wave takes DPW/4
+// column blocks and all the parts; with DPW < 4, 4/DPW waves share a column
+// block, split its parts and are summed in LDS at the end.  Parts are
+// processed in chunks of kChunk: a first pass over the chunks' log-sum-exps
+// gives each row's maximum and sum (merged online across chunks), a second
+// pass weights and sums the partial rows.  With one chunk (the usual case)
+// the second pass reuses the slots and weights already in LDS, and the
+// first partial rows are requested with the first log-sum-exps.
 constexpr int kTiledThreads = 256;
 constexpr int kTiledWaves = kTiledThreads / 64;
-constexpr int kChunk = 64;
+constexpr int kChunk = 256;
 
 // 32-bit forms of the balanced-split worker ranges (tile counts < 2^22).
 __device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) {
@@ -188,9 +189,10 @@ __device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) 
 
 template <int DPW>
 __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs a) {
-  constexpr int kShare = kTiledWaves / DPW;  // waves sharing one column block
+  constexpr int kShare = DPW >= kTiledWaves ? 1 : kTiledWaves / DPW;  // waves per column block
+  constexpr int kDW = DPW >= kTiledWaves ? DPW / kTiledWaves : 1;     // column blocks per wave
   __shared__ int32_t s_slot[kChunk];
-  __shared__ float s_lse[kChunk][16];
+  __shared__ float s_lse[kChunk][16];  // log-sum-exps, then weights
   __shared__ float s_red[kTiledThreads];
   __shared__ float s_m[16], s_z[16];
   __shared__ float4 s_acc[kTiledWaves][64];
@@ -199,8 +201,8 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   const int row_blocks = (a.R + 15) / 16;
   const int kdb = a.dc / 16;
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, li = lane & 15;
-  const int d = DPW * blockIdx.z + wave / kShare;  // this wave's column block
-  const int share = wave % kShare;                 // ... and its share of the parts
+  const int d0 = DPW * blockIdx.z + (wave / kShare) * kDW;  // this wave's first column block
+  const int share = wave % kShare;                         // ... and its share of the parts
 
   int64_t g0 = 0, n = 0;
   int64_t N = 0, G = a.workers;
@@ -218,8 +220,8 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   // runs once the slots are known, before the log-sum-exps are read.
   auto load_chunk = [&](int64_t c0, auto&& between) {
     __syncthreads();  // previous chunk's readers are done
-    if (tid < kChunk) {
-      const int64_t i = c0 + tid;
+    for (int t = tid; t < kChunk; t += kTiledThreads) {
+      const int64_t i = c0 + t;
       int32_t slot = -1;
       if (i < n) {
         if (a.num_splits > 0) {
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
           if (tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = (int32_t)(gg + b);
         }
       }
-      s_slot[tid] = slot;
+      s_slot[t] = slot;
     }
     __syncthreads();
     between();
@@ -241,15 +243,16 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
     __syncthreads();
   };
 
-  const float* po = a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4;
   const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
   const bool lane_rows = 16 * w + 4 * g < a.R;  // lanes holding only padding rows load nothing
+  auto part_ptr = [&](int d) { return a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4; };
   // Parts of a chunk handled by this wave: share, share + kShare, ...,
   // loaded kBatch at a time.
   constexpr int kPer = kChunk / kShare;
-  constexpr int kBatch = kPer < 8 ? kPer : 8;
+  constexpr int kBatch = kShare > 1 ? 16 : 8;
   float4 p[kBatch];
-  auto load_parts = [&](int64_t c0, int j0) {
+  auto load_parts = [&](int64_t c0, int j0, int d) {
+    const float* po = part_ptr(d);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = share + kShare * (j0 + j);
@@ -262,8 +265,7 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   const int rr = tid & 15;
   float m_run = -INFINITY, z_run = 0.f;
   for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
-    // The first partial rows are requested with the first log-sum-exps.
-    load_chunk(c0, [&] { if (c0 == 0) load_parts(0, 0); });
+    load_chunk(c0, [&] { if (c0 == 0) load_parts(0, 0, d0); });
     float pm = -INFINITY;
     for (int i = tid >> 4; i < kChunk; i += kTiledThreads / 16) pm = fmaxf(pm, s_lse[i][rr]);
     s_red[tid] = pm;
@@ -299,52 +301,63 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
     const int r = 16 * w + tid;
     if (a.lse && blockIdx.z == 0 && r < a.R) a.lse[(int64_t)b * a.R + r] = m_run == -INFINITY ? -INFINITY : m_run + logf(z_run);
   }
-  __syncthreads();
 
   // Pass 2: weights e^(lse - m) / z, zero for empty parts; zero-weight parts
   // may hold stale data and are selected away, never multiplied.
-  float m4[4], iz4[4];
+  auto to_weights = [&]() {
+    __syncthreads();  // s_m, s_z and the chunk's log-sum-exps are complete
+    for (int k = tid; k < kChunk * 16; k += kTiledThreads) {
+      const int i = k >> 4, r = k & 15;
+      const float l = s_lse[i][r];
+      s_lse[i][r] = l == -INFINITY || s_m[r] == -INFINITY ? 0.f : __expf(l - s_m[r]) / s_z[r];
+    }
+    __syncthreads();
+  };
+  float4 acc[kDW];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    m4[k] = s_m[4 * g + k];
-    iz4[k] = s_z[4 * g + k] > 0.f ? 1.f / s_z[4 * g + k] : 0.f;
-  }
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int dd = 0; dd < kDW; ++dd) acc[dd] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t c0 = 0; c0 < n; c0 += kChunk) {
     if (c0 > 0 || n > kChunk) load_chunk(c0, [] {});  // pass 1 left the last chunk in LDS
-    for (int j0 = 0; j0 < kPer && c0 + share + kShare * j0 < n; j0 += kBatch) {
-      if (c0 > 0 || j0 > 0) load_parts(c0, j0);
+    to_weights();
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = share + kShare * (j0 + j);
-        const bool valid = c0 + i < n;
-        const float pv[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
-        float r[4];
+    for (int dd = 0; dd < kDW; ++dd) {
+      for (int j0 = 0; j0 < kPer && c0 + share + kShare * j0 < n; j0 += kBatch) {
+        if (c0 > 0 || j0 > 0 || dd > 0) load_parts(c0, j0, d0 + dd);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float l = valid ? s_lse[i][4 * g + k] : -INFINITY;
-          const float wt = l == -INFINITY || m4[k] == -INFINITY ? 0.f : __expf(l - m4[k]) * iz4[k];
-          r[k] = wt != 0.f ? wt * pv[k] : 0.f;
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = share + kShare * (j0 + j);
+          const float* wt = s_lse[i < kChunk ? i : 0] + 4 * g;
+          const bool valid = c0 + i < n;
+          const float pv[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+          float r[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float wk = valid ? wt[k] : 0.f;
+            r[k] = wk != 0.f ? wk * pv[k] : 0.f;
+          }
+          acc[dd].x += r[0]; acc[dd].y += r[1]; acc[dd].z += r[2]; acc[dd].w += r[3];
         }
-        acc.x += r[0]; acc.y += r[1]; acc.z += r[2]; acc.w += r[3];
       }
     }
   }
   if constexpr (kShare > 1) {
-    s_acc[wave][lane] = acc;
+    s_acc[wave][lane] = acc[0];
     __syncthreads();
     if (share != 0) return;
 #pragma unroll
     for (int k = 1; k < kShare; ++k) {
       const float4 o = s_acc[wave + k][lane];
-      acc.x += o.x; acc.y += o.y; acc.z += o.z; acc.w += o.w;
+      acc[0].x += o.x; acc[0].y += o.y; acc[0].z += o.z; acc[0].w += o.w;
     }
   }
-  const float v[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * g + i;
-    if (r < a.R) a.o[((int64_t)b * a.R + r) * a.dc + 16 * d + li] = v[i];
+  for (int dd = 0; dd < kDW; ++dd) {
+    const float v[4] = {acc[dd].x, acc[dd].y, acc[dd].z, acc[dd].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * g + i;
+      if (r < a.R) a.o[((int64_t)b * a.R + r) * a.dc + 16 * (d0 + dd) + li] = v[i];
+    }
   }
 }
 
@@ -358,14 +371,24 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   if ((int64_t)a.B * a.R == 0) return hipSuccess;
   if (a.part_tiled) {
-    // Few parts per sequence: each wave takes its own column block (DPW = 4);
-    // many parts: the four waves share one column block and split the parts.
+    // About 1024 workgroups: DPW column blocks per workgroup, a power of two
+    // dividing dc/16; many parts per sequence favour DPW < 4 (waves share a
+    // column block and split its parts).
+    const int kdb = a.dc / 16;
+    const int64_t cells = (int64_t)a.B * ((a.R + 15) / 16) * kdb;
     const int64_t parts = a.num_splits > 0 ? a.num_splits : (a.workers + a.B - 1) / a.B + 1;
-    const int dpw = parts > 32 ? 1 : 4;
-    if (a.dc % (16 * dpw)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(a.dc / (16 * dpw)));
-    if (dpw == 1) combine_tiled_kernel<1><<<grid, kTiledThreads, 0, s>>>(a);
-    else combine_tiled_kernel<4><<<grid, kTiledThreads, 0, s>>>(a);
+    int dpw = 1;
+    while (dpw < 32 && cells / (2 * dpw) >= 1024 && kdb % (2 * dpw) == 0) dpw *= 2;
+    if (parts > 32 && dpw > 1) dpw = 1;
+    const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(kdb / dpw));
+    switch (dpw) {
+      case 1: combine_tiled_kernel<1><<<grid, kTiledThreads, 0, s>>>(a); break;
+      case 2: combine_tiled_kernel<2><<<grid, kTiledThreads, 0, s>>>(a); break;
+      case 4: combine_tiled_kernel<4><<<grid, kTiledThreads, 0, s>>>(a); break;
+      case 8: combine_tiled_kernel<8><<<grid, kTiledThreads, 0, s>>>(a); break;
+      case 16: combine_tiled_kernel<16><<<grid, kTiledThreads, 0, s>>>(a); break;
+      default: combine_tiled_kernel<32><<<grid, kTiledThreads, 0, s>>>(a); break;
+    }
   } else {
     combine_kernel<<<dim3((unsigned)((int64_t)a.B * a.R)), kCombineThreads, 0, s>>>(a);
   }
