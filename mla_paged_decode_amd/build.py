@@ -26,6 +26,7 @@ SOURCES = [
     "combine.hip",
     "decode_simt.hip",
     "decode_mfma.hip",
+    "decode_fp8.hip",
     "proj_simt.hip",
     "proj_mfma.hip",
 ]

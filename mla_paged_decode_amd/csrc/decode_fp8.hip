@@ -1,0 +1,416 @@
+// Split-KV paged MLA decode for the fp8 cache on the matrix cores (gfx950),
+// for up to 128 query rows per sequence (several query tokens per sequence,
+// as in a multi-token-prediction verify step).
+//
+// The cached row is 528 B: 512 e4m3 values (448 latent, then 64 RoPE) and 16
+// e8m0 scales, one per 32 values (the GLM-4.7-Flash model record, ENGINE
+// KERNEL CONSTRAINTS item (2)).  Per tile of 32 tokens:
+//   1. the raw rows (one contiguous 16.5 KB block when the tile lies in one
+//      page) go from HBM to an LDS ring with direct-to-LDS loads, kRaw - 1
+//      tiles ahead of the one being computed;
+//   2. all waves decode the raw tile into a bf16 tile, value * 2^(E-127),
+//      which is exact (3 mantissa bits fit bf16's 7, the exponents fit);
+//   3. QK^T and PV run on v_mfma_f32_16x16x32_bf16 exactly as in the bf16
+//      kernel (same operand layouts and swizzled bf16 tile), except that each
+//      wave owns two 16-row blocks: every tile operand read from LDS feeds two
+//      MFMAs, which halves LDS reads per MFMA.
+// A wave holds 2 x 16 rows of bf16 queries (128 VGPRs) and 2 x 16 x 448
+// fp32 accumulators (224 AGPRs), so one wave runs per SIMD: one workgroup
+// of ceil(R / 32) waves per CU, 256 balanced workers.
+//
+// Online softmax, the rescale-free main loop and the partial layout follow
+// the bf16 kernel: per row a reference maximum kept while scores stay
+// within 2^64 of it; a tile that would exceed it sends the wave to a second
+// loop that rescales.  Partials use the tiled matrix-core layout.
+#include <cmath>
+#include <type_traits>
+
+#include "decode_common.h"
+#include "device_common.h"
+#include "internal.h"
+#include "schedule.h"
+
+namespace mla {
+namespace {
+
+using namespace mfma;
+
+constexpr int kDc = 448;                       // latent width of the fp8 row
+constexpr int kVals = kDc + kDr;               // 512 values per row
+constexpr int kKs = kVals / 32;                // 16 QK k-steps
+constexpr int kKsLat = kDc / 32;               // 14 over the latent
+constexpr int kDb = kDc / 16;                  // 28 PV column blocks
+constexpr int kRowBytes = kVals + kVals / 32;  // 528
+constexpr int kRawChunks = kTile * kRowBytes / 16;           // 1056 16-B chunks per tile
+constexpr int kRawInst = (kRawChunks + 63) / 64;             // 17 wave loads per tile
+constexpr int kRawBuf = kRawInst * 1024;                     // raw buffer stride
+constexpr int kRaw = 4;                                      // raw ring depth
+// Converted bf16 tile, as in the bf16 kernel: latent rows (56 chunks) then
+// the RoPE rows (8 chunks), chunks XOR-swizzled by token.
+constexpr int kLatRow = kDc * 2;                   // 896
+constexpr int kRopeRow = kDr * 2;                  // 128
+constexpr int kRopeBase = kTile * kLatRow;         // 28672
+constexpr int kTileBytes = kRopeBase + kTile * kRopeRow;  // 32768
+
+// Raw tile loads: wave w issues instructions w, w + NW, ...; instruction k
+// covers chunks 64k .. 64k + 63 of the tile (row q / 33, chunk q % 33).
+template <int NW>
+struct RawStaging {
+  static constexpr int kMinOps = kRawInst / NW;  // fewest loads any wave issues per tile
+
+  __device__ __forceinline__ static void load(const TileSrc& ts, lds_char* buf) {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    if (ts.n == kTile && ts.kb >= kTile) {  // whole tile in one page: one contiguous block
+#pragma unroll
+      for (int i = 0; i < (kRawInst + NW - 1) / NW; ++i) {
+        const int k = wave + NW * i;
+        if (NW * i + NW <= kRawInst || k < kRawInst) {
+          const int q = min(64 * k + lane, kRawChunks - 1);
+          dma16((const void*)(uintptr_t)ts.base0, 16u * q, buf + 1024 * k);
+        }
+      }
+      return;
+    }
+    // Last tile of a unit (rows past its end repeat the last valid one), or
+    // a tile across two pages of 16 tokens.
+#pragma unroll
+    for (int i = 0; i < (kRawInst + NW - 1) / NW; ++i) {
+      const int k = wave + NW * i;
+      if (NW * i + NW <= kRawInst || k < kRawInst) {
+        const int q = min(64 * k + lane, kRawChunks - 1);
+        const int row = min(q / 33, ts.n - 1), c = q % 33;
+        const uint64_t base = row < ts.kb ? ts.base0 : ts.base1;
+        dma16_vaddr((const void*)(uintptr_t)(base + (uint64_t)(row * kRowBytes + 16 * c)), buf + 1024 * k);
+      }
+    }
+  }
+};
+
+// Decode a raw tile into the bf16 tile: unit u = (token u / 32, value chunk
+// u % 32 of 16 values), spread over all threads of the workgroup.
+template <int NW>
+__device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile) {
+  for (int u = threadIdx.x; u < kTile * 32; u += 64 * NW) {
+    const int tok = u >> 5, c = u & 31;
+    const lds_char* src = raw + tok * kRowBytes;
+    const u32x4 v = *(const lds_u32x4*)(src + 16 * c);
+    const float scale = e8m0_to_f32((uint32_t)(uint8_t)src[kVals + (c >> 1)]);
+    // e4m3 * 2^(E-127) is exact in bf16, so the bf16 value is the upper half
+    // of the fp32 product (no rounding step).
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
+      o[2 * i + 0] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[1] * scale),
+                                           __builtin_bit_cast(uint32_t, lo[0] * scale), 0x07060302u);
+      o[2 * i + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi[1] * scale),
+                                           __builtin_bit_cast(uint32_t, hi[0] * scale), 0x07060302u);
+    }
+    const int c0 = 2 * c;  // first bf16 chunk of these 16 values
+    lds_char* d0 = c0 < kDc / 8 ? tile + lds_off(tok, c0, kLatRow)
+                                : tile + kRopeBase + lds_off(tok, c0 - kDc / 8, kRopeRow);
+    lds_char* d1 = c0 < kDc / 8 ? tile + lds_off(tok, c0 + 1, kLatRow)
+                                : tile + kRopeBase + lds_off(tok, c0 + 1 - kDc / 8, kRopeRow);
+    *(lds_u32x4*)d0 = u32x4{o[0], o[1], o[2], o[3]};
+    *(lds_u32x4*)d1 = u32x4{o[4], o[5], o[6], o[7]};
+  }
+}
+
+template <int NW, int kRBW>
+__global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char tile_mem[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char raw_mem[kRaw * kRawBuf];
+  __shared__ int32_t s_ts[kMaxInKernelPlan + 1];
+  __shared__ int32_t s_scan[64 * NW];
+  __shared__ int32_t s_lens[kMaxInKernelPlan];
+  lds_char* const tile = (lds_char*)tile_mem;
+  lds_char* const raws = (lds_char*)raw_mem;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+  const int row_blocks = (a.R + 15) / 16;
+
+  const int32_t* ts = a.tile_start;
+  if (a.num_splits == 0 && a.plan_in_kernel) {
+    block_plan(a.seq_lens, a.B, s_ts, s_scan, s_lens);
+    if (blockIdx.x == 0)  // publish the plan for the merge kernel
+      for (int i = threadIdx.x; i <= a.B; i += 64 * NW) a.tile_start[i] = s_ts[i];
+    ts = s_ts;
+  }
+  constexpr int D = kRaw - 1;  // raw tiles in flight ahead of the one being decoded
+  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens);
+  Unit unit;
+  while (unit_it.next(a, unit)) {
+    const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
+    const int64_t slot = a.num_splits > 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x + b;
+    const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
+    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+
+    // ---- queries (bf16, B-operand layout) of this wave's two row blocks ----
+    // Loaded and waited for before any tile transfer, so that later waits
+    // on the transfers are not mixed up with the query loads.
+    bf16x8 q[kRBW][kKs];
+#pragma unroll
+    for (int r = 0; r < kRBW; ++r) {
+      const int row = (kRBW * wave + r) * 16 + li;
+      const bool ok = row < a.R;
+      const uint16_t* src = static_cast<const uint16_t*>(a.q_abs) + ((int64_t)b * a.R + (ok ? row : 0)) * kVals + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        q[r][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * ks));
+        if (!ok) q[r][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
+    }
+    wait_vmcnt_lgkm0<0>();
+
+    f32x4 acc[kRBW][kDb];
+#pragma unroll
+    for (int r = 0; r < kRBW; ++r)
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) acc[r][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[kRBW], lsum[kRBW];
+#pragma unroll
+    for (int r = 0; r < kRBW; ++r) {
+      m[r] = -INFINITY;
+      lsum[r] = 0.f;
+    }
+
+    TilePages pages_next;
+    if (ntiles > 0) {
+      lds_barrier();  // the previous unit's readers of the tile and ring are done
+#pragma unroll
+      for (int x = 0; x < D; ++x)
+        if (x < ntiles) RawStaging<NW>::load(tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), raws + (x % kRaw) * kRawBuf);
+      if (D < ntiles) pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
+    }
+
+    // One pipeline step: tile `it` has landed in the ring (everyone's part),
+    // the transfer of tile it + D starts into the buffer tile it-1 used, and
+    // tile `it` is decoded into the bf16 tile once everyone is done with
+    // tile it-1.
+    auto step = [&](int it) __attribute__((always_inline)) {
+      const int younger = min(D - 1, ntiles - 1 - it);
+      constexpr int M = RawStaging<NW>::kMinOps;
+      if (younger >= 2) wait_vmcnt_lgkm0<2 * M>();
+      else if (younger == 1) wait_vmcnt_lgkm0<M>();
+      else wait_vmcnt_lgkm0<0>();
+      lds_barrier();  // tile `it` landed; everyone finished tile it-1
+      const int x = it + D;
+      if (x < ntiles) {
+        RawStaging<NW>::load(tile_src(a, pages_next, t1), raws + (x % kRaw) * kRawBuf);
+        if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+      }
+      decode_tile<NW>(raws + (it % kRaw) * kRawBuf, tile);
+      wait_lgkm0();
+      lds_barrier();  // the bf16 tile is complete
+    };
+
+    constexpr float kHeadroom = 64.f;
+    auto compute = [&](int it, auto rescale_tag) __attribute__((always_inline)) -> bool {
+      constexpr bool kRescale = decltype(rescale_tag)::value;
+      const int tt0 = t0 + it * kTile;
+
+      // ---- S^T = Tile . Q^T: two token blocks x two row blocks ----
+      f32x4 s[2][kRBW];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) s[tb][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const lds_char* lat_base[2][2];
+      const lds_char* rope_base[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int tok = tb * 16 + li;
+        const int xs = swz(tok);
+        const int flip = 64 * (xs >> 2);
+        const lds_char* bl = tile + tok * kLatRow + 16 * (g ^ (xs & 3));
+        const lds_char* br = tile + kRopeBase + tok * kRopeRow + 16 * (g ^ (xs & 3));
+        lat_base[tb][0] = bl + flip;
+        lat_base[tb][1] = bl - flip;
+        rope_base[tb][0] = br + flip;
+        rope_base[tb][1] = br - flip;
+      }
+      auto tile_a = [&](int ks, int tb) {
+        const lds_char* p = ks < kKsLat ? lat_base[tb][ks & 1] + 64 * ks : rope_base[tb][ks & 1] + 64 * (ks - kKsLat);
+        return *(const lds_bf16x8*)p;
+      };
+      constexpr int kAhead = 2;
+      bf16x8 ta[kAhead][2];
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k) {
+        ta[k][0] = tile_a(k, 0);
+        ta[k][1] = tile_a(k, 1);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        const bf16x8 a0 = ta[ks % kAhead][0], a1 = ta[ks % kAhead][1];
+        if (ks + kAhead < kKs) {
+          ta[ks % kAhead][0] = tile_a(ks + kAhead, 0);
+          ta[ks % kAhead][1] = tile_a(ks + kAhead, 1);
+        }
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) {
+          s[0][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, q[r][ks], s[0][r], 0, 0, 0);
+          s[1][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, q[r][ks], s[1][r], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- online softmax per row block ----
+      float sv[kRBW][2][4], mx[kRBW];
+#pragma unroll
+      for (int r = 0; r < kRBW; ++r) {
+        const int row = (kRBW * wave + r) * 16 + li;
+        const bool row_ok = row < a.R;
+        const int last_visible = L - a.Sq + (row_ok ? row / a.H : 0);
+        mx[r] = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tt0 + tb * 16 + 4 * g + i;
+            const bool ok = row_ok && t < t1 && t <= last_visible;
+            sv[r][tb][i] = ok ? s[tb][r][i] * a.scale_log2 : -INFINITY;
+            mx[r] = fmaxf(mx[r], sv[r][tb][i]);
+          }
+        mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 16));
+        mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 32));
+      }
+      if constexpr (kRescale) {
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) {
+          const bool raise = mx[r] > m[r] + 8.f;
+          if (__any(raise)) {
+            const float m_new = raise ? mx[r] : m[r];
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[r] - m_new);
+            lsum[r] *= alpha;
+            m[r] = m_new;
+            float al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+            for (int d = 0; d < kDb; ++d)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[r][d][i] *= al[i];
+          }
+        }
+      } else {
+        bool over = false;
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) over = over || (m[r] != -INFINITY && mx[r] > m[r] + kHeadroom);
+        if (__any(over)) return false;
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) m[r] = m[r] == -INFINITY ? mx[r] : m[r];
+      }
+      bf16x8 pa[kRBW];
+#pragma unroll
+      for (int r = 0; r < kRBW; ++r) {
+        float psum = 0.f;
+        uint32_t pk[4];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float e0 = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][tb][i] - m[r]);
+            const float e1 = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][tb][i + 1] - m[r]);
+            psum += e0 + e1;
+            pk[2 * tb + i / 2] = pack_bf16(e0, e1);
+          }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        lsum[r] += psum;
+        pa[r] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+      }
+
+      // ---- O += P . V for both row blocks, V read transposed once ----
+      const lds_char* vbase[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int tok = 16 * half + 4 * g + (li >> 2);
+        const int xs = swz(tok);
+        const int h = (li & 3) >> 1;
+        const lds_char* b0 = tile + tok * kLatRow + 16 * (h ^ (xs & 1)) + 8 * (li & 1);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) vbase[half][rr] = b0 + 32 * (rr ^ (xs >> 1));
+      }
+      auto tile_v = [&](int d) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[0][d & 3] + 128 * (d >> 2)));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[1][d & 3] + 128 * (d >> 2)));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      constexpr int kPrefetch = 4;
+      bf16x8 vq[kPrefetch];
+#pragma unroll
+      for (int d = 0; d < kPrefetch; ++d) vq[d] = tile_v(d);
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) {
+        const bf16x8 vb = vq[d % kPrefetch];
+        if (d + kPrefetch < kDb) vq[d % kPrefetch] = tile_v(d + kPrefetch);
+#pragma unroll
+        for (int r = 0; r < kRBW; ++r) acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[r], vb, acc[r][d], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return true;
+    };
+
+    int it = 0;
+    for (; it < ntiles; ++it) {
+      step(it);
+      if (!compute(it, std::false_type{})) break;
+    }
+    if (it < ntiles) {  // tile `it` is decoded but not yet computed
+      compute(it, std::true_type{});
+      for (++it; it < ntiles; ++it) {
+        step(it);
+        compute(it, std::true_type{});
+      }
+    }
+
+    // ---- normalise and write this unit's partials (tiled layout) ----
+#pragma unroll
+    for (int r = 0; r < kRBW; ++r) {
+      const int rb = kRBW * wave + r;
+      const int row = rb * 16 + li;
+      const float inv = lsum[r] > 0.f ? 1.f / lsum[r] : 0.f;
+      float inv_r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) inv_r[i] = __shfl(inv, 4 * g + i);
+      if (g == 0 && row < a.R)
+        a.part_lse[slot * a.R + row] = lsum[r] > 0.f ? (m[r] + log2f(lsum[r])) * kLn2 : -INFINITY;
+      if (rb < row_blocks && rb * 16 + 4 * g < a.R) {
+        float* dst = a.part_o + ((slot * row_blocks + rb) * kDb * 64 + lane) * 4;
+#pragma unroll
+        for (int d = 0; d < kDb; ++d)
+          *reinterpret_cast<float4*>(dst + 256 * d) =
+              make_float4(acc[r][d][0] * inv_r[0], acc[r][d][1] * inv_r[1], acc[r][d][2] * inv_r[2],
+                          acc[r][d][3] * inv_r[3]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Workgroups of ceil(R / 32) waves, one per CU (the accumulators of two row
+// blocks fill a SIMD's registers).
+bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32) {
+  return fmt == kFP8 && dc == kDc && dr == kDr && !q_f32 && R >= 1 && R <= 128;
+}
+
+hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s) {
+  const unsigned units = a.num_splits > 0 ? (unsigned)(a.B * a.num_splits) : (unsigned)a.workers;
+  switch ((a.R + 15) / 16) {
+#define MLA_CASE(N) \
+  case N: decode_fp8_kernel<(N < 2 ? 2 : N), 1><<<units, 64 * (N < 2 ? 2 : N), 0, s>>>(a); break;
+    MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
+#undef MLA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -39,6 +39,7 @@
 #include <cmath>
 #include <type_traits>
 
+#include "decode_common.h"
 #include "device_common.h"
 #include "internal.h"
 #include "schedule.h"
@@ -46,22 +47,7 @@
 namespace mla {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-// The block table is read-only during a call: reading it through the
-// constant address space lets the compiler use scalar loads.
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-
-constexpr int kTile = 32;      // tokens per tile
-constexpr int kDr = 64;        // RoPE dims
-constexpr float kLn2 = 0.693147180559945309f;
+using namespace mfma;
 
 template <int FMT>
 struct Geo {
@@ -77,143 +63,6 @@ struct Geo {
   static constexpr int kTileBytes = kRopeBase + kTile * kRopeRow;
   static constexpr int kSrcChunks = kVals / 16;             // stored fp8 16-value chunks per row
 };
-
-// Swizzle of 16-B chunk index within a row: a permutation of 0..7 on the
-// token's low 3 bits such that 8 consecutive tokens get 8 distinct values
-// and each 4 consecutive tokens get 4 distinct chunk pairs.
-__device__ __forceinline__ int swz(int tok) { return ((tok & 3) << 1) | ((tok >> 2) & 1); }
-
-// Byte offset of 16-B chunk `chunk` of token `tok` in a region with the
-// given row stride (rows are a multiple of 8 chunks).
-__device__ __forceinline__ int lds_off(int tok, int chunk, int row_bytes) {
-  return tok * row_bytes + 16 * (chunk ^ swz(tok));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Source of one tile: tokens [tt0, tt0 + n) of the current sequence.  Work
-// units start at multiples of kTile tokens and page_block is a power of two
-// >= 16, so the tile lies in one page (page_block >= 32) or two (16).  Tile
-// token k is read from row kk = min(k, n - 1) (tokens past the end repeat the
-// last valid one, so every row read holds finite values), at
-//   (kk < kb ? base0 : base1) + kk * row_bytes.
-// All fields are wave-uniform and live in scalar registers.
-struct TileSrc {
-  int n, kb;
-  uint64_t base0, base1;
-};
-
-// Physical pages of one tile, looked up (scalar loads) one tile before they
-// are used, so that the lookup latency overlaps the wait for the tile before.
-struct TilePages {
-  int tt0, pg0, pg1;
-};
-
-__device__ __forceinline__ TilePages tile_pages(const DecodeArgs& a, const_i32_ptr bt, int tt0, int t1) {
-  const int n = min(kTile, t1 - tt0);
-  return TilePages{tt0, bt[tt0 >> a.P_log2], bt[(tt0 + n - 1) >> a.P_log2]};
-}
-
-__device__ __forceinline__ TileSrc tile_src(const DecodeArgs& a, const TilePages& tp, int t1) {
-  TileSrc r;
-  r.n = min(kTile, t1 - tp.tt0);
-  const int s0 = tp.tt0 & (a.P - 1);
-  r.kb = a.P - s0;
-  const uint64_t pool = (uint64_t)(uintptr_t)a.pool;
-  r.base0 = pool + (uint64_t)((int64_t)uniform(tp.pg0) * a.P + s0) * (uint64_t)a.row_bytes;
-  r.base1 = pool + (uint64_t)((int64_t)uniform(tp.pg1) * a.P - r.kb) * (uint64_t)a.row_bytes;
-  asm volatile("" : "+s"(r.n), "+s"(r.kb), "+s"(r.base0), "+s"(r.base1));
-  return r;
-}
-
-// Address of the row holding tile token k (wave-uniform k).
-__device__ __forceinline__ const uint8_t* tile_row_ptr(const TileSrc& ts, int k, int64_t row_bytes) {
-  const int kk = min(k, ts.n - 1);
-  return (const uint8_t*)(uintptr_t)((kk < ts.kb ? ts.base0 : ts.base1) + (uint64_t)(kk * (int)row_bytes));
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
-}
-
-// s_waitcnt lgkmcnt(0): this wave's LDS reads have completed.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
-
-// Workgroup barrier for LDS hand-off only.  The caller has already waited
-// for its own LDS operations and tile transfers; unlike __syncthreads() this
-// does not drain the tile transfers still in flight for later tiles.  The
-// signal fences keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// One 16-byte direct-to-LDS load per lane from sbase + voff: the wave's 64
-// chunks land at lds + 16 * lane.  Issued as inline assembly so that the
-// compiler does not treat the pending LDS write as aliasing every LDS read
-// (which would make it drain all transfers before reading the current
-// tile); completion is tracked explicitly with wait_vmcnt_lgkm0.  m0 holds
-// the LDS destination during the instruction and is restored afterwards.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const lds_char* lds) {
-  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(lds_addr)
-      : "memory");
-}
-
-// Eight direct-to-LDS loads of one wave: lane l loads 16 B from
-// sbase + voff[j] into lds + 1024 * j + 16 * l, for j = 0..7.
-__device__ __forceinline__ void dma16x8(const void* sbase, const uint32_t (&voff)[8], const lds_char* lds) {
-  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)lds);
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %10\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %4, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %5, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %6, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %7, %9\n\t"
-      "s_add_u32 m0, m0, 0x400\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %8, %9\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
-        "v"(voff[7]), "s"(sbase), "s"(lds_addr)
-      : "memory", "scc");
-}
 
 // bf16 tiles go straight from HBM to LDS.  A wave instruction fills 64
 // consecutive 16-B LDS chunks: one token's latent row (lane = swizzled
@@ -744,6 +593,7 @@ int waves_for(int R) { return max(2, (R + 15) / 16); }
 // fp32 (hi + lo) queries need twice the query registers, which limits them
 // to four waves.
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32) {
+  if (decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) return true;
   if (dr != kDr) return false;
   if (!((fmt == kBF16 && dc == 512) || (fmt == kFP8 && dc == 448))) return false;
   const int nw = waves_for(R);
@@ -751,6 +601,7 @@ bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s) {
+  if (decode_fp8_rows_supported(fmt, a.dc, a.dr, a.R, a.q_f32)) return launch_decode_fp8_rows(a, s);
   const int nw = waves_for(a.R);
   if (nw > (a.q_f32 ? 4 : 8)) return hipErrorInvalidValue;
   if (fmt == kBF16) return a.q_f32 ? launch_nw<kBF16, true>(a, nw, s) : launch_nw<kBF16, false>(a, nw, s);

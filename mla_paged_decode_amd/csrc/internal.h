@@ -19,6 +19,9 @@ constexpr int kBalancedWorkers = 512;
 // balanced worker count it runs with (at most kBalancedWorkers).
 constexpr int kRingBf16 = 2;
 constexpr int kMfmaWorkersBf16 = 512;
+// Balanced worker count of the fp8 kernel for many query rows (one
+// workgroup per CU).
+constexpr int kFp8RowsWorkers = 256;
 // Batches up to this size are planned inside the matrix-core decode kernel
 // (each workgroup scans seq_lens itself); larger ones use the plan kernel.
 constexpr int kMaxInKernelPlan = 512;
@@ -62,6 +65,10 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s);
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
+// fp8 cache with bf16 queries: two 16-row blocks per wave (decode_fp8.hip);
+// launch_decode_mfma dispatches to it when it applies.
+bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32);
+hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 
 struct ProjArgs {
