@@ -11,12 +11,12 @@
 //   2. all waves decode the raw tile into a bf16 tile, value * 2^(E-127),
 //      which is exact (3 mantissa bits fit bf16's 7, the exponents fit);
 //   3. QK^T and PV run on v_mfma_f32_16x16x32_bf16 exactly as in the bf16
-//      kernel (same operand layouts and swizzled bf16 tile), except that each
-//      wave owns two 16-row blocks: every tile operand read from LDS feeds two
-//      MFMAs, which halves LDS reads per MFMA.
-// A wave holds 2 x 16 rows of bf16 queries (128 VGPRs) and 2 x 16 x 448
-// fp32 accumulators (224 AGPRs), so one wave runs per SIMD: one workgroup
-// of ceil(R / 32) waves per CU, 256 balanced workers.
+//      kernel (same operand layouts and swizzled bf16 tile), each wave owning
+//      one 16-row block of query rows.
+// A wave holds 16 rows of bf16 queries (64 VGPRs) and 16 x 448 fp32
+// accumulators (112 AGPRs).  One workgroup of ceil(R / 16) waves (at least
+// 2) runs per CU: 256 balanced workers.  Every wave reads the whole bf16
+// tile from LDS, so the per-tile cost is bound by LDS instructions.
 //
 // Online softmax, the rescale-free main loop and the partial layout follow
 // the bf16 kernel: per row a reference maximum kept while scores stay
