@@ -117,7 +117,7 @@ WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
   WorkspaceLayout w{};
   w.slots = num_splits > 0 ? (int64_t)B * num_splits : (int64_t)kBalancedWorkers + B;
   w.tile_start_off = 0;
-  size_t off = round_up(sizeof(int32_t) * ((size_t)B + 1), 256);
+  size_t off = round_up(sizeof(int32_t) * ((size_t)B + 2), 256);
   w.part_lse_off = off;
   off = round_up(off + sizeof(float) * (size_t)w.slots * R, 256);
   w.part_o_off = off;

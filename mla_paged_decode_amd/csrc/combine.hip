@@ -15,29 +15,12 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 
-// tile_start[b] = sum over b' < b of ceil(max(L_b', 0) / kPlanTile).
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B,
+// The balanced plan (schedule.h) for batches too large for the decode
+// kernel to plan itself.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int G,
                                                             int32_t* __restrict__ tile_start) {
-  __shared__ int32_t s[kPlanThreads];
-  const int tid = threadIdx.x;
-  const int per = (B + kPlanThreads - 1) / kPlanThreads;
-  const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-  int32_t sum = 0;
-  for (int b = b0; b < b1; ++b) sum += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
-  s[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int32_t v = tid >= off ? s[tid - off] : 0;
-    __syncthreads();
-    s[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = s[tid] - sum;
-  for (int b = b0; b < b1; ++b) {
-    tile_start[b] = run;
-    run += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
-  }
-  if (tid == kPlanThreads - 1) tile_start[B] = s[tid];
+  __shared__ int64_t s[kPlanThreads];
+  block_plan(lens, B, G, tile_start, s);
 }
 
 constexpr int kCombineThreads = 128;  // x 4 values = one 512-wide latent row per pass
@@ -71,13 +54,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
   const int tid = threadIdx.x;
 
   // Candidate parts: uniform mode, splits 0..S-1 (slot b*S + s); balanced
-  // mode, workers g0..g1 (slot g + b), skipping workers with no tiles.
+  // mode, the workers g0..g1 that own real tiles of the sequence (slot
+  // g + b), skipping workers with no positions at all.
   int64_t g0 = 0, n = 0;
   int64_t N = 0, G = a.workers;
   if (a.num_splits > 0) {
     n = a.num_splits;
   } else {
-    const int64_t ts = a.tile_start[b], te = a.tile_start[b + 1];
+    const int64_t te = a.tile_start[b + 1];
+    const int64_t ts = a.tile_start[b] + plan_lead(a.tile_start[b], te, a.tile_start[a.B + 1]);  // first real tile
     N = a.tile_start[a.B];
     if (ts < te) {
       g0 = worker_of_tile(ts, N, G);
@@ -209,7 +194,8 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   if (a.num_splits > 0) {
     n = a.num_splits;
   } else {
-    const int64_t ts = a.tile_start[b], te = a.tile_start[b + 1];
+    const int64_t te = a.tile_start[b + 1];
+    const int64_t ts = a.tile_start[b] + plan_lead(a.tile_start[b], te, a.tile_start[a.B + 1]);  // first real tile
     N = a.tile_start[a.B];
     if (ts < te) {
       g0 = worker_of_tile(ts, N, G);
@@ -364,7 +350,7 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
 }  // namespace
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
-  plan_kernel<<<1, kPlanThreads, 0, s>>>(a.seq_lens, a.B, a.tile_start);
+  plan_kernel<<<1, kPlanThreads, 0, s>>>(a.seq_lens, a.B, a.workers, a.tile_start);
   return hipGetLastError();
 }
 

@@ -41,9 +41,7 @@ __device__ __forceinline__ int lds_off(int tok, int chunk, int row_bytes) {
   return tok * row_bytes + 16 * (chunk ^ swz(tok));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return bf16x2_bits(lo, hi); }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -138,6 +136,23 @@ __device__ __forceinline__ void dma16_vaddr(const void* src, const lds_char* lds
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+// One 4-byte direct-to-LDS load per lane from a full 64-bit address: the
+// wave's 64 dwords land at lds + 4 * lane.  Used to pull lines into L2
+// ahead of their use (the LDS words written are never read).
+__device__ __forceinline__ void dma4_vaddr(const void* src, const lds_char* lds) {
+  const uint32_t lds_addr = uniform((uint32_t)(uintptr_t)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(lds_addr)

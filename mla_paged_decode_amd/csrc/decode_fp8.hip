@@ -122,8 +122,7 @@ template <int NW, int kRBW>
 __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char tile_mem[kTileBytes];
   __shared__ __attribute__((aligned(16))) char raw_mem[kRaw * kRawBuf];
-  __shared__ int32_t s_ts[kMaxInKernelPlan + 1];
-  __shared__ int32_t s_scan[64 * NW];
+  __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
   lds_char* const tile = (lds_char*)tile_mem;
   lds_char* const raws = (lds_char*)raw_mem;
@@ -136,9 +135,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
-    block_plan(a.seq_lens, a.B, s_ts, s_scan, s_lens);
+    // The tile buffer is free until the first transfer: it holds the scan.
+    block_plan(a.seq_lens, a.B, a.workers, s_ts, reinterpret_cast<int64_t*>(tile_mem), s_lens);
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
-      for (int i = threadIdx.x; i <= a.B; i += 64 * NW) a.tile_start[i] = s_ts[i];
+      for (int i = threadIdx.x; i <= a.B + 1; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
   }
   constexpr int D = kRaw - 1;  // raw tiles in flight ahead of the one being decoded
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   Unit unit;
   while (unit_it.next(a, unit)) {
     const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
-    const int64_t slot = a.num_splits > 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x + b;
+    const int64_t slot = unit.slot;
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
     const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
 

@@ -243,9 +243,9 @@ template <int FMT, bool HILO, int NW, int NBUF>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   using G = Geo<FMT>;
   __shared__ __attribute__((aligned(16))) char tiles_mem[NBUF * G::kTileBytes];
-  __shared__ int32_t s_ts[kMaxInKernelPlan + 1];
-  __shared__ int32_t s_scan[64 * NW];
+  __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
+  __shared__ int32_t s_sink[64];  // destination of L2 prefetch loads, never read
   lds_char* const tiles = (lds_char*)tiles_mem;
 
   const int lane = threadIdx.x & 63;
@@ -255,11 +255,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   const int row = wave * 16 + li;   // this lane's query row (B / P side)
   const bool row_ok = row < a.R;
 
+  // Pull the block table into L2 while the plan is computed, so that the
+  // page lookups after it hit in L2: one 4-byte load per 128-byte line,
+  // spread over all workgroups.
+  {
+    const int64_t lines = ((int64_t)a.B * a.max_blocks * 4 + 127) / 128;
+    const int64_t first = ((int64_t)blockIdx.x * NW + uniform(wave)) * 64;
+    if (first < lines)
+      dma4_vaddr((const char*)a.block_table + 128 * min(first + lane, lines - 1), (lds_char*)s_sink);
+  }
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
-    block_plan(a.seq_lens, a.B, s_ts, s_scan, s_lens);
+    // The tile buffer is free until the first transfer: it holds the scan.
+    block_plan(a.seq_lens, a.B, a.workers, s_ts, reinterpret_cast<int64_t*>(tiles_mem), s_lens);
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
-      for (int i = threadIdx.x; i <= a.B; i += 64 * NW) a.tile_start[i] = s_ts[i];
+      for (int i = threadIdx.x; i <= a.B + 1; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
   }
   using St = Staging<FMT, NW, NBUF>;
@@ -267,25 +277,68 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   St st;
   st.init();
   UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens);
-  Unit unit;
-  while (unit_it.next(a, unit)) {
+  // Units are walked one ahead: with early issue, the first tile of the next
+  // unit is transferred while the last tile of the current one is computed,
+  // so a worker's tile stream does not stall where it crosses into another
+  // sequence.  `ring` is the buffer of the unit's tile 0; `pre` says whether
+  // that tile is already in flight when the unit starts.
+  Unit unit, nxt;
+  // (uniform(): the loop is the same for every lane, and its carried values
+  // must stay in scalar registers.)
+  bool have = uniform(unit_it.next(a, unit));
+  bool have_next = have && uniform(unit_it.next(a, nxt));
+  int ring = 0;
+  bool pre = false, first_unit = true;
+  while (have) {
     // The unit is the same for the whole workgroup: keep it in scalar
     // registers so page lookups below are scalar loads.
     const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
-    const int64_t slot = a.num_splits > 0 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x + b;
+    const int64_t slot = unit.slot;
 
-    // The first tile transfers start before the queries are loaded, so that
-    // the two latencies overlap.
+    // Unless the unit's first tile is already in flight, its queries are
+    // loaded first and its first tiles are issued after them: the tile
+    // transfers complete in order after everything issued before them, so
+    // queries requested after the tiles would only arrive with the last of
+    // them, while queries requested first arrive in about one memory latency
+    // (the page lookups overlap it).  With early issue every ring buffer is
+    // free here, so kPro = NBUF tiles start at once (one more than in the
+    // loop).
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
     const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+    constexpr int kPro = St::kEarlyIssue ? NBUF : D;
+    auto ring_buf = [&](int i) { return tiles + ((ring + i) % NBUF) * G::kTileBytes; };
     TilePages pages_next;  // pages of the next tile to issue, looked up one tile early
+    TilePages pages_pro[kPro];
+    int issued = 0;        // tiles of this unit issued so far
     if (ntiles > 0) {
-      wait_vmcnt_lgkm0<0>();
-      lds_barrier();  // the previous unit's readers of the ring are done
+      if (pre) {
+        issued = 1;  // tile 0 is in flight; tile 1 follows once the ring slot is free
+      } else {
+        if (!first_unit) {
+          wait_vmcnt_lgkm0<0>();
+          lds_barrier();  // the previous unit's readers of the ring are done
+        }
 #pragma unroll
-      for (int x = 0; x < D; ++x)
-        if (x < ntiles) st.issue(a, tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), tiles + x * G::kTileBytes);
-      if (D < ntiles) pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
+        for (int x = 0; x < kPro; ++x)
+          if (x < ntiles) pages_pro[x] = tile_pages(a, bt, t0 + x * kTile, t1);
+        issued = min(kPro, ntiles);
+      }
+      if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+    }
+    // First tile of the next unit (pages looked up now, issued after this
+    // unit's last tile).
+    bool ahead = false, ahead_done = false;
+    int n_t1 = 0;
+    TilePages pages_ahead;
+    if constexpr (St::kEarlyIssue) {
+      if (have_next && ntiles > 0) {
+        const int n_b = uniform(nxt.b), n_t0 = uniform(nxt.t0);
+        n_t1 = uniform(nxt.t1);
+        if (n_t1 > n_t0) {
+          ahead = true;
+          pages_ahead = tile_pages(a, (const_i32_ptr)(a.block_table) + (int64_t)n_b * a.max_blocks, n_t0, n_t1);
+        }
+      }
     }
 
     // ---- queries in the B-operand layout: column = row, k = 8g..8g+7 ----
@@ -310,16 +363,15 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
             x[2 * i + 1] = bf16_bits_to_f32(uw[i] >> 16);
           }
         }
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float v = row_ok ? x[i] : 0.f;
-          const uint32_t hb = f32_to_bf16_bits(v);
-          qh[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)hb);
-          if constexpr (HILO) {
-            const float r = v - bf16_bits_to_f32(hb);
-            ql[ks][i] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(r));
-          }
+        for (int i = 0; i < 4; ++i) {
+          const float v0 = row_ok ? x[2 * i] : 0.f, v1 = row_ok ? x[2 * i + 1] : 0.f;
+          if constexpr (HILO) split_bf16x2(v0, v1, hw[i], lw[i]);
+          else hw[i] = bf16x2_bits(v0, v1);
         }
+        qh[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+        if constexpr (HILO) ql[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
       }
     }
     // The queries are only ever read as the MFMA B operand, which may come
@@ -329,6 +381,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       asm volatile("" : "+a"(qh[ks]));
       if constexpr (HILO) asm volatile("" : "+a"(ql[ks]));
     }
+    if (ntiles > 0 && !pre) {
+#pragma unroll
+      for (int x = 0; x < kPro; ++x)
+        if (x < ntiles) st.issue(a, tile_src(a, pages_pro[x], t1), ring_buf(x));
+    }
     const int j_q = row_ok ? row / a.H : 0;
     const int last_visible = L - a.Sq + j_q;
 
@@ -337,34 +394,39 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     for (int d = 0; d < G::kDb; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
 
-    if (ntiles > 0) st.finish(tiles);  // fp8: first tile from registers to LDS
+    if (ntiles > 0) st.finish(ring_buf(0));  // fp8: first tile from registers to LDS
 
     // One pipeline step before computing tile `it`.  Early issue: once every
-    // wave is done with tile it-1, start tile it+D into its buffer, then wait
-    // for tile it.  Otherwise (fp8, staged through registers one tile ahead):
-    // wait for tile it, then start loading tile it+1 into registers.
+    // wave is done with tile it-1, start tile it+D into its buffer (unless
+    // the prologue did), then wait for tile it.  Otherwise (fp8, staged
+    // through registers one tile ahead): wait for tile it, then start
+    // loading tile it+1 into registers.
     auto sync_issue = [&](int it) __attribute__((always_inline)) {
       const int x = it + D;
       if constexpr (St::kEarlyIssue) {
         wait_lgkm0();
         lds_barrier();  // everyone finished tile it-1: its buffer is free
-        if (x < ntiles) {
-          st.issue(a, tile_src(a, pages_next, t1), tiles + (x % NBUF) * G::kTileBytes);
-          if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+        if (issued <= x && issued < ntiles) {
+          st.issue(a, tile_src(a, pages_next, t1), ring_buf(issued));
+          ++issued;
+          if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+        } else if (ahead && !ahead_done && issued <= x) {
+          st.issue(a, tile_src(a, pages_ahead, n_t1), ring_buf(ntiles));
+          ahead_done = true;
         }
-        st.wait(min(D, ntiles - 1 - it));  // this wave's part of tile `it` landed
-        lds_barrier();                     // everyone's did
+        st.wait(issued - 1 - it + (ahead_done ? 1 : 0));  // this wave's part of tile `it` landed
+        lds_barrier();                                    // everyone's did
       } else {
         st.wait(min(D - 1, ntiles - 1 - it));
         lds_barrier();  // everyone's part of tile `it` landed; everyone finished tile it-1
         if (x < ntiles) {
-          st.issue(a, tile_src(a, pages_next, t1), tiles + (x % NBUF) * G::kTileBytes);
+          st.issue(a, tile_src(a, pages_next, t1), ring_buf(x));
           if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
         }
       }
     };
     auto finish_next = [&](int it) __attribute__((always_inline)) {
-      if (D == 1 && it + 1 < ntiles) st.finish(tiles + ((it + 1) % NBUF) * G::kTileBytes);
+      if (D == 1 && it + 1 < ntiles) st.finish(ring_buf(it + 1));
     };
 
     // Online softmax with a reference maximum m per row (base-2 domain).
@@ -382,7 +444,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     // and kRescale is false.
     auto tile = [&](int it, auto rescale_tag) __attribute__((always_inline)) -> bool {
       constexpr bool kRescale = decltype(rescale_tag)::value;
-      const lds_char* buf = tiles + (it % NBUF) * G::kTileBytes;
+      const lds_char* buf = ring_buf(it);
       const int tt0 = t0 + it * kTile;
 
       // ---- S^T = Tile . Q^T for two 16-token blocks ----
@@ -485,10 +547,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           const float e0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i] - m);
           const float e1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i + 1] - m);
           psum += e0 + e1;
-          const uint32_t h0 = f32_to_bf16_bits(e0), h1 = f32_to_bf16_bits(e1);
-          pk[2 * tb + i / 2] = h0 | (h1 << 16);
-          if constexpr (HILO)
-            pl[2 * tb + i / 2] = pack_bf16(e0 - bf16_bits_to_f32(h0), e1 - bf16_bits_to_f32(h1));
+          if constexpr (HILO) split_bf16x2(e0, e1, pk[2 * tb + i / 2], pl[2 * tb + i / 2]);
+          else pk[2 * tb + i / 2] = bf16x2_bits(e0, e1);
         }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
@@ -566,7 +626,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         *reinterpret_cast<float4*>(dst + 256 * d) =
             make_float4(acc[d][0] * inv_r[0], acc[d][1] * inv_r[1], acc[d][2] * inv_r[2], acc[d][3] * inv_r[3]);
     }
+    ring = uniform((ring + ntiles) % NBUF);
+    pre = uniform(ahead_done);
+    first_unit = false;
+    unit = nxt;
+    have = have_next;
+    have_next = have && uniform(unit_it.next(a, nxt));
   }
+  wait_vmcnt_lgkm0<0>();  // no transfer into LDS outlives the workgroup
 }
 
 template <int FMT, bool HILO>

@@ -19,6 +19,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two floats -> packed bfloat16 pair (lo in bits 0-15, hi in 16-31), round
+// to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f2;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 b2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+
+// Splits the pair (x0, x1) into bf16 parts h + l with x = h + l + O(2^-16 x):
+// h = bf16(x), l = bf16(x - h); returns the packed pairs.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t& h, uint32_t& l) {
+  h = bf16x2_bits(x0, x1);
+  l = bf16x2_bits(x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u));
+}
+
 // OCP e4m3fn byte -> float: 1 sign, 4 exponent bits (bias 7), 3 mantissa
 // bits, exponent 0 subnormal, S.1111.111 NaN, no infinities.
 __device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {

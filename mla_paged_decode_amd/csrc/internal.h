@@ -12,6 +12,10 @@ namespace mla {
 // Tokens per planning tile: balanced split-KV cuts every sequence into tiles
 // of this many tokens and hands each worker a contiguous run of tiles.
 constexpr int kPlanTile = 32;
+// Virtual tiles charged to a worker for each sequence it starts (balanced
+// mode): about what loading that sequence's queries and restarting the tile
+// stream cost, measured in tile times on MI355X.
+constexpr int kUnitCostTiles = 4;
 // Worker count of balanced mode: two workgroups per compute unit on a
 // 256-CU MI355X, which fills the chip in one pass.
 constexpr int kBalancedWorkers = 512;
@@ -47,7 +51,7 @@ struct DecodeArgs {
   int part_tiled;         // 1: matrix-core layout [slots][ceil(R/16)][dc/16][64 lanes][4]:
                           //    row 16w + 4(l/16) + i, column 16d + l%16 at [slot][w][d][l][i]
   float* part_lse;        // [slots][R], natural log
-  int32_t* tile_start;    // balanced: [B + 1] exclusive prefix of tiles
+  int32_t* tile_start;    // balanced: [B + 2] plan (schedule.h)
   int plan_in_kernel;     // balanced: the decode kernel computes tile_start
   float* o;               // [B][R][dc]
   float* lse;             // [B][R] or null
@@ -65,7 +69,7 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s);
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
-// fp8 cache with bf16 queries: two 16-row blocks per wave (decode_fp8.hip);
+// fp8 cache with bf16 queries: one 16-row block per wave (decode_fp8.hip);
 // launch_decode_mfma dispatches to it when it applies.
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32);
 hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s);

@@ -42,8 +42,6 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
-
 template <bool kOutF32, int NKS>  // NKS = d_nope / 32
 __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   constexpr int kRows = 32 * NKS;               // d_nope
@@ -148,16 +146,11 @@ __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) 
     for (int j = 0; j < kStep && k0 + j < NKS; ++j) {
       const float x[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
                           raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
-      uint32_t hb[8], lb[8];
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hb[i] = f32_to_bf16_bits(x[i]);
-        lb[i] = f32_to_bf16_bits(x[i] - bf16_bits_to_f32(hb[i]));
-      }
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(pack2(hb[0], hb[1]), pack2(hb[2], hb[3]),
-                                                              pack2(hb[4], hb[5]), pack2(hb[6], hb[7])));
-      const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(pack2(lb[0], lb[1]), pack2(lb[2], lb[3]),
-                                                              pack2(lb[4], lb[5]), pack2(lb[6], lb[7])));
+      for (int i = 0; i < 4; ++i) split_bf16x2(x[2 * i], x[2 * i + 1], hw[i], lw[i]);
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[k0 + j], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[k0 + j], acc, 0, 0, 0);
     }

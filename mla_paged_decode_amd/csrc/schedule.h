@@ -10,15 +10,26 @@
 // In both modes a unit starts at a multiple of kPlanTile tokens.
 //
 // Balanced mode (num_splits = 0): every sequence is cut into tiles of
-// kPlanTile tokens; tile_start[b] is the exclusive prefix sum of tile counts
-// and N = tile_start[B].  Worker g of G owns the concatenated tiles
-// [g*N/G, (g+1)*N/G), which may span several sequences; its partial for
-// sequence b goes to slot g + b (unique, < G + B).
+// kPlanTile tokens, preceded by c virtual tiles (none for an empty sequence)
+// that stand for what starting another sequence costs a worker (its queries
+// are loaded and its tile stream restarts).  tile_start[b] is the exclusive
+// prefix sum of these counts, N = tile_start[B] and c = tile_start[B + 1].
+// Worker g of G owns the concatenated positions [g*N/G, (g+1)*N/G), which
+// may span several sequences; the real tiles among them are its units, and
+// its partial for sequence b goes to slot g + b (unique, < G + B).  A worker
+// whose positions in b are all virtual has no unit there.  c is
+// kUnitCostTiles, or 0 when, without it, every sequence would start exactly
+// where a worker starts (no worker would cross into another sequence, and the
+// virtual tiles would only unbalance the split).  Worker g runs on the
+// workgroup given by balanced_worker().
 #pragma once
 
 #include "internal.h"
 
 namespace mla {
+
+// Virtual positions at the start of a sequence that spans [ts, te).
+__device__ __forceinline__ int64_t plan_lead(int64_t ts, int64_t te, int32_t c) { return te > ts ? c : 0; }
 
 __device__ __forceinline__ int64_t worker_tile_begin(int64_t g, int64_t N, int64_t G) {
   return g * N / G;
@@ -39,37 +50,67 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* ts, int B, int64_t t) 
   return lo;
 }
 
-// Balanced-mode plan computed by one workgroup: ts[b] = sum over b' < b of
-// ceil(max(L_b', 0) / kPlanTile), ts[B] = total, written to `ts` (LDS or
-// global).  `scan` is LDS scratch of blockDim.x ints.  If lens_out is not
+// Balanced-mode plan computed by one workgroup for G workers: tile_start
+// as described above (B + 2 values), written to `ts` (LDS or global).
+// `scan` is LDS scratch of blockDim.x 64-bit values.  If lens_out is not
 // null, max(lens[b], 0) is also stored there.  Contains barriers: every
 // thread of the workgroup must call it.
-__device__ __forceinline__ void block_plan(const int32_t* lens, int B, int32_t* ts, int32_t* scan,
+__device__ __forceinline__ void block_plan(const int32_t* lens, int B, int G, int32_t* ts, int64_t* scan,
                                            int32_t* lens_out = nullptr) {
   const int nt = blockDim.x, tid = threadIdx.x;
   const int per = (B + nt - 1) / nt;
   const int b0 = min(B, tid * per), b1 = min(B, b0 + per);
-  int32_t sum = 0;
+  // Counts packed as tiles + (non-empty sequences << 32).
+  auto count = [](int32_t L) -> int64_t { return L > 0 ? ((L + kPlanTile - 1) / kPlanTile) + (1ll << 32) : 0; };
+  int64_t sum = 0;
   for (int b = b0; b < b1; ++b) {
     const int32_t L = max(lens[b], 0);
     if (lens_out) lens_out[b] = L;
-    sum += (L + kPlanTile - 1) / kPlanTile;
+    sum += count(L);
   }
   scan[tid] = sum;
   __syncthreads();
   for (int off = 1; off < nt; off <<= 1) {
-    const int32_t v = tid >= off ? scan[tid - off] : 0;
+    const int64_t v = tid >= off ? scan[tid - off] : 0;
     __syncthreads();
     scan[tid] += v;
     __syncthreads();
   }
-  int32_t run = scan[tid] - sum;
+  const int64_t total = scan[nt - 1];
+  const int64_t N0 = total & 0xffffffffll;  // real tiles
+  // Does any sequence start strictly inside a worker's range of the plan
+  // without virtual tiles?
+  bool crossing = false;
+  int64_t run = scan[tid] - sum;
   for (int b = b0; b < b1; ++b) {
-    ts[b] = run;
-    run += (max(lens[b], 0) + kPlanTile - 1) / kPlanTile;
+    const int64_t p = run & 0xffffffffll;
+    if (lens[b] > 0 && p > 0) {
+      const int64_t g = (p * G + N0 - 1) / N0;  // first worker starting at or after p
+      crossing |= g * N0 / G != p;
+    }
+    run += count(max(lens[b], 0));
   }
-  if (tid == nt - 1) ts[B] = scan[tid];
+  const int32_t c = __syncthreads_or(crossing) ? kUnitCostTiles : 0;
+  run = scan[tid] - sum;
+  for (int b = b0; b < b1; ++b) {
+    ts[b] = (int32_t)((run & 0xffffffffll) + c * (run >> 32));
+    run += count(max(lens[b], 0));
+  }
+  if (tid == nt - 1) {
+    ts[B] = (int32_t)(N0 + c * (total >> 32));
+    ts[B + 1] = c;
+  }
   __syncthreads();
+}
+
+// Balanced-mode worker index of this workgroup.  Workgroups are dispatched
+// round-robin over the 8 XCDs, each with its own L2, so workers are numbered
+// XCD-major: the workgroups of one XCD own one contiguous run of tiles, and
+// a sequence split over several of them has its queries read into one L2.
+__device__ __forceinline__ int balanced_worker(int G) {
+  constexpr int kXcds = 8;
+  const int x = blockIdx.x;
+  return G % kXcds == 0 ? (x % kXcds) * (G / kXcds) + x / kXcds : x;
 }
 
 // One work unit: tokens [t0, t1) of sequence b (length L), partial -> slot.
@@ -82,18 +123,24 @@ struct Unit {
 //   UnitIter it(a); Unit u; while (it.next(a, u)) { ... }
 // All lanes of the workgroup see the same sequence of units.
 struct UnitIter {
-  const int32_t* ts;    // tile_start[0..B] (global memory or LDS)
+  const int32_t* ts;    // tile_start[0..B+1] (global memory or LDS)
   const int32_t* lens;  // sequence lengths (global memory, or clamped copies in LDS)
   int b;                // next sequence to consider (balanced) / done flag (uniform)
+  int g;                // worker index (balanced)
+  int32_t c;            // virtual tiles at the start of each sequence (balanced)
   int64_t tb, te;       // this worker's tile range (balanced)
 
   __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start, const int32_t* seq_lens)
       : ts(tile_start), lens(seq_lens) {
     if (a.num_splits > 0) {
       b = 0;
+      g = 0;
+      c = 0;
       tb = te = 0;
     } else {
-      const int64_t G = a.workers, N = ts[a.B], g = blockIdx.x;
+      g = balanced_worker(a.workers);
+      c = ts[a.B + 1];
+      const int64_t G = a.workers, N = ts[a.B];
       tb = worker_tile_begin(g, N, G);
       te = worker_tile_begin(g + 1, N, G);
       b = tb < te ? seq_of_tile(ts, a.B, tb) : a.B;
@@ -115,14 +162,15 @@ struct UnitIter {
       return true;
     }
     for (; b < a.B && ts[b] < te; ++b) {
-      const int64_t s0 = max(tb, (int64_t)ts[b]);
+      const int64_t first = ts[b] + plan_lead(ts[b], ts[b + 1], c);  // first real tile
+      const int64_t s0 = max(tb, first);
       const int64_t s1 = min(te, (int64_t)ts[b + 1]);
       if (s0 >= s1) continue;
       u.b = b;
       u.L = max(lens[b], 0);
-      u.t0 = (int)((s0 - ts[b]) * kPlanTile);
-      u.t1 = (int)min((int64_t)u.L, (s1 - ts[b]) * kPlanTile);
-      u.slot = (int64_t)blockIdx.x + b;
+      u.t0 = (int)((s0 - first) * kPlanTile);
+      u.t1 = (int)min((int64_t)u.L, (s1 - first) * kPlanTile);
+      u.slot = (int64_t)g + b;
       ++b;
       return true;
     }
