@@ -72,7 +72,7 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
-COUNTER_SOURCES = ["decode_mfma.hip", "schedule.h", "internal.h", "device_common.h"]
+COUNTER_SOURCES = ["decode_mfma.hip", "decode_common.h", "schedule.h", "internal.h", "device_common.h"]
 
 
 def kernel_source_digest() -> str:

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char raw_mem[kRaw * kRawBuf];
   __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
+  __shared__ int32_t s_first;
   lds_char* const tile = (lds_char*)tile_mem;
   lds_char* const raws = (lds_char*)raw_mem;
 
@@ -135,14 +136,14 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
-    // The tile buffer is free until the first transfer: it holds the scan.
-    block_plan(a.seq_lens, a.B, a.workers, s_ts, reinterpret_cast<int64_t*>(tile_mem), s_lens);
+    if (threadIdx.x < 64) wave_plan(a.seq_lens, a.B, a.workers, s_ts, s_lens, &s_first);
+    __syncthreads();
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
       for (int i = threadIdx.x; i <= a.B + 1; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
   }
   constexpr int D = kRaw - 1;  // raw tiles in flight ahead of the one being decoded
-  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens);
+  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens, ts == s_ts ? s_first : -1);
   Unit unit;
   while (unit_it.next(a, unit)) {
     const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);

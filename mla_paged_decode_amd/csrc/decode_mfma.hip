@@ -245,6 +245,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char tiles_mem[NBUF * G::kTileBytes];
   __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
+  __shared__ int32_t s_first;
   __shared__ int32_t s_sink[64];  // destination of L2 prefetch loads, never read
   lds_char* const tiles = (lds_char*)tiles_mem;
 
@@ -266,8 +267,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   }
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
-    // The tile buffer is free until the first transfer: it holds the scan.
-    block_plan(a.seq_lens, a.B, a.workers, s_ts, reinterpret_cast<int64_t*>(tiles_mem), s_lens);
+    if (threadIdx.x < 64) wave_plan(a.seq_lens, a.B, a.workers, s_ts, s_lens, &s_first);
+    __syncthreads();
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
       for (int i = threadIdx.x; i <= a.B + 1; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = St::kDepth;
   St st;
   st.init();
-  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens);
+  UnitIter unit_it(a, ts, ts == s_ts ? s_lens : a.seq_lens, ts == s_ts ? s_first : -1);
   // Units are walked one ahead: with early issue, the first tile of the next
   // unit is transferred while the last tile of the current one is computed,
   // so a worker's tile stream does not stall where it crosses into another

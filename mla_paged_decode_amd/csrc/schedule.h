@@ -50,6 +50,15 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* ts, int B, int64_t t) 
   return lo;
 }
 
+// Whether some worker's range starts exactly at position p (0 < p < N0) of
+// a plan over N0 positions and G workers: worker starts are floor(g*N0/G),
+// so p is one iff the first multiple of N0 at or above p*G is below (p+1)*G.
+__device__ __forceinline__ bool starts_worker(int64_t p, int64_t N0, int64_t G) {
+  const uint64_t pg = (uint64_t)p * (uint64_t)G;
+  const uint64_t r = pg < (1ull << 32) && N0 < (1ll << 32) ? (uint32_t)pg % (uint32_t)N0 : pg % (uint64_t)N0;
+  return r == 0 || (uint64_t)N0 - r < (uint64_t)G;
+}
+
 // Balanced-mode plan computed by one workgroup for G workers: tile_start
 // as described above (B + 2 values), written to `ts` (LDS or global).
 // `scan` is LDS scratch of blockDim.x 64-bit values.  If lens_out is not
@@ -84,10 +93,7 @@ __device__ __forceinline__ void block_plan(const int32_t* lens, int B, int G, in
   int64_t run = scan[tid] - sum;
   for (int b = b0; b < b1; ++b) {
     const int64_t p = run & 0xffffffffll;
-    if (lens[b] > 0 && p > 0) {
-      const int64_t g = (p * G + N0 - 1) / N0;  // first worker starting at or after p
-      crossing |= g * N0 / G != p;
-    }
+    if (lens[b] > 0 && p > 0) crossing |= !starts_worker(p, N0, G);
     run += count(max(lens[b], 0));
   }
   const int32_t c = __syncthreads_or(crossing) ? kUnitCostTiles : 0;
@@ -101,6 +107,73 @@ __device__ __forceinline__ void block_plan(const int32_t* lens, int B, int G, in
     ts[B + 1] = c;
   }
   __syncthreads();
+}
+
+// Worker index of this workgroup in balanced mode (defined below).
+__device__ __forceinline__ int balanced_worker(int G);
+
+// The same plan computed by one wave, for B <= 64 * kPlanPerLane, without
+// barriers: lane l handles sequences [l * per, (l + 1) * per).  Also stores
+// in *first the sequence holding this workgroup's first position (the
+// largest b with ts[b] <= that position).  Every lane of the wave must call
+// it; the caller synchronises the workgroup afterwards.
+constexpr int kPlanPerLane = kMaxInKernelPlan / 64;
+__device__ __forceinline__ void wave_plan(const int32_t* lens, int B, int G, int32_t* ts, int32_t* lens_out,
+                                          int32_t* first) {
+  const int lane = threadIdx.x & 63;
+  const int per = (B + 63) / 64;
+  const int b0 = lane * per;
+  int32_t L[kPlanPerLane];
+  int32_t tiles = 0, ne = 0;
+#pragma unroll
+  for (int i = 0; i < kPlanPerLane; ++i) {
+    const int b = b0 + i;
+    L[i] = i < per && b < B ? max(lens[b], 0) : 0;
+    tiles += (L[i] + kPlanTile - 1) / kPlanTile;
+    ne += L[i] > 0;
+  }
+  int32_t st = tiles, sn = ne;  // inclusive prefix sums over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(st, off), v = __shfl_up(sn, off);
+    if (lane >= off) {
+      st += u;
+      sn += v;
+    }
+  }
+  const int32_t N0 = __shfl(st, 63), Bn = __shfl(sn, 63);
+  bool crossing = false;
+  int32_t p = st - tiles;
+#pragma unroll
+  for (int i = 0; i < kPlanPerLane; ++i) {
+    if (L[i] > 0 && p > 0) crossing |= !starts_worker(p, N0, G);
+    p += (L[i] + kPlanTile - 1) / kPlanTile;
+  }
+  const int32_t c = __any(crossing) ? kUnitCostTiles : 0;
+  const int64_t N = (int64_t)N0 + (int64_t)c * Bn;
+  const int64_t tb = worker_tile_begin(balanced_worker(G), N, G);
+  p = st - tiles;
+  int32_t q = sn - ne;
+  int32_t cand = -1;
+#pragma unroll
+  for (int i = 0; i < kPlanPerLane; ++i) {
+    const int b = b0 + i;
+    if (i < per && b < B) {
+      const int32_t t = p + c * q;
+      ts[b] = t;
+      if (lens_out) lens_out[b] = L[i];
+      if (t <= tb) cand = b;
+    }
+    p += (L[i] + kPlanTile - 1) / kPlanTile;
+    q += L[i] > 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cand = max(cand, __shfl_xor(cand, off));
+  if (lane == 63) {
+    ts[B] = (int32_t)N;
+    ts[B + 1] = c;
+  }
+  if (lane == 0) *first = N <= tb ? B : cand;
 }
 
 // Balanced-mode worker index of this workgroup.  Workgroups are dispatched
@@ -130,7 +203,10 @@ struct UnitIter {
   int32_t c;            // virtual tiles at the start of each sequence (balanced)
   int64_t tb, te;       // this worker's tile range (balanced)
 
-  __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start, const int32_t* seq_lens)
+  // first_b >= 0: the sequence holding this worker's first position, known
+  // from the plan (otherwise it is searched for).
+  __device__ __forceinline__ UnitIter(const DecodeArgs& a, const int32_t* tile_start, const int32_t* seq_lens,
+                                      int first_b = -1)
       : ts(tile_start), lens(seq_lens) {
     if (a.num_splits > 0) {
       b = 0;
@@ -143,7 +219,7 @@ struct UnitIter {
       const int64_t G = a.workers, N = ts[a.B];
       tb = worker_tile_begin(g, N, G);
       te = worker_tile_begin(g + 1, N, G);
-      b = tb < te ? seq_of_tile(ts, a.B, tb) : a.B;
+      b = tb < te ? (first_b >= 0 ? first_b : seq_of_tile(ts, a.B, tb)) : a.B;
     }
   }
 
