@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
 // first partial rows are requested with the first log-sum-exps.
 constexpr int kTiledThreads = 256;
 constexpr int kTiledWaves = kTiledThreads / 64;
-constexpr int kChunk = 256;
+constexpr int kChunk = 64;
 
 // 32-bit forms of the balanced-split worker ranges (tile counts < 2^22).
 __device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) {
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   // Parts of a chunk handled by this wave: share, share + kShare, ...,
   // loaded kBatch at a time.
   constexpr int kPer = kChunk / kShare;
-  constexpr int kBatch = kShare > 1 ? 16 : 8;
+  constexpr int kBatch = (kShare > 1 ? 16 : 8) < kPer ? (kShare > 1 ? 16 : 8) : kPer;  // divides kPer
   float4 p[kBatch];
   auto load_parts = [&](int64_t c0, int j0, int d) {
     const float* po = part_ptr(d);
@@ -346,6 +346,7 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
     }
   }
 }
+
 
 }  // namespace
 
