@@ -22,6 +22,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 // The block table is read-only during a call: reading it through the
 // constant address space lets the compiler use scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;

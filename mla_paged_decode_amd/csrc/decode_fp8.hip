@@ -10,18 +10,19 @@
 //      tiles ahead of the one being computed;
 //   2. all waves decode the raw tile into a bf16 tile, value * 2^(E-127),
 //      which is exact (3 mantissa bits fit bf16's 7, the exponents fit);
-//   3. QK^T and PV run on v_mfma_f32_16x16x32_bf16 exactly as in the bf16
-//      kernel (same operand layouts and swizzled bf16 tile), each wave owning
-//      one 16-row block of query rows.
-// A wave holds 16 rows of bf16 queries (64 VGPRs) and 16 x 448 fp32
-// accumulators (112 AGPRs).  One workgroup of ceil(R / 16) waves (at least
-// 2) runs per CU: 256 balanced workers.  Every wave reads the whole bf16
-// tile from LDS, so the per-tile cost is bound by LDS instructions.
+//   3. QK^T and PV run on v_mfma_f32_16x16x32_bf16 with the operand layouts
+//      and swizzled bf16 tile of the bf16 kernel.  QK^T and the softmax are
+//      split by 16-row blocks (one per wave); PV is split by column blocks,
+//      each wave covering all rows, with P handed over through LDS.
+// One workgroup of ceil(R / 16) waves (at least 2) runs per CU: 256 balanced
+// workers.  The per-tile cost is bound by LDS instructions (about 8 cycles
+// per wave instruction), which the column split keeps to one transposed
+// read per V chunk per tile.
 //
 // Online softmax, the rescale-free main loop and the partial layout follow
 // the bf16 kernel: per row a reference maximum kept while scores stay
-// within 2^64 of it; a tile that would exceed it sends the wave to a second
-// loop that rescales.  Partials use the tiled matrix-core layout.
+// within 2^64 of it; a tile that would exceed it sends the workgroup to a
+// second loop that rescales.  Partials use the tiled matrix-core layout.
 #include <cmath>
 #include <type_traits>
 
@@ -118,21 +119,37 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
   }
 }
 
-template <int NW, int kRBW>
+// Waves split the work two ways.  Wave w < RB owns query rows 16w..16w+15
+// for QK^T and the softmax (its queries stay in registers); every wave owns
+// the PV column blocks [w*kDb/NW, (w+1)*kDb/NW) for all RB row blocks.  P
+// goes from the row owners to all waves through LDS, so each transposed V
+// read feeds RB MFMAs and every V column block is read once per tile.
+template <int NW, int RB>
 __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
+  static_assert(RB >= 1 && RB <= NW, "row blocks are owned by distinct waves");
+  constexpr int kCols = (kDb + NW - 1) / NW;  // most column blocks a wave owns
   __shared__ __attribute__((aligned(16))) char tile_mem[kTileBytes];
   __shared__ __attribute__((aligned(16))) char raw_mem[kRaw * kRawBuf];
+  __shared__ __attribute__((aligned(16))) char p_mem[RB * 64 * 16];  // P per row block, A-operand layout
+  __shared__ __attribute__((aligned(16))) float s_row[RB][16];       // per row: rescale factor, then 1/sum
+  __shared__ __attribute__((aligned(16))) int32_t s_flag[8];         // per row block: 0, 1 rescaled, 2 overflow
   __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
   __shared__ int32_t s_first;
   lds_char* const tile = (lds_char*)tile_mem;
   lds_char* const raws = (lds_char*)raw_mem;
+  lds_char* const pbuf = (lds_char*)p_mem;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int li = lane & 15;
   const int row_blocks = (a.R + 15) / 16;
+  const bool owner = wave < RB;
+  const int row = wave * 16 + li;  // the owner's query row for this lane (B / P side)
+  const bool row_ok = owner && row < a.R;
+  const int c_begin = wave * kDb / NW;
+  const int c_count = (wave + 1) * kDb / NW - c_begin;
 
   const int32_t* ts = a.tile_start;
   if (a.num_splits == 0 && a.plan_in_kernel) {
@@ -151,38 +168,30 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
     const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
 
-    // ---- queries (bf16, B-operand layout) of this wave's two row blocks ----
+    // ---- queries (bf16, B-operand layout) of the owned row block ----
     // Loaded and waited for before any tile transfer, so that later waits
     // on the transfers are not mixed up with the query loads.
-    bf16x8 q[kRBW][kKs];
-#pragma unroll
-    for (int r = 0; r < kRBW; ++r) {
-      const int row = (kRBW * wave + r) * 16 + li;
-      const bool ok = row < a.R;
-      const uint16_t* src = static_cast<const uint16_t*>(a.q_abs) + ((int64_t)b * a.R + (ok ? row : 0)) * kVals + 8 * g;
+    bf16x8 q[kKs];
+    {
+      const uint16_t* src = static_cast<const uint16_t*>(a.q_abs) + ((int64_t)b * a.R + (row_ok ? row : 0)) * kVals + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < kKs; ++ks) {
-        q[r][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * ks));
-        if (!ok) q[r][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        q[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        if (row_ok) q[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(src + 32 * ks));
       }
     }
     wait_vmcnt_lgkm0<0>();
 
-    f32x4 acc[kRBW][kDb];
+    f32x4 acc[RB][kCols];
 #pragma unroll
-    for (int r = 0; r < kRBW; ++r)
+    for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int d = 0; d < kDb; ++d) acc[r][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[kRBW], lsum[kRBW];
-#pragma unroll
-    for (int r = 0; r < kRBW; ++r) {
-      m[r] = -INFINITY;
-      lsum[r] = 0.f;
-    }
+      for (int d = 0; d < kCols; ++d) acc[r][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;  // the owner's row statistics (base 2)
 
     TilePages pages_next;
     if (ntiles > 0) {
-      lds_barrier();  // the previous unit's readers of the tile and ring are done
+      lds_barrier();  // the previous unit's readers of the tile, ring and P are done
 #pragma unroll
       for (int x = 0; x < D; ++x)
         if (x < ntiles) RawStaging<NW>::load(tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), raws + (x % kRaw) * kRawBuf);
@@ -210,124 +219,139 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
       lds_barrier();  // the bf16 tile is complete
     };
 
+    // Per row a reference maximum m, set by the first tile with a visible
+    // token.  The main loop keeps it while scores stay below m + 64 (P
+    // cannot overflow, and P, the sum and the accumulators share m); a tile
+    // beyond that is redone by the second loop, which raises m when a score
+    // exceeds it by 8 and rescales the accumulators of that row block.
     constexpr float kHeadroom = 64.f;
     auto compute = [&](int it, auto rescale_tag) __attribute__((always_inline)) -> bool {
       constexpr bool kRescale = decltype(rescale_tag)::value;
-      const int tt0 = t0 + it * kTile;
-
-      // ---- S^T = Tile . Q^T: two token blocks x two row blocks ----
-      f32x4 s[2][kRBW];
+      const float m_save = m, lsum_save = lsum;
+      if (owner) {
+        const int tt0 = t0 + it * kTile;
+        // ---- S^T = Tile . Q^T for the two token blocks ----
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const lds_char* lat_base[2][2];
+        const lds_char* rope_base[2][2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb) {
+          const int tok = tb * 16 + li;
+          const int xs = swz(tok);
+          const int flip = 64 * (xs >> 2);
+          const lds_char* bl = tile + tok * kLatRow + 16 * (g ^ (xs & 3));
+          const lds_char* br = tile + kRopeBase + tok * kRopeRow + 16 * (g ^ (xs & 3));
+          lat_base[tb][0] = bl + flip;
+          lat_base[tb][1] = bl - flip;
+          rope_base[tb][0] = br + flip;
+          rope_base[tb][1] = br - flip;
+        }
+        auto tile_a = [&](int ks, int tb) {
+          const lds_char* p = ks < kKsLat ? lat_base[tb][ks & 1] + 64 * ks : rope_base[tb][ks & 1] + 64 * (ks - kKsLat);
+          return *(const lds_bf16x8*)p;
+        };
+        constexpr int kAhead = NW > 4 ? 2 : 3;  // two waves per SIMD: half the registers
+        bf16x8 ta[kAhead][2];
 #pragma unroll
-        for (int r = 0; r < kRBW; ++r) s[tb][r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const lds_char* lat_base[2][2];
-      const lds_char* rope_base[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int tok = tb * 16 + li;
-        const int xs = swz(tok);
-        const int flip = 64 * (xs >> 2);
-        const lds_char* bl = tile + tok * kLatRow + 16 * (g ^ (xs & 3));
-        const lds_char* br = tile + kRopeBase + tok * kRopeRow + 16 * (g ^ (xs & 3));
-        lat_base[tb][0] = bl + flip;
-        lat_base[tb][1] = bl - flip;
-        rope_base[tb][0] = br + flip;
-        rope_base[tb][1] = br - flip;
-      }
-      auto tile_a = [&](int ks, int tb) {
-        const lds_char* p = ks < kKsLat ? lat_base[tb][ks & 1] + 64 * ks : rope_base[tb][ks & 1] + 64 * (ks - kKsLat);
-        return *(const lds_bf16x8*)p;
-      };
-      constexpr int kAhead = 2;
-      bf16x8 ta[kAhead][2];
-#pragma unroll
-      for (int k = 0; k < kAhead; ++k) {
-        ta[k][0] = tile_a(k, 0);
-        ta[k][1] = tile_a(k, 1);
-      }
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) {
-        const bf16x8 a0 = ta[ks % kAhead][0], a1 = ta[ks % kAhead][1];
-        if (ks + kAhead < kKs) {
-          ta[ks % kAhead][0] = tile_a(ks + kAhead, 0);
-          ta[ks % kAhead][1] = tile_a(ks + kAhead, 1);
+        for (int k = 0; k < kAhead; ++k) {
+          ta[k][0] = tile_a(k, 0);
+          ta[k][1] = tile_a(k, 1);
         }
 #pragma unroll
-        for (int r = 0; r < kRBW; ++r) {
-          s[0][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, q[r][ks], s[0][r], 0, 0, 0);
-          s[1][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, q[r][ks], s[1][r], 0, 0, 0);
+        for (int ks = 0; ks < kKs; ++ks) {
+          const bf16x8 a0 = ta[ks % kAhead][0], a1 = ta[ks % kAhead][1];
+          if (ks + kAhead < kKs) {
+            ta[ks % kAhead][0] = tile_a(ks + kAhead, 0);
+            ta[ks % kAhead][1] = tile_a(ks + kAhead, 1);
+          }
+          s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, q[ks], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, q[ks], s[1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
 
-      // ---- online softmax per row block ----
-      float sv[kRBW][2][4], mx[kRBW];
-#pragma unroll
-      for (int r = 0; r < kRBW; ++r) {
-        const int row = (kRBW * wave + r) * 16 + li;
-        const bool row_ok = row < a.R;
+        // ---- online softmax of the owned rows ----
         const int last_visible = L - a.Sq + (row_ok ? row / a.H : 0);
-        mx[r] = -INFINITY;
+        float sv[2][4], mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = tt0 + tb * 16 + 4 * g + i;
             const bool ok = row_ok && t < t1 && t <= last_visible;
-            sv[r][tb][i] = ok ? s[tb][r][i] * a.scale_log2 : -INFINITY;
-            mx[r] = fmaxf(mx[r], sv[r][tb][i]);
+            sv[tb][i] = ok ? s[tb][i] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[tb][i]);
           }
-        mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 16));
-        mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 32));
-      }
-      if constexpr (kRescale) {
-#pragma unroll
-        for (int r = 0; r < kRBW; ++r) {
-          const bool raise = mx[r] > m[r] + 8.f;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        int flag = 0;
+        if constexpr (kRescale) {
+          const bool raise = mx > m + 8.f;  // also true when m = -inf < mx
           if (__any(raise)) {
-            const float m_new = raise ? mx[r] : m[r];
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[r] - m_new);
-            lsum[r] *= alpha;
-            m[r] = m_new;
-            float al[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-            for (int d = 0; d < kDb; ++d)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[r][d][i] *= al[i];
+            const float m_new = raise ? mx : m;
+            const float alpha = m == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= alpha;
+            m = m_new;
+            if (g == 0) s_row[wave][li] = alpha;
+            flag = 1;
           }
+        } else {
+          if (__any(m != -INFINITY && mx > m + kHeadroom)) flag = 2;
+          else m = m == -INFINITY ? mx : m;
         }
-      } else {
+        if (flag != 2) {
+          float psum = 0.f;
+          uint32_t pk[4];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+              const float e0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i] - m);
+              const float e1 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb][i + 1] - m);
+              psum += e0 + e1;
+              pk[2 * tb + i / 2] = pack_bf16(e0, e1);
+            }
+          psum += __shfl_xor(psum, 16);
+          psum += __shfl_xor(psum, 32);
+          lsum += psum;
+          *(lds_u32x4*)(pbuf + (wave * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        }
+        if (lane == 0) s_flag[wave] = flag;
+      }
+      wait_lgkm0();
+      lds_barrier();  // P, flags and rescale factors of every row block are in LDS
+
+      int flags[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) flags[r] = uniform(s_flag[r]);
+      if constexpr (!kRescale) {
         bool over = false;
 #pragma unroll
-        for (int r = 0; r < kRBW; ++r) over = over || (m[r] != -INFINITY && mx[r] > m[r] + kHeadroom);
-        if (__any(over)) return false;
+        for (int r = 0; r < RB; ++r) over = over || flags[r] == 2;
+        if (over) {  // every wave sees the same flags: redo this tile in the second loop
+          m = m_save;
+          lsum = lsum_save;
+          return false;
+        }
+      } else {
 #pragma unroll
-        for (int r = 0; r < kRBW; ++r) m[r] = m[r] == -INFINITY ? mx[r] : m[r];
-      }
-      bf16x8 pa[kRBW];
+        for (int r = 0; r < RB; ++r)
+          if (flags[r] == 1) {
+            const f32x4 al4 = *(const lds_f32x4*)(&s_row[r][4 * g]);
+            const float4 al = make_float4(al4[0], al4[1], al4[2], al4[3]);
 #pragma unroll
-      for (int r = 0; r < kRBW; ++r) {
-        float psum = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const float e0 = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][tb][i] - m[r]);
-            const float e1 = m[r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][tb][i + 1] - m[r]);
-            psum += e0 + e1;
-            pk[2 * tb + i / 2] = pack_bf16(e0, e1);
+            for (int d = 0; d < kCols; ++d) {
+              acc[r][d][0] *= al.x;
+              acc[r][d][1] *= al.y;
+              acc[r][d][2] *= al.z;
+              acc[r][d][3] *= al.w;
+            }
           }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        lsum[r] += psum;
-        pa[r] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
       }
+      bf16x8 pa[RB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r) pa[r] = *(const lds_bf16x8*)(pbuf + (r * 64 + lane) * 16);
 
-      // ---- O += P . V for both row blocks, V read transposed once ----
+      // ---- O[:, own columns] += P . V, each V read feeding every row block ----
       const lds_char* vbase[2][4];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -338,21 +362,23 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) vbase[half][rr] = b0 + 32 * (rr ^ (xs >> 1));
       }
-      auto tile_v = [&](int d) {
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[0][d & 3] + 128 * (d >> 2)));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[1][d & 3] + 128 * (d >> 2)));
+      auto tile_v = [&](int c) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[0][c & 3] + 128 * (c >> 2)));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[1][c & 3] + 128 * (c >> 2)));
         return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      constexpr int kPrefetch = 4;
+      constexpr int kPrefetch = NW > 4 ? 2 : kCols < 4 ? kCols : 4;
       bf16x8 vq[kPrefetch];
 #pragma unroll
-      for (int d = 0; d < kPrefetch; ++d) vq[d] = tile_v(d);
+      for (int d = 0; d < kPrefetch; ++d) vq[d] = tile_v(c_begin + min(d, c_count - 1));
 #pragma unroll
-      for (int d = 0; d < kDb; ++d) {
-        const bf16x8 vb = vq[d % kPrefetch];
-        if (d + kPrefetch < kDb) vq[d % kPrefetch] = tile_v(d + kPrefetch);
+      for (int d = 0; d < kCols; ++d) {
+        if (d < c_count) {
+          const bf16x8 vb = vq[d % kPrefetch];
+          if (d + kPrefetch < kCols) vq[d % kPrefetch] = tile_v(c_begin + min(d + kPrefetch, c_count - 1));
 #pragma unroll
-        for (int r = 0; r < kRBW; ++r) acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[r], vb, acc[r][d], 0, 0, 0);
+          for (int r = 0; r < RB; ++r) acc[r][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[r], vb, acc[r][d], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       return true;
@@ -372,32 +398,35 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
     }
 
     // ---- normalise and write this unit's partials (tiled layout) ----
-#pragma unroll
-    for (int r = 0; r < kRBW; ++r) {
-      const int rb = kRBW * wave + r;
-      const int row = rb * 16 + li;
-      const float inv = lsum[r] > 0.f ? 1.f / lsum[r] : 0.f;
-      float inv_r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) inv_r[i] = __shfl(inv, 4 * g + i);
-      if (g == 0 && row < a.R)
-        a.part_lse[slot * a.R + row] = lsum[r] > 0.f ? (m[r] + log2f(lsum[r])) * kLn2 : -INFINITY;
-      if (rb < row_blocks && rb * 16 + 4 * g < a.R) {
-        float* dst = a.part_o + ((slot * row_blocks + rb) * kDb * 64 + lane) * 4;
-#pragma unroll
-        for (int d = 0; d < kDb; ++d)
-          *reinterpret_cast<float4*>(dst + 256 * d) =
-              make_float4(acc[r][d][0] * inv_r[0], acc[r][d][1] * inv_r[1], acc[r][d][2] * inv_r[2],
-                          acc[r][d][3] * inv_r[3]);
+    if (owner) {
+      if (g == 0) {
+        s_row[wave][li] = lsum > 0.f ? 1.f / lsum : 0.f;
+        if (row_ok) a.part_lse[slot * a.R + row] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
       }
+    }
+    wait_lgkm0();
+    lds_barrier();  // every row's 1/sum is in LDS
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      if (r * 16 + 4 * g >= a.R) continue;  // lanes holding only padding rows
+      const f32x4 inv4 = *(const lds_f32x4*)(&s_row[r][4 * g]);
+      const float4 inv = make_float4(inv4[0], inv4[1], inv4[2], inv4[3]);
+      float* dst = a.part_o + ((slot * row_blocks + r) * kDb * 64 + lane) * 4;
+#pragma unroll
+      for (int d = 0; d < kCols; ++d)
+        if (d < c_count)
+          *reinterpret_cast<float4*>(dst + 256 * (c_begin + d)) =
+              make_float4(acc[r][d][0] * inv.x, acc[r][d][1] * inv.y, acc[r][d][2] * inv.z, acc[r][d][3] * inv.w);
     }
   }
 }
 
 }  // namespace
 
-// Workgroups of ceil(R / 32) waves, one per CU (the accumulators of two row
-// blocks fill a SIMD's registers).
+// One workgroup per CU.  Up to four row blocks: one wave per row block (at
+// least two), each with a whole SIMD's registers.  Five to eight row blocks:
+// eight waves, two per SIMD, of which the first RB own row blocks; all eight
+// split the PV columns, which keeps the SIMDs' matrix work close to even.
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32) {
   return fmt == kFP8 && dc == kDc && dr == kDr && !q_f32 && R >= 1 && R <= 128;
 }
@@ -406,7 +435,7 @@ hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s) {
   const unsigned units = a.num_splits > 0 ? (unsigned)(a.B * a.num_splits) : (unsigned)a.workers;
   switch ((a.R + 15) / 16) {
 #define MLA_CASE(N) \
-  case N: decode_fp8_kernel<(N < 2 ? 2 : N), 1><<<units, 64 * (N < 2 ? 2 : N), 0, s>>>(a); break;
+  case N: decode_fp8_kernel<(N < 2 ? 2 : N <= 4 ? N : 8), N><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); break;
     MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
 #undef MLA_CASE
     default: return hipErrorInvalidValue;

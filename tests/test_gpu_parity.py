@@ -214,6 +214,58 @@ def test_row_counts(kernel, heads, sq):
     assert np.max(np.abs(step.lse.cpu().numpy() - ref_lse)) <= lse_tol(kernel)
 
 
+@pytest.mark.parametrize("heads,sq", [(4, 1), (20, 1), (33, 1), (16, 4), (20, 4), (25, 4), (32, 4)])
+def test_fp8_row_counts(heads, sq):
+    """fp8 cache with bf16 queries on the matrix cores: one to eight 16-row
+    blocks (2, 3, 4 or 8 waves; with five or more row blocks, waves without
+    rows of their own take PV columns only)."""
+    from mla_paged_decode_amd import MLA_BF16
+    lens = (40, 129, 300)
+    wl = WORKLOADS["fp8_mtp4_b64_h20_ctx16k"].with_(batch=3, heads=heads, q_per_seq=sq, lens=("fixed", lens))
+    say(f"[fp8 rows] H={heads} Sq={sq}")
+    inp = make_inputs(wl, poison_tail=True)
+    q_abs = bf16_bits_from_f32(make_q_abs(wl))
+    step = run_step(inp, kernel=MFMA, q_abs=q_abs, q_abs_dtype=MLA_BF16)
+    ref_o, ref_lse = oracle.latent_attention(oracle.bf16_to_f64(q_abs), inp)
+    o, lse = step.o_latent.cpu().numpy(), step.lse.cpu().numpy()
+    err = rel_err(o, ref_o)
+    say(f"  o rel err {err:.3e}")
+    assert err <= TAU_FP8
+    assert np.max(np.abs(lse - ref_lse)) <= lse_tol(MFMA)
+
+
+@pytest.mark.parametrize("kernel", kernels())
+@pytest.mark.parametrize("name", ["glm_b32_h20_ctx4096_bf16", "fp8_mtp4_b64_h20_ctx16k"])
+def test_wide_score_range(kernel, name):
+    """Queries scaled by 64: scores spread over hundreds of powers of two, so
+    later tiles exceed the main loop's reference maximum by more than its
+    headroom and the rescaling loop takes over."""
+    from mla_paged_decode_amd import MLA_BF16
+    lens = (300, 1000)
+    wl = WORKLOADS[name].with_(batch=len(lens), lens=("fixed", lens))
+    skip_unsupported(kernel, wl)
+    say(f"[wide scores] {name} kernel={kernel}")
+    inp = make_inputs(wl, poison_tail=True)
+    q_abs = (make_q_abs(wl) * 64.0).astype(np.float32)
+    qd = None
+    if kernel == MFMA and wl.heads * wl.q_per_seq > 64:
+        q_abs, qd = bf16_bits_from_f32(q_abs), MLA_BF16
+    step = run_step(inp, kernel=kernel, q_abs=q_abs, q_abs_dtype=qd)
+    q_ref = oracle.bf16_to_f64(q_abs) if q_abs.dtype == np.uint16 else q_abs.astype(np.float64)
+    ref_o, ref_lse = oracle.latent_attention(q_ref, inp)
+    o, lse = step.o_latent.cpu().numpy(), step.lse.cpu().numpy()
+    assert np.isfinite(o).all()
+    err = rel_err(o, ref_o)
+    say(f"  o rel err {err:.3e}")
+    # fp32 scores carry a relative rounding error, so their absolute error,
+    # which the exponential turns into a relative error of the weights,
+    # grows with the 64x scale; the fp32 path's bound grows with it.  The
+    # matrix-core bounds are set by bf16 rounding and hold as they are.
+    tau = tau_for(kernel, wl.kv_format) * (64 if kernel == SIMT else 1)
+    assert err <= tau
+    assert np.max(np.abs(lse - ref_lse)) <= lse_tol(kernel) * 64
+
+
 @pytest.mark.parametrize("P", [16, 32, 64, 128])
 def test_page_sizes_mfma(P):
     """Every supported page-block size, with tiles straddling page ends."""
