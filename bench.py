@@ -72,7 +72,7 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
-COUNTER_SOURCES = ["decode_mfma.hip", "decode_common.h", "schedule.h", "internal.h", "device_common.h"]
+COUNTER_SOURCES = ["decode_mfma.hip", "decode_fp8.hip", "decode_common.h", "schedule.h", "internal.h", "device_common.h"]
 
 
 def kernel_source_digest() -> str:
@@ -85,12 +85,18 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-def counter_traffic(workload: str):
+def counter_file(workload: str, splits: int) -> str:
+    """Name of the committed counter summary of a workload (and split mode)."""
+    tag = "" if splits == 0 else f"_splits{splits}"
+    return os.path.join(ROOT, "profiles", f"decode_mfma_{workload}{tag}_counters.txt")
+
+
+def counter_traffic(workload: str, splits: int = 0):
     """HBM bytes per attention-kernel launch from the committed counter
     summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the
     same counter's reading for a plain copy of known size), or None if there
     is none or the kernel has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_counters.txt")
+    path = counter_file(workload, splits)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -278,7 +284,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": counter_traffic(wl.name),
+            "traffic": counter_traffic(wl.name, splits),
         },
         "cpu_baseline": base,
     }
