@@ -100,11 +100,17 @@ def check_empty_rows(inp, o, lse):
 
 # ------------------------------------------------------- single steps --
 
-@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16"])
+def proj_batch(name):
+    """Small batches for most cases; the 256-sequence workload at full size
+    (5,120 rows of queries or outputs)."""
+    return WORKLOADS[name].batch if name.startswith("ragged") else min(WORKLOADS[name].batch, 8)
+
+
+@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16", "ragged_b256_h20_ctx512_8k_bf16"])
 @pytest.mark.parametrize("out_f32", [True, False])
 def test_absorb_q(name, out_f32):
     import mla_paged_decode_amd as mla
-    wl = WORKLOADS[name].with_(batch=min(WORKLOADS[name].batch, 8), lens=("const", 16))
+    wl = WORKLOADS[name].with_(batch=proj_batch(name), lens=("const", 16))
     say(f"[absorb] {name} out_f32={out_f32}")
     inp = make_inputs(wl)
     from mla_paged_decode_amd.step import DeviceBatch
@@ -127,10 +133,11 @@ def test_absorb_q(name, out_f32):
         assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * rms).all()
 
 
-@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16", "fp8_mtp4_b64_h20_ctx16k"])
+@pytest.mark.parametrize("name", ["tiny_b2_h4_f32", "glm_b32_h20_ctx4096_bf16", "fp8_mtp4_b64_h20_ctx16k",
+                                  "ragged_b256_h20_ctx512_8k_bf16"])
 def test_out_proj(name):
     import mla_paged_decode_amd as mla
-    wl = WORKLOADS[name].with_(batch=min(WORKLOADS[name].batch, 8), lens=("const", 16))
+    wl = WORKLOADS[name].with_(batch=proj_batch(name), lens=("const", 16))
     say(f"[out_proj] {name}")
     inp = make_inputs(wl)
     o_lat = make_o_latent(wl)
