@@ -173,7 +173,7 @@ __device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) 
 }
 
 template <int DPW>
-__global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kTiledThreads, 4) void combine_tiled_kernel(DecodeArgs a) {
   constexpr int kShare = DPW >= kTiledWaves ? 1 : kTiledWaves / DPW;  // waves per column block
   constexpr int kDW = DPW >= kTiledWaves ? DPW / kTiledWaves : 1;     // column blocks per wave
   __shared__ int32_t s_slot[kChunk];
@@ -234,8 +234,12 @@ __global__ __launch_bounds__(kTiledThreads) void combine_tiled_kernel(DecodeArgs
   auto part_ptr = [&](int d) { return a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4; };
   // Parts of a chunk handled by this wave: share, share + kShare, ...,
   // loaded kBatch at a time.
+  // kBatch partial loads per lane in flight: 8 keeps the kernel under 128
+  // VGPRs, so four of its 4-wave workgroups fit on a CU and a grid of about
+  // 1024 workgroups runs in one round (16 needed about 190 VGPRs, two
+  // workgroups per CU and two rounds).
   constexpr int kPer = kChunk / kShare;
-  constexpr int kBatch = (kShare > 1 ? 16 : 8) < kPer ? (kShare > 1 ? 16 : 8) : kPer;  // divides kPer
+  constexpr int kBatch = 8 < kPer ? 8 : kPer;  // divides kPer
   float4 p[kBatch];
   auto load_parts = [&](int64_t c0, int j0, int d) {
     const float* po = part_ptr(d);
@@ -365,7 +369,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
     const int64_t cells = (int64_t)a.B * ((a.R + 15) / 16) * kdb;
     const int64_t parts = a.num_splits > 0 ? a.num_splits : (a.workers + a.B - 1) / a.B + 1;
     int dpw = 1;
-    while (dpw < 32 && cells / (2 * dpw) >= 1024 && kdb % (2 * dpw) == 0) dpw *= 2;
+    while (dpw < 16 && cells / (2 * dpw) >= 1024 && kdb % (2 * dpw) == 0) dpw *= 2;
     if (parts > 32 && dpw > 1) dpw = 1;
     const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)(kdb / dpw));
     switch (dpw) {
@@ -373,8 +377,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
       case 2: combine_tiled_kernel<2><<<grid, kTiledThreads, 0, s>>>(a); break;
       case 4: combine_tiled_kernel<4><<<grid, kTiledThreads, 0, s>>>(a); break;
       case 8: combine_tiled_kernel<8><<<grid, kTiledThreads, 0, s>>>(a); break;
-      case 16: combine_tiled_kernel<16><<<grid, kTiledThreads, 0, s>>>(a); break;
-      default: combine_tiled_kernel<32><<<grid, kTiledThreads, 0, s>>>(a); break;
+      default: combine_tiled_kernel<16><<<grid, kTiledThreads, 0, s>>>(a); break;
     }
   } else {
     combine_kernel<<<dim3((unsigned)((int64_t)a.B * a.R)), kCombineThreads, 0, s>>>(a);

@@ -297,13 +297,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     const int64_t slot = unit.slot;
 
     // Unless the unit's first tile is already in flight, its queries are
-    // loaded first and its first tiles are issued after them: the tile
-    // transfers complete in order after everything issued before them, so
-    // queries requested after the tiles would only arrive with the last of
-    // them, while queries requested first arrive in about one memory latency
-    // (the page lookups overlap it).  With early issue every ring buffer is
-    // free here, so kPro = NBUF tiles start at once (one more than in the
-    // loop).
+    // loaded first and its first tiles are issued after them: transfers
+    // complete in order, so queries requested after the tiles would only
+    // arrive with the last of them (measured: tiles issued first land later
+    // too, the start-up burst then being slower).  With early issue every
+    // ring buffer is free here, so kPro = NBUF tiles start at once (one more
+    // than in the loop).
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
     const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
     constexpr int kPro = St::kEarlyIssue ? NBUF : D;
@@ -343,27 +342,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     }
 
     // ---- queries in the B-operand layout: column = row, k = 8g..8g+7 ----
+    // Every load of the row is issued before the first conversion, so the
+    // queries cost one memory round trip.  Padding rows read row 0 (always
+    // in bounds) and are zeroed after the load, which keeps the loads free of
+    // divergent branches; the dtype test is uniform and outside the loads.
     bf16x8 qh[G::kKs], ql[HILO ? G::kKs : 1];
     {
       const int64_t qoff = ((int64_t)b * a.R + (row_ok ? row : 0)) * G::kVals + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < G::kKs; ++ks) {
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (!row_ok) {
-          // padding rows load nothing
-        } else if (a.q_f32) {
-          const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q_abs) + qoff + 32 * ks);
-          const float4 u = p[0], w = p[1];
-          x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
-        } else {
-          const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_abs) + qoff + 32 * ks);
-          const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_bits_to_f32(uw[i] & 0xffffu);
-            x[2 * i + 1] = bf16_bits_to_f32(uw[i] >> 16);
-          }
-        }
+      auto put = [&](int ks, const float (&x)[8]) __attribute__((always_inline)) {
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -373,6 +359,37 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         }
         qh[ks] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
         if constexpr (HILO) ql[ks] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+      };
+      if (uniform(a.q_f32)) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.q_abs) + qoff);
+        float4 raw[G::kKs][2];
+#pragma unroll
+        for (int ks = 0; ks < G::kKs; ++ks) {
+          raw[ks][0] = p[8 * ks];
+          raw[ks][1] = p[8 * ks + 1];
+        }
+#pragma unroll
+        for (int ks = 0; ks < G::kKs; ++ks) {
+          const float4 u = raw[ks][0], w = raw[ks][1];
+          const float x[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+          put(ks, x);
+        }
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q_abs) + qoff);
+        uint4 raw[G::kKs];
+#pragma unroll
+        for (int ks = 0; ks < G::kKs; ++ks) raw[ks] = p[4 * ks];
+#pragma unroll
+        for (int ks = 0; ks < G::kKs; ++ks) {
+          const uint32_t uw[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_bits_to_f32(uw[i] & 0xffffu);
+            x[2 * i + 1] = bf16_bits_to_f32(uw[i] >> 16);
+          }
+          put(ks, x);
+        }
       }
     }
     // The queries are only ever read as the MFMA B operand, which may come

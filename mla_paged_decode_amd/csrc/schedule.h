@@ -123,12 +123,15 @@ __device__ __forceinline__ void wave_plan(const int32_t* lens, int B, int G, int
   const int lane = threadIdx.x & 63;
   const int per = (B + 63) / 64;
   const int b0 = lane * per;
+  // The lane's lengths are loaded together (indices clamped into [0, B), the
+  // extra values masked afterwards), so the plan waits one memory round trip.
   int32_t L[kPlanPerLane];
   int32_t tiles = 0, ne = 0;
 #pragma unroll
+  for (int i = 0; i < kPlanPerLane; ++i) L[i] = lens[min(b0 + i, B - 1)];
+#pragma unroll
   for (int i = 0; i < kPlanPerLane; ++i) {
-    const int b = b0 + i;
-    L[i] = i < per && b < B ? max(lens[b], 0) : 0;
+    L[i] = i < per && b0 + i < B ? max(L[i], 0) : 0;
     tiles += (L[i] + kPlanTile - 1) / kPlanTile;
     ne += L[i] > 0;
   }
