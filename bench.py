@@ -113,6 +113,44 @@ def counter_traffic(workload: str, splits: int = 0):
         return None
 
 
+def cache_write_timing(inp, dev, reps: int):
+    """mla_cache_write of the step's new tokens: B * Sq rows (synthetic,
+    seeded N(0, 1) f32) stored at the slots of the last Sq positions of each
+    sequence, into a copy of the cache; average over reps calls (HIP events
+    on the launch stream)."""
+    import torch
+
+    import mla_paged_decode_amd as mla
+
+    wl = inp.wl
+    P = wl.page_block
+    slots = []
+    for b in range(wl.batch):
+        L = int(inp.seq_lens[b])
+        for j in range(wl.q_per_seq):
+            t = L - wl.q_per_seq + j
+            slots.append(int(inp.block_table[b, t // P]) * P + t % P if t >= 0 else -1)
+    n = len(slots)
+    n_vals = wl.d_latent + wl.d_rope
+    rows = torch.randn((n, n_vals), generator=torch.Generator().manual_seed(7)).cuda()
+    slots_t = torch.tensor(slots, dtype=torch.int64).cuda()
+    pool = dev.kv_pool.clone()
+    fmt = dev.kv_format
+    args = (dev.dims, n, rows, slots_t, pool, fmt, pool.shape[0], P)
+    for _ in range(3):
+        mla.mla_cache_write(*args)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(reps):
+        mla.mla_cache_write(*args)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / reps
+    nbytes = n * n_vals * 4 + n * inp.row_bytes + n * 8
+    return {"rows": n, "us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +282,9 @@ def main() -> int:
         f"{decode_avg_s * 1e6:.1f} us ({achieved_call:.0f} GB/s), attention kernel "
         f"{kernel_avg_s * 1e6:.1f} us ({achieved:.0f} GB/s)")
 
+    cache_write = cache_write_timing(inp, dev, args.steps)
+    log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -287,6 +328,7 @@ def main() -> int:
             "traffic": counter_traffic(wl.name, splits),
         },
         "cpu_baseline": base,
+        "cache_write": cache_write,
     }
     print(json.dumps(line), flush=True)
     return 0

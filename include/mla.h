@@ -184,6 +184,31 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens,
                           const void* w_kv_b, mla_dtype_t w_dtype,
                           void* out, mla_dtype_t out_dtype, void* stream);
 
+/* Cache append: store new tokens' rows into the paged cache.
+ *   rows        [n_rows][d_latent + d_rope]  rows_dtype (F32 or BF16): the
+ *               latent c_t, then the RoPE key k^R_t (already rotated)
+ *   slots       [n_rows] int64, device: physical token slot of row i,
+ *               page * page_block + position in the page; slots[i] < 0, or
+ *               >= num_pages * page_block, leaves the cache untouched for row i
+ *   kv_pool     [num_pages][page_block][row bytes of kv_format], written in
+ *               place; only the rows named by slots change
+ * Formats: MLA_KV_F32 stores the values; MLA_KV_BF16 rounds them to nearest,
+ * ties to even; MLA_KV_FP8_E4M3_E8M0 (d_latent 448 + d_rope 64 = 512 values)
+ * quantises each block of 32 values with the scale 2^(E - 127), E the
+ * smallest exponent in [0, 254] with max|value| <= 448 * 2^(E - 127) (127 for
+ * an all-zero block), and stores each value / scale as the nearest e4m3fn
+ * value, ties to the even code, sign taken from the value (-0 -> 0x80).
+ * Inputs must be finite.  Two rows with the same slot race.  Source: the
+ * cache row layouts of the model record "GLM-4.7-Flash" (SERVICEABILITY
+ * JOIN: latent plus RoPE key per token; ENGINE KERNEL CONSTRAINTS (2): the
+ * 528-byte e4m3 row with per-token e8m0 scales).  Errors: see the
+ * conventions above (pool and rows 16-byte aligned, slots 8-byte aligned). */
+mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows,
+                             const void* rows, mla_dtype_t rows_dtype,
+                             const int64_t* slots,
+                             void* kv_pool, mla_kv_format_t kv_format,
+                             int64_t num_pages, int32_t page_block, void* stream);
+
 const char* mla_status_string(mla_status_t status);
 /* Message of the last failed call on this thread ("" if none). */
 const char* mla_last_error_message(void);

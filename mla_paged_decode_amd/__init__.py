@@ -17,7 +17,7 @@ from typing import Optional
 __all__ = [
     "MlaError", "Dims", "DecodeParams", "lib", "library_path",
     "mla_kv_row_bytes", "mla_absorb_q", "mla_decode_workspace_size",
-    "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_abi_version",
+    "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_cache_write", "mla_abi_version",
     "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
 ]
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.mla_absorb_q.restype = st
         L.mla_out_proj.argtypes = [ctypes.POINTER(Dims), i32, vp, st, vp, st, vp, st, vp]
         L.mla_out_proj.restype = st
+        L.mla_cache_write.argtypes = [ctypes.POINTER(Dims), i32, vp, st, vp, vp, st, ctypes.c_int64, i32, vp]
+        L.mla_cache_write.restype = st
         L.mla_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(ctypes.c_size_t)]
         L.mla_decode_workspace_size.restype = st
         L.mla_decode_select_kernel.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(ctypes.c_int)]
@@ -175,6 +177,15 @@ def mla_out_proj(dims, n_tokens: int, o_latent, w_kv_b, out, *, w_dtype=None, st
     _check(lib().mla_out_proj(ctypes.byref(_dims(dims)), n_tokens,
                               _ptr(o_latent), MLA_F32, _ptr(w_kv_b), _dtype_code(w_kv_b, w_dtype),
                               _ptr(out), MLA_F32, _stream(stream)))
+
+
+def mla_cache_write(dims, n_rows: int, rows, slots, kv_pool, kv_format: int, num_pages: int,
+                    page_block: int, *, rows_dtype=None, stream=None) -> None:
+    """Store rows [n_rows][d_latent + d_rope] at the int64 token slots
+    (page * page_block + offset) of kv_pool, in kv_format."""
+    _check(lib().mla_cache_write(ctypes.byref(_dims(dims)), n_rows, _ptr(rows), _dtype_code(rows, rows_dtype),
+                                 _ptr(slots), _ptr(kv_pool), kv_format, num_pages, page_block,
+                                 _stream(stream)))
 
 
 def make_decode_params(*, dims, batch, q_per_seq, q_abs, kv_pool, kv_format, num_pages,

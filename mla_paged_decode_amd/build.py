@@ -29,6 +29,7 @@ SOURCES = [
     "decode_fp8.hip",
     "proj_simt.hip",
     "proj_mfma.hip",
+    "cache_write.hip",
 ]
 
 FLAGS = [

@@ -229,6 +229,43 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens, const void* 
   return ok();
 }
 
+mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows, const void* rows, mla_dtype_t rows_dtype,
+                             const int64_t* slots, void* kv_pool, mla_kv_format_t kv_format, int64_t num_pages,
+                             int32_t page_block, void* stream) {
+  if (kv_format != MLA_KV_F32 && kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3_E8M0)
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16) or 2 (fp8 e4m3+e8m0), got %d",
+                (int)kv_format);
+  mla_status_t st = check_dims(dims, latent_for_format(kv_format));
+  if (st) return st;
+  if (n_rows < 0) return fail(MLA_ERR_INVALID_SHAPE, "n_rows: expected >= 0, got %d", n_rows);
+  if (!valid_dtype(rows_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "rows_dtype: expected 0 (f32) or 1 (bf16), got %d", (int)rows_dtype);
+  if (page_block != 16 && page_block != 32 && page_block != 64 && page_block != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "page_block: expected one of {16,32,64,128}, got %d", page_block);
+  if (num_pages < 0) return fail(MLA_ERR_INVALID_SHAPE, "num_pages: expected >= 0, got %lld", (long long)num_pages);
+  if (n_rows == 0) return ok();
+  if (!rows) return fail(MLA_ERR_NULL_POINTER, "rows: expected non-null, got NULL");
+  if (!slots) return fail(MLA_ERR_NULL_POINTER, "slots: expected non-null, got NULL");
+  if (!kv_pool && num_pages > 0) return fail(MLA_ERR_NULL_POINTER, "kv_pool: expected non-null, got NULL");
+  if (!aligned(rows, 16) || !aligned(kv_pool, 16) || !aligned(slots, 8))
+    return fail(MLA_ERR_ALIGNMENT, "rows/kv_pool/slots: expected 16/16/8-byte aligned pointers, got %p/%p/%p", rows,
+                kv_pool, slots);
+  mla::CacheWriteArgs a{};
+  a.n_rows = n_rows;
+  a.n_vals = dims->d_latent + dims->d_rope;
+  a.rows = rows;
+  a.rows_f32 = rows_dtype == MLA_F32;
+  a.slots = slots;
+  a.n_slots = num_pages * (int64_t)page_block;
+  a.pool = static_cast<uint8_t*>(kv_pool);
+  a.row_bytes = (int64_t)mla_kv_row_bytes(dims, kv_format);
+  a.fmt = kv_format;
+  if (a.n_slots == 0) return ok();
+  hipError_t e = mla::launch_cache_write(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mla_cache_write launch", e);
+  return ok();
+}
+
 mla_status_t mla_decode_workspace_size(const mla_decode_params_t* p, size_t* bytes) {
   if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
   mla_status_t st = check_decode_scalars(p);

@@ -93,4 +93,17 @@ bool out_proj_mfma_supported(const ProjArgs& a);
 hipError_t launch_absorb_mfma(const ProjArgs& a, hipStream_t s);
 hipError_t launch_out_proj_mfma(const ProjArgs& a, hipStream_t s);
 
+struct CacheWriteArgs {
+  int64_t n_rows;
+  int n_vals;              // d_latent + d_rope values per row
+  const void* rows;        // [n_rows][n_vals], f32 or bf16
+  int rows_f32;
+  const int64_t* slots;    // [n_rows] physical token slot (page * P + offset), < 0 skips
+  int64_t n_slots;         // num_pages * P; slots at or beyond it are skipped too
+  uint8_t* pool;           // [n_slots][row_bytes]
+  int64_t row_bytes;
+  int fmt;                 // KvFormat
+};
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+
 }  // namespace mla

@@ -2,10 +2,15 @@
 smoke check and the benchmark's CPU-baseline leg use it."""
 from .reference import (  # noqa: F401
     absorb_q,
+    bf16_nearest,
     bf16_to_f64,
+    cache_write,
     combine_partials,
     decode_rows,
+    encode_row,
+    e4m3fn_nearest,
     e4m3fn_value,
+    e8m0_for_block,
     e8m0_value,
     latent_attention,
     mla_decode,

@@ -242,3 +242,95 @@ def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray):
                  (w[..., None] * np.nan_to_num(o_parts)).sum(axis=0) / np.where(finite, z, 1.0)[..., None],
                  0.0)
     return o, lse
+
+
+# ------------------------------------------------------------ cache write --
+# Storing new tokens' rows in the cache's row formats: f32 as is, bf16 by
+# rounding to the nearest bfloat16, and the fp8 row of the model record
+# "GLM-4.7-Flash" (ENGINE KERNEL CONSTRAINTS (2): 512 e4m3 values, RoPE dims
+# included, plus one e8m0 scale per 32 values, 528 B per token).  The
+# record fixes the layout but not how a scale is chosen; the reading taken
+# here is the smallest power of two that brings the block's largest
+# magnitude within the largest e4m3fn value, 448, and round to nearest with
+# ties to even for the codes.  Each step below is the definition searched
+# out directly, with no bit tricks.
+
+_E4M3_NONNEG = _E4M3[:127]  # codes 0..126: 0 and the positive finite values, increasing
+
+
+def e8m0_for_block(amax: float) -> int:
+    """Scale code of a block: the smallest E in [0, 254] with
+    amax <= 448 * 2^(E - 127); 127 (scale 1) for an all-zero block."""
+    if amax == 0.0:
+        return 127
+    for E in range(255):
+        if amax <= 448.0 * 2.0 ** (E - 127):
+            return E
+    return 254
+
+
+def e4m3fn_nearest(x: float) -> int:
+    """Code of the e4m3fn value nearest to x (|x| <= 448), ties to the code
+    whose last (mantissa) bit is 0; the sign bit is x's (so -0.0 -> 0x80)."""
+    mag = abs(float(x))
+    assert mag <= 448.0
+    c = int(np.searchsorted(_E4M3_NONNEG, mag))  # first code with value >= mag
+    if c == 0:
+        best = 0
+    else:
+        lo, hi = c - 1, c
+        d_lo, d_hi = mag - _E4M3_NONNEG[lo], _E4M3_NONNEG[hi] - mag
+        if d_lo < d_hi:
+            best = lo
+        elif d_hi < d_lo:
+            best = hi
+        else:
+            best = lo if lo % 2 == 0 else hi
+    return best | (0x80 if math.copysign(1.0, float(x)) < 0 else 0)
+
+
+def bf16_nearest(x) -> int:
+    """Bits of the bfloat16 nearest to the float32 value x (finite), ties to
+    the even bit pattern; the sign is x's."""
+    u = int(np.asarray(x, dtype=np.float32).view(np.uint32))
+    sign, t = (u >> 16) & 0x8000, (u & 0x7FFFFFFF) >> 16
+    mag = abs(float(np.float32(x)))
+    lo, hi = float(bf16_to_f64(np.uint16(t))), float(bf16_to_f64(np.uint16(t + 1)))
+    if mag - lo < hi - mag:
+        best = t
+    elif hi - mag < mag - lo:
+        best = t + 1
+    else:
+        best = t if t % 2 == 0 else t + 1
+    return sign | best
+
+
+def encode_row(vals, kv_format: str) -> np.ndarray:
+    """One row of values (float64, exactly the f32 / bf16 input) -> stored bytes."""
+    vals = np.asarray(vals, dtype=np.float64)
+    if kv_format == "f32":
+        return vals.astype(np.float32).view(np.uint8)
+    if kv_format == "bf16":
+        return np.array([bf16_nearest(v) for v in vals], dtype=np.uint16).view(np.uint8)
+    assert kv_format == "fp8_e4m3_e8m0" and vals.size % FP8_BLOCK == 0
+    codes, scales = [], []
+    for k in range(vals.size // FP8_BLOCK):
+        block = vals[k * FP8_BLOCK:(k + 1) * FP8_BLOCK]
+        E = e8m0_for_block(float(np.max(np.abs(block))))
+        scales.append(E)
+        codes.extend(e4m3fn_nearest(v / 2.0 ** (E - 127)) for v in block)
+    return np.array(codes + scales, dtype=np.uint8)
+
+
+def cache_write(pool: np.ndarray, rows: np.ndarray, rows_dtype: str, slots, kv_format: str) -> np.ndarray:
+    """A copy of pool ([num_pages][page_block][row_bytes] uint8) with row i
+    of rows ([n][d_latent + d_rope], stored as rows_dtype) encoded at token
+    slot slots[i] = page * page_block + offset; slots outside
+    [0, num_pages * page_block) leave the pool unchanged for that row."""
+    out = np.array(pool, dtype=np.uint8, copy=True)
+    flat = out.reshape(-1, out.shape[-1])
+    vals = to_f64(rows, rows_dtype)
+    for i, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if 0 <= s < flat.shape[0]:
+            flat[s] = encode_row(vals[i], kv_format)
+    return out

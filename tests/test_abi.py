@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -128,3 +128,32 @@ def test_projection_argument_checks(call):
     expect_error(lambda: f(GLM, 4, FAKE + 8, FAKE, FAKE), 4, "expected 16-byte aligned pointers")
     expect_error(lambda: f(GLM, 4, FAKE, FAKE, FAKE, 7), 3, "expected 0 or 1, got 7")
     expect_error(lambda: f(Dims(20, 500, 64, 192, 256), 4, FAKE, FAKE, FAKE), 3, "d_latent: expected a multiple of 32")
+
+
+@pytest.mark.parametrize("kw,status,fragment", [
+    (dict(page_block=96), 3, "page_block"),
+    (dict(dims=GLM, kv_format=MLA_KV_FP8_E4M3_E8M0), 3, "d_latent"),
+    (dict(kv_format=7), 3, "kv_format"),
+    (dict(n_rows=-1), 2, "n_rows"),
+    (dict(rows_dtype=5), 3, "rows_dtype"),
+    (dict(rows=0), 1, "rows"),
+    (dict(slots=0), 1, "slots"),
+    (dict(pool=0), 1, "kv_pool"),
+    (dict(rows=FAKE + 4), 4, "aligned"),
+    (dict(slots=FAKE + 4), 4, "aligned"),
+])
+def test_cache_write_rejects_before_launch(kw, status, fragment):
+    args = dict(dims=GLM, n_rows=8, rows=FAKE, rows_dtype=MLA_F32, slots=FAKE, pool=FAKE,
+                kv_format=MLA_KV_BF16, num_pages=4, page_block=16)
+    args.update(kw)
+    with pytest.raises(MlaError) as e:
+        mla.mla_cache_write(args["dims"], args["n_rows"], args["rows"], args["slots"], args["pool"],
+                            args["kv_format"], args["num_pages"], args["page_block"],
+                            rows_dtype=args["rows_dtype"], stream=0)
+    assert e.value.status == status
+    assert fragment in e.value.message
+
+
+def test_cache_write_without_rows_or_pages_is_a_no_op():
+    mla.mla_cache_write(GLM, 0, 0, 0, 0, MLA_KV_BF16, 4, 16, rows_dtype=MLA_F32, stream=0)
+    mla.mla_cache_write(GLM, 8, FAKE, FAKE, FAKE, MLA_KV_BF16, 0, 16, rows_dtype=MLA_F32, stream=0)
