@@ -16,10 +16,16 @@
 // bf16 parts, so the products are exact to ~16 significant bits;
 // accumulation is fp32.
 //
-// Decode batches are small (tens to hundreds of tokens), so the cost is
-// reading the weights: workgroups are small (16 tokens, one head, 64 output
-// columns, one wave per 16 columns) to spread those reads over the chip.
-// grid = (ceil(N / 16), out_cols / 64, H).
+// Decode batches are small (tens to hundreds of tokens): the weights are
+// read once per step and the cost is memory latency.  A workgroup covers one
+// head, 64 output columns (one wave per 16) and one or more 16-token blocks,
+// keeping its weight slice (LDS or registers) across its blocks; blocks per
+// workgroup are chosen for about 512 workgroups (one block for small
+// batches).  Every load of a block is issued before the first one is waited
+// for, and the next block's inputs before this block's products.
+// grid = (ceil(N / (16 * tok_blocks)), out_cols / 64, H).
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,6 +42,7 @@ constexpr int kWaves = 4;
 constexpr int kTok = 16;                  // tokens per workgroup
 constexpr int kCols = 16 * kWaves;        // output columns per workgroup
 constexpr int kMaxNope = 512;
+constexpr int kMaxRope = 64;            // d_rope (the host accepts 64 only)
 constexpr int kWRow = kCols * 2 + 16;     // LDS row stride (bytes) of the weight tile
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
@@ -51,28 +58,46 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int h = blockIdx.z, c0 = blockIdx.y * kCols;
-  const int n0 = blockIdx.x * kTok;
+  const int n0 = blockIdx.x * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + (int64_t)h * (a.dn + a.dv) * a.dc;
 
   // Weight tile W[0:dn][c0:c0+64] and the query operands: every load is
   // issued before the first one is waited for.
+  // (Indices past the tile are clamped, not branched around, so that the
+  // loads are issued back to back.)
   u32x4 wt[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = j * 64 * kWaves + threadIdx.x;
-    if (i < kChunks) wt[j] = *reinterpret_cast<const u32x4*>(w + (int64_t)(i >> 3) * a.dc + c0 + 8 * (i & 7));
+    const int i = min(j * 64 * kWaves + (int)threadIdx.x, kChunks - 1);
+    wt[j] = *reinterpret_cast<const u32x4*>(w + (int64_t)(i >> 3) * a.dc + c0 + 8 * (i & 7));
   }
-  const int n = n0 + li;
-  const bool n_ok = n < a.N;
   const int qw = a.dn + a.dr, ow = a.dc + a.dr;
-  const uint16_t* q = static_cast<const uint16_t*>(a.in) + ((int64_t)(n_ok ? n : 0) * a.H + h) * qw;
-  bf16x8 qa[NKS];
   const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  // Query operands of a token block (padding tokens read token 0, no branch
+  // around the loads, and use zeros).  The first column block also copies
+  // the RoPE part of the query: thread t holds values t, t + 256, ... of the
+  // block's kTok x d_rope part, loaded with the query operands.
+  constexpr int kRopePer = kTok * kMaxRope / (64 * kWaves);
+  const uint16_t* qin = static_cast<const uint16_t*>(a.in);
+  const bool rope_wg = blockIdx.y == 0;
+  auto load_q = [&](int nb, bf16x8 (&qv)[NKS], uint16_t (&rv)[kRopePer]) __attribute__((always_inline)) {
+    const int n = nb + li;
+    const uint16_t* q = qin + ((int64_t)(n < a.N ? n : 0) * a.H + h) * qw;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    qa[ks] = load_bf16x8(q + 32 * ks + 8 * g);  // padding tokens read token 0 ...
-    if (!n_ok) qa[ks] = zero;                   // ... and use zeros
-  }
+    for (int ks = 0; ks < NKS; ++ks) qv[ks] = load_bf16x8(q + 32 * ks + 8 * g);
+    if (rope_wg) {
+#pragma unroll
+      for (int u = 0; u < kRopePer; ++u) {
+        const int i = min(u * 64 * kWaves + (int)threadIdx.x, kTok * a.dr - 1);
+        const int nn = min(nb + i / a.dr, a.N - 1);
+        rv[u] = qin[((int64_t)nn * a.H + h) * qw + a.dn + i % a.dr];
+      }
+    }
+  };
+  bf16x8 qa[NKS];
+  uint16_t ra[kRopePer];
+  load_q(n0, qa, ra);
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first is waited for
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = j * 64 * kWaves + threadIdx.x;
@@ -80,34 +105,53 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   }
   __syncthreads();
 
-  // This wave's 16 columns c0 + 16 * wave + li.
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The workgroup's token blocks share the weight tile; the next block's
+  // queries are requested before this block's products.
+  const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
+  for (int nb = n0; nb < nb_end; nb += kTok) {
+    bf16x8 qn[NKS];
+    uint16_t rn[kRopePer];
+    if (nb + kTok < nb_end) load_q(nb + kTok, qn, rn);
+    if (nb + li >= a.N) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    const char* rows = w_tile + (32 * ks + 8 * g + (li >> 2)) * kWRow + 32 * wave + 8 * (li & 3);
-    const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)rows);
-    const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + 4 * kWRow));
-    const bf16x8 wb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], wb, acc, 0, 0, 0);
-  }
-
+      for (int ks = 0; ks < NKS; ++ks) qa[ks] = zero;
+    }
+    // This wave's 16 columns c0 + 16 * wave + li.
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nn = n0 + 4 * g + i;
-    if (nn >= a.N) continue;
-    const int64_t o = ((int64_t)nn * a.H + h) * ow + c0 + 16 * wave + li;
-    if (kOutF32) static_cast<float*>(a.out)[o] = acc[i];
-    else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
-  }
-  // The RoPE part of the query is copied unchanged by the first column block.
-  if (blockIdx.y == 0) {
-    for (int i = threadIdx.x; i < kTok * a.dr; i += 64 * kWaves) {
-      const int nn = n0 + i / a.dr, k = i % a.dr;
+    for (int ks = 0; ks < NKS; ++ks) {
+      const char* rows = w_tile + (32 * ks + 8 * g + (li >> 2)) * kWRow + 32 * wave + 8 * (li & 3);
+      const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)rows);
+      const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + 4 * kWRow));
+      const bf16x8 wb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], wb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nn = nb + 4 * g + i;
       if (nn >= a.N) continue;
-      const int64_t r = (int64_t)nn * a.H + h;
-      const uint16_t v = static_cast<const uint16_t*>(a.in)[r * qw + a.dn + k];
-      if (kOutF32) static_cast<float*>(a.out)[r * ow + a.dc + k] = bf16_bits_to_f32(v);
-      else static_cast<uint16_t*>(a.out)[r * ow + a.dc + k] = v;
+      const int64_t o = ((int64_t)nn * a.H + h) * ow + c0 + 16 * wave + li;
+      if (kOutF32) static_cast<float*>(a.out)[o] = acc[i];
+      else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
+    }
+    if (rope_wg) {
+#pragma unroll
+      for (int u = 0; u < kRopePer; ++u) {
+        const int i = u * 64 * kWaves + threadIdx.x;
+        const int nn = nb + i / a.dr, k = i % a.dr;
+        if (i >= kTok * a.dr || nn >= a.N) continue;
+        const int64_t r = (int64_t)nn * a.H + h;
+        if (kOutF32) static_cast<float*>(a.out)[r * ow + a.dc + k] = bf16_bits_to_f32(ra[u]);
+        else static_cast<uint16_t*>(a.out)[r * ow + a.dc + k] = ra[u];
+      }
+    }
+    if (nb + kTok < nb_end) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qa[ks] = qn[ks];
+      if (rope_wg) {
+#pragma unroll
+        for (int u = 0; u < kRopePer; ++u) ra[u] = rn[u];
+      }
     }
   }
 }
@@ -116,66 +160,109 @@ constexpr int kMaxLatent = 512;
 
 template <int NKS>  // NKS = d_latent / 32
 __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) {
-  constexpr int kStep = NKS;  // k-steps of latent operands in flight (all of them)
+  // The token block's fp32 latent rows (16 x d_latent) are the A operand of
+  // all four waves.  They are staged once per workgroup in LDS and read back
+  // per k-step, instead of each wave holding all of them in registers: that
+  // keeps the kernel near 120 VGPRs, four workgroups per CU.  The next
+  // block's rows are requested before this block's products.
+  constexpr int kDc = 32 * NKS;
+  constexpr int kRow = kDc * 4 + 16;  // LDS row stride: rows start 16 B apart in the bank cycle
+  constexpr int kQuads = kDc / 4;     // float4 per row
+  constexpr int kChunks = kTok * kQuads;
+  constexpr int kPer = (kChunks + 64 * kWaves - 1) / (64 * kWaves);
+  __shared__ __attribute__((aligned(16))) char o_tile[kTok * kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const int h = blockIdx.z, v = blockIdx.y * kCols + 16 * wave + li;
-  const int n0 = blockIdx.x * kTok;
-  const int n = n0 + li;
-  const bool n_ok = n < a.N;
-  const float* o = static_cast<const float*>(a.in) + ((int64_t)(n_ok ? n : 0) * a.H + h) * a.dc;
+  const int n0 = blockIdx.x * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + ((int64_t)h * (a.dn + a.dv) + a.dn + v) * a.dc;
 
-  // B operand: this lane's weight row (value column v), all of K.
+  // B operand: this lane's weight row (value column v), all of K, kept for
+  // every token block of the workgroup.
   bf16x8 wb[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) wb[ks] = load_bf16x8(w + 32 * ks + 8 * g);
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Latent rows of token block nb: thread t loads quads t, t + 256, ...
+  // (indices clamped, not branched around; padding tokens read token 0).
+  float4 st[kPer];
+  auto load_rows = [&](int nb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k0 = 0; k0 < NKS; k0 += kStep) {
-    float4 raw[kStep][2];
-#pragma unroll
-    for (int j = 0; j < kStep && k0 + j < NKS; ++j) {
-      // Padding tokens read token 0 (no branch around the loads) and use zeros.
-      raw[j][0] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g);
-      raw[j][1] = *reinterpret_cast<const float4*>(o + 32 * (k0 + j) + 8 * g + 4);
-      if (!n_ok) raw[j][0] = raw[j][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < kPer; ++j) {
+      const int i = min(j * 64 * kWaves + (int)threadIdx.x, kChunks - 1);
+      const int n = nb + i / kQuads;
+      st[j] = reinterpret_cast<const float4*>(static_cast<const float*>(a.in) +
+                                              ((int64_t)(n < a.N ? n : 0) * a.H + h) * a.dc)[i % kQuads];
     }
+  };
+  load_rows(n0);
+  __builtin_amdgcn_sched_barrier(0);  // weights and rows requested before the first wait
+
+  float* out = static_cast<float*>(a.out);
+  const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
+  for (int nb = n0; nb < nb_end; nb += kTok) {
 #pragma unroll
-    for (int j = 0; j < kStep && k0 + j < NKS; ++j) {
-      const float x[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
-                          raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * 64 * kWaves + threadIdx.x;
+      if (i < kChunks) {
+        const int r = i / kQuads;
+        *reinterpret_cast<float4*>(o_tile + r * kRow + 16 * (i % kQuads)) =
+            nb + r < a.N ? st[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    __syncthreads();
+    if (nb + kTok < nb_end) load_rows(nb + kTok);
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* arow = o_tile + li * kRow + 32 * g;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const float4 x0 = *reinterpret_cast<const float4*>(arow + 128 * ks);
+      const float4 x1 = *reinterpret_cast<const float4*>(arow + 128 * ks + 16);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) split_bf16x2(x[2 * i], x[2 * i + 1], hw[i], lw[i]);
       const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
       const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[k0 + j], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[k0 + j], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[ks], acc, 0, 0, 0);
     }
-  }
-  float* out = static_cast<float*>(a.out);
-  const int vc = blockIdx.y * kCols + 16 * wave + li;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nn = n0 + 4 * g + i;
-    if (nn < a.N) out[((int64_t)nn * a.H + h) * a.dv + vc] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      const int nn = nb + 4 * g + i;
+      if (nn < a.N) out[((int64_t)nn * a.H + h) * a.dv + v] = acc[i];
+    }
+    __syncthreads();  // the tile is rewritten for the next block
   }
+}
+
+// 16-token blocks per workgroup: about 512 workgroups, so that small batches
+// get one block each and batches of hundreds of tokens a few, with every
+// workgroup's weight slice loaded once for all of them.
+int token_blocks(int N, int col_groups, int H, unsigned& grid_x) {
+  const int nblk = (N + kTok - 1) / kTok;
+  int tb = (int)std::max<int64_t>(1, (int64_t)nblk * col_groups * H / 512);
+  tb = std::min(tb, nblk);
+  const int gx = (nblk + tb - 1) / tb;
+  grid_x = (unsigned)gx;
+  return (nblk + gx - 1) / gx;
 }
 
 }  // namespace
 
 bool absorb_mfma_supported(const ProjArgs& a) {
-  return !a.in_f32 && !a.w_f32 && a.dc % kCols == 0 && a.dn % 32 == 0 && a.dn <= kMaxNope && a.dr % 16 == 0;
+  return !a.in_f32 && !a.w_f32 && a.dc % kCols == 0 && a.dn % 32 == 0 && a.dn <= kMaxNope && a.dr % 16 == 0 && a.dr <= kMaxRope;
 }
 
 bool out_proj_mfma_supported(const ProjArgs& a) {
   return !a.w_f32 && a.dv % kCols == 0 && a.dc % 32 == 0 && a.dc <= kMaxLatent;
 }
 
-hipError_t launch_absorb_mfma(const ProjArgs& a, hipStream_t s) {
-  const dim3 grid((a.N + kTok - 1) / kTok, a.dc / kCols, a.H);
+hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
+  ProjArgs a = args;
+  unsigned gx;
+  a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx);
+  const dim3 grid(gx, a.dc / kCols, a.H);
   switch (a.dn / 32) {
 #define MLA_CASE(K)                                                                   \
   case K:                                                                             \
@@ -190,8 +277,11 @@ hipError_t launch_absorb_mfma(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_out_proj_mfma(const ProjArgs& a, hipStream_t s) {
-  const dim3 grid((a.N + kTok - 1) / kTok, a.dv / kCols, a.H);
+hipError_t launch_out_proj_mfma(const ProjArgs& args, hipStream_t s) {
+  ProjArgs a = args;
+  unsigned gx;
+  a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx);
+  const dim3 grid(gx, a.dv / kCols, a.H);
   switch (a.dc / 32) {
 #define MLA_CASE(K) \
   case K: out_proj_mfma_kernel<K><<<grid, 64 * kWaves, 0, s>>>(a); break;
