@@ -20,8 +20,8 @@
 // read once per step and the cost is memory latency.  A workgroup covers one
 // head, 64 output columns (one wave per 16) and one or more 16-token blocks,
 // keeping its weight slice (LDS or registers) across its blocks; blocks per
-// workgroup are chosen for about 512 workgroups (one block for small
-// batches).  Every load of a block is issued before the first one is waited
+// workgroup are chosen for about 1024 (absorb) or 512 (out_proj) workgroups,
+// one block for small batches.  Every load of a block is issued before the first one is waited
 // for, and the next block's inputs before this block's products.
 // grid = (ceil(N / (16 * tok_blocks)), out_cols / 64, H).
 #include <algorithm>
@@ -236,12 +236,12 @@ __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) 
   }
 }
 
-// 16-token blocks per workgroup: about 512 workgroups, so that small batches
+// 16-token blocks per workgroup: about `target` workgroups, so that small batches
 // get one block each and batches of hundreds of tokens a few, with every
 // workgroup's weight slice loaded once for all of them.
-int token_blocks(int N, int col_groups, int H, unsigned& grid_x) {
+int token_blocks(int N, int col_groups, int H, unsigned& grid_x, int target) {
   const int nblk = (N + kTok - 1) / kTok;
-  int tb = (int)std::max<int64_t>(1, (int64_t)nblk * col_groups * H / 512);
+  int tb = (int)std::max<int64_t>(1, (int64_t)nblk * col_groups * H / target);
   tb = std::min(tb, nblk);
   const int gx = (nblk + tb - 1) / tb;
   grid_x = (unsigned)gx;
@@ -261,7 +261,10 @@ bool out_proj_mfma_supported(const ProjArgs& a) {
 hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
-  a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx);
+  // about 1024 workgroups: at 88 VGPRs and 27 KB of LDS five fit per CU, and
+  // fewer blocks per workgroup measured faster (at 256 tokens, 2 blocks:
+  // 17.6 us; 4 blocks: 19.5 us)
+  a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx, 1024);
   const dim3 grid(gx, a.dc / kCols, a.H);
   switch (a.dn / 32) {
 #define MLA_CASE(K)                                                                   \
@@ -280,7 +283,7 @@ hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
 hipError_t launch_out_proj_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
-  a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx);
+  a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx, 512);
   const dim3 grid(gx, a.dv / kCols, a.H);
   switch (a.dc / 32) {
 #define MLA_CASE(K) \
