@@ -151,6 +151,57 @@ def cache_write_timing(inp, dev, reps: int):
     return {"rows": n, "us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
 
 
+def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int, reps: int):
+    """mla_decode_sparse_paged over topk_width listed tokens per query (a
+    seeded random half of the visible positions, -1 padded): the attention
+    kernel's average duration (HIP events the library records on the launch
+    stream) and the listed rows' bytes per launch."""
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_amd as mla
+
+    wl = inp.wl
+    rng = np.random.default_rng(11)
+    topk = np.full((wl.batch, wl.q_per_seq, topk_width), -1, dtype=np.int32)
+    listed = 0
+    for b in range(wl.batch):
+        for j in range(wl.q_per_seq):
+            limit = int(inp.seq_lens[b]) - wl.q_per_seq + j
+            k = min(topk_width, max(0, limit + 1))
+            if k:
+                topk[b, j, :k] = rng.choice(limit + 1, size=k, replace=False)
+            listed += k
+    N, H = wl.n_tokens, wl.heads
+    o_lat = torch.empty((N, H, wl.d_latent), device="cuda")
+    params = mla.make_decode_params(
+        dims=dev.dims, batch=wl.batch, q_per_seq=wl.q_per_seq, q_abs=q_abs, kv_pool=dev.kv_pool,
+        kv_format=dev.kv_format, num_pages=dev.kv_pool.shape[0], page_block=dev.page_block,
+        block_table=dev.block_table, max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens,
+        softmax_scale=dev.softmax_scale, num_splits=num_splits, o_latent=o_lat, lse=None,
+        q_abs_dtype=q_abs_dtype)
+    nbytes = mla.mla_decode_sparse_workspace_size(params, topk_width)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
+    topk_t = torch.from_numpy(topk).cuda()
+    for _ in range(2):
+        mla.mla_decode_sparse_paged(params, topk_t, topk_width)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for e in evs:
+        params.kernel_start_event, params.kernel_stop_event = e[0].cuda_event, e[1].cuda_event
+        mla.mla_decode_sparse_paged(params, topk_t, topk_width)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    row_bytes = inp.row_bytes
+    return {"topk_width": topk_width, "listed_tokens": listed, "num_splits": num_splits,
+            "kernel": "simt", "attention_kernel_us": us, "bytes": listed * row_bytes,
+            "gbs": listed * row_bytes / (us * 1e-6) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +218,8 @@ def main() -> int:
                     help="total bytes of rotated cache copies (>= 4x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sparse-topk", type=int, default=2048,
+                    help="also time mla_decode_sparse_paged over this many listed tokens per query (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB before the timed "
                          "region, as the reference kernel for scaling byte counters")
@@ -283,6 +336,11 @@ def main() -> int:
         f"{kernel_avg_s * 1e6:.1f} us ({achieved:.0f} GB/s)")
 
     cache_write = cache_write_timing(inp, dev, args.steps)
+    sparse = None
+    if args.sparse_topk > 0:
+        sparse = sparse_timing(inp, dev, step.q_abs, qd, args.sparse_topk, 16, min(args.steps, 10))
+        log(f"[bench] sparse decode over {args.sparse_topk} listed tokens per query: "
+            f"{sparse['attention_kernel_us']:.1f} us ({sparse['gbs']:.0f} GB/s)")
     log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
 
     base = None
@@ -329,6 +387,7 @@ def main() -> int:
         },
         "cpu_baseline": base,
         "cache_write": cache_write,
+        "sparse_decode": sparse,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -172,6 +172,28 @@ mla_status_t mla_decode_select_kernel(const mla_decode_params_t* p, mla_kernel_t
  * size and fp8 row format).  Errors: see the conventions above. */
 mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
 
+/* Sparse top-k decode: each query attends only to the cached tokens its
+ * index list names, as the sparse MLA path of the vLLM API page for
+ * vllm.models.glm5next.common.model prepares it (a per-token buffer of top-k
+ * token indices, padded to whole tiles, padded slots masked).
+ *   topk_indices  [batch][q_per_seq][topk_width] int32, device: logical
+ *                 token positions in the sequence.  Entries < 0 or beyond the
+ *                 query's causal limit (L - Sq + j, as in mla_decode_paged)
+ *                 are padding and masked.  Each listed entry is one score, so
+ *                 a position listed twice counts twice; lists are expected to
+ *                 hold distinct positions.
+ * For query j of sequence b and head h:
+ *   o_lat = sum_{t listed} softmax(s)_t latent_t over the listed tokens,
+ *   lse   = log sum exp(s_t); no listed token: o_lat = 0, lse = -inf.
+ * Every other parameter means what it means for mla_decode_paged, except:
+ * num_splits >= 1 cuts each index list into that many uniform chunks (0 is
+ * rejected), the kernel is the vector-ALU one (kernel = MLA_KERNEL_MFMA is
+ * rejected), and the workspace size comes from
+ * mla_decode_sparse_workspace_size.  Errors: see the conventions above. */
+mla_status_t mla_decode_sparse_workspace_size(const mla_decode_params_t* p, int32_t topk_width, size_t* bytes);
+mla_status_t mla_decode_sparse_paged(const mla_decode_params_t* p, const int32_t* topk_indices,
+                                     int32_t topk_width, void* stream);
+
 /* Value up-projection.
  *   o_latent [n_tokens][H][d_latent]    F32
  *   w_kv_b   [H][d_nope + d_v][d_latent] w_dtype (F32 or BF16)

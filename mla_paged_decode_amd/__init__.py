@@ -18,6 +18,7 @@ __all__ = [
     "MlaError", "Dims", "DecodeParams", "lib", "library_path",
     "mla_kv_row_bytes", "mla_absorb_q", "mla_decode_workspace_size",
     "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_cache_write", "mla_abi_version",
+    "mla_decode_sparse_paged", "mla_decode_sparse_workspace_size",
     "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
 ]
@@ -103,6 +104,11 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_workspace_size.restype = st
         L.mla_decode_select_kernel.argtypes = [ctypes.POINTER(DecodeParams), ctypes.POINTER(ctypes.c_int)]
         L.mla_decode_select_kernel.restype = st
+        L.mla_decode_sparse_workspace_size.argtypes = [ctypes.POINTER(DecodeParams), i32,
+                                                       ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_decode_sparse_workspace_size.restype = st
+        L.mla_decode_sparse_paged.argtypes = [ctypes.POINTER(DecodeParams), vp, i32, vp]
+        L.mla_decode_sparse_paged.restype = st
         L.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeParams), vp]
         L.mla_decode_paged.restype = st
         L.mla_status_string.argtypes = [st]
@@ -220,3 +226,14 @@ def mla_decode_select_kernel(params: DecodeParams) -> int:
 
 def mla_decode_paged(params: DecodeParams, stream=None) -> None:
     _check(lib().mla_decode_paged(ctypes.byref(params), _stream(stream)))
+
+
+def mla_decode_sparse_workspace_size(params: DecodeParams, topk_width: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_decode_sparse_workspace_size(ctypes.byref(params), topk_width, ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_decode_sparse_paged(params: DecodeParams, topk_indices, topk_width: int, stream=None) -> None:
+    """Decode over the cached tokens named by topk_indices [B][Sq][topk_width] int32."""
+    _check(lib().mla_decode_sparse_paged(ctypes.byref(params), _ptr(topk_indices), topk_width, _stream(stream)))

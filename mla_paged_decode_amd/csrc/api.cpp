@@ -129,6 +129,29 @@ WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
 
 }  // namespace mla
 
+namespace {
+
+mla_status_t check_sparse(const mla_decode_params_t* p, int32_t topk_width) {
+  mla_status_t st = check_decode_scalars(p);
+  if (st) return st;
+  if (topk_width < 1 || topk_width > (1 << 24))
+    return fail(MLA_ERR_INVALID_SHAPE, "topk_width: expected 1..16777216, got %d", topk_width);
+  if (p->num_splits < 1)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "num_splits: expected >= 1 (uniform chunks of each index list) for the sparse call, got %d",
+                p->num_splits);
+  if (p->kernel == MLA_KERNEL_MFMA)
+    return fail(MLA_ERR_UNSUPPORTED,
+                "kernel: expected MLA_KERNEL_AUTO or MLA_KERNEL_SIMT (the sparse call runs on the vector ALUs), got %d",
+                (int)p->kernel);
+  if ((int64_t)p->batch * p->q_per_seq * p->num_splits > 0x7fffffffLL)
+    return fail(MLA_ERR_INVALID_SHAPE, "batch * q_per_seq * num_splits: expected < 2^31, got %lld",
+                (long long)p->batch * p->q_per_seq * p->num_splits);
+  return MLA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
@@ -263,6 +286,81 @@ mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows, const void*
   if (a.n_slots == 0) return ok();
   hipError_t e = mla::launch_cache_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("mla_cache_write launch", e);
+  return ok();
+}
+
+mla_status_t mla_decode_sparse_workspace_size(const mla_decode_params_t* p, int32_t topk_width, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
+  mla_status_t st = check_sparse(p, topk_width);
+  if (st) return st;
+  *bytes = mla::workspace_layout(p->batch * p->q_per_seq, p->dims.num_heads, p->dims.d_latent, p->num_splits).total;
+  return ok();
+}
+
+mla_status_t mla_decode_sparse_paged(const mla_decode_params_t* p, const int32_t* topk_indices, int32_t topk_width,
+                                     void* stream) {
+  mla_status_t st = check_sparse(p, topk_width);
+  if (st) return st;
+  const int B = p->batch, Sq = p->q_per_seq, H = p->dims.num_heads;
+  const int dc = p->dims.d_latent, dr = p->dims.d_rope;
+  if (B == 0) return ok();
+  const struct {
+    const void* ptr;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{p->q_abs, "q_abs", 16},           {p->kv_pool, "kv_pool", 16},
+              {p->block_table, "block_table", 4}, {p->seq_lens, "seq_lens", 4},
+              {p->workspace, "workspace", 16},    {p->o_latent, "o_latent", 16},
+              {topk_indices, "topk_indices", 4}};
+  for (const auto& x : ptrs) {
+    if (!x.ptr) return fail(MLA_ERR_NULL_POINTER, "%s: expected non-null, got NULL", x.name);
+    if (!aligned(x.ptr, x.align))
+      return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
+  }
+  if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
+  const mla::WorkspaceLayout w = mla::workspace_layout(B * Sq, H, dc, p->num_splits);
+  if (p->workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
+                p->workspace_bytes);
+
+  // Every (sequence, query token) pair is one sequence of H query rows.
+  mla::DecodeArgs a{};
+  a.B = B * Sq;
+  a.Sq = 1;
+  a.H = H;
+  a.R = H;
+  a.dc = dc;
+  a.dr = dr;
+  a.q_abs = p->q_abs;
+  a.q_f32 = p->q_abs_dtype == MLA_F32;
+  a.pool = static_cast<const uint8_t*>(p->kv_pool);
+  a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
+  a.P = p->page_block;
+  a.P_log2 = __builtin_ctz((unsigned)p->page_block);
+  a.block_table = p->block_table;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.seq_lens = p->seq_lens;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.num_splits = p->num_splits;
+  a.workers = mla::kBalancedWorkers;
+  char* ws = static_cast<char*>(p->workspace);
+  a.tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start_off);
+  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse_off);
+  a.part_o = reinterpret_cast<float*>(ws + w.part_o_off);
+  a.o = static_cast<float*>(p->o_latent);
+  a.lse = p->lse;
+  a.topk = topk_indices;
+  a.topk_width = topk_width;
+  a.sparse_sq = Sq;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
+    return hip_fail("kernel_start_event record", e);
+  if ((e = mla::launch_decode_simt(a, p->kv_format, s)) != hipSuccess) return hip_fail("sparse decode launch", e);
+  if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
+    return hip_fail("kernel_stop_event record", e);
+  if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);
   return ok();
 }
 

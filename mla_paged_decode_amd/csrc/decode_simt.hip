@@ -7,6 +7,12 @@
 // Workgroup = 256 threads = (16 query rows) x (16 tokens per inner tile) for
 // the scores; the same threads own 2 latent columns x 16 rows of the output
 // accumulator.  grid = (work units, ceil(R / 16)).
+//
+// Sparse top-k mode (DecodeArgs::sparse_sq > 0): a unit covers slots of a
+// (sequence, query token) pair's index list instead of token positions; slot
+// t names the cached token topk[b][t], and slots whose entry is negative or
+// beyond the query's causal limit are masked (padding).  The page-gather
+// and masking are the only differences.
 #include <cmath>
 
 #include "device_common.h"
@@ -28,17 +34,19 @@ __device__ __forceinline__ const uint8_t* row_ptr(const DecodeArgs& a, int b, in
   return a.pool + ((int64_t)page * a.P + (t % a.P)) * a.row_bytes;
 }
 
-// Decode tokens [tt0, min(tt0 + kTok, t1)) into sK as fp32; zero the rest.
+// Decode the tile's tokens into sK as fp32; zero the rest.  pos[k] is the
+// cached position of tile token k, or -1 (no token: past the unit's end, or
+// a masked slot of a sparse index list).
 template <int FMT>
-__device__ void load_tile(const DecodeArgs& a, int b, int tt0, int t1, float (*sK)[kStride]) {
+__device__ void load_tile(const DecodeArgs& a, int b, const int* pos, float (*sK)[kStride]) {
   const int n = a.dc + a.dr;
   if constexpr (FMT == kF32) {
     const int per_row = n / 4;
     for (int idx = threadIdx.x; idx < kTok * per_row; idx += kThreads) {
       const int tk = idx / per_row, c = idx % per_row;
-      const int t = tt0 + tk;
+      const int t = pos[tk];
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < t1) v = *reinterpret_cast<const float4*>(row_ptr(a, b, t) + 16 * c);
+      if (t >= 0) v = *reinterpret_cast<const float4*>(row_ptr(a, b, t) + 16 * c);
       sK[tk][4 * c + 0] = v.x;
       sK[tk][4 * c + 1] = v.y;
       sK[tk][4 * c + 2] = v.z;
@@ -48,9 +56,9 @@ __device__ void load_tile(const DecodeArgs& a, int b, int tt0, int t1, float (*s
     const int per_row = n / 8;
     for (int idx = threadIdx.x; idx < kTok * per_row; idx += kThreads) {
       const int tk = idx / per_row, c = idx % per_row;
-      const int t = tt0 + tk;
+      const int t = pos[tk];
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < t1) v = *reinterpret_cast<const uint4*>(row_ptr(a, b, t) + 16 * c);
+      if (t >= 0) v = *reinterpret_cast<const uint4*>(row_ptr(a, b, t) + 16 * c);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -63,10 +71,10 @@ __device__ void load_tile(const DecodeArgs& a, int b, int tt0, int t1, float (*s
     const int per_row = n / 16;
     for (int idx = threadIdx.x; idx < kTok * per_row; idx += kThreads) {
       const int tk = idx / per_row, c = idx % per_row;
-      const int t = tt0 + tk;
+      const int t = pos[tk];
       uint4 v = make_uint4(0, 0, 0, 0);
       float scale = 0.f;
-      if (t < t1) {
+      if (t >= 0) {
         const uint8_t* row = row_ptr(a, b, t);
         v = *reinterpret_cast<const uint4*>(row + 16 * c);
         scale = e8m0_to_f32(row[n + c / 2]);
@@ -76,7 +84,7 @@ __device__ void load_tile(const DecodeArgs& a, int b, int tt0, int t1, float (*s
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          sK[tk][16 * c + 4 * i + k] = (t < t1) ? e4m3fn_to_f32((w[i] >> (8 * k)) & 0xffu) * scale : 0.f;
+          sK[tk][16 * c + 4 * i + k] = (t >= 0) ? e4m3fn_to_f32((w[i] >> (8 * k)) & 0xffu) * scale : 0.f;
     }
   }
 }
@@ -87,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void decode_simt_kernel(DecodeArgs a) {
   __shared__ float sK[kTok][kStride];
   __shared__ float sP[kRows][kTok + 1];
   __shared__ float sRow[kRows];
+  __shared__ int sPos[kTok];
 
   const int n = a.dc + a.dr;
   const int row0 = blockIdx.y * kRows;
@@ -107,6 +116,10 @@ __global__ __launch_bounds__(kThreads) void decode_simt_kernel(DecodeArgs a) {
       sQ[r][k] = v;
     }
     const bool row_ok = my_r < nrows;
+    // Sparse: pair b is query token jq of sequence sb; its slots name tokens.
+    const int sb = a.sparse_sq ? b / a.sparse_sq : b;
+    const int jq = a.sparse_sq ? b % a.sparse_sq : 0;
+    const int sparse_visible = a.sparse_sq ? max(a.seq_lens[sb], 0) - a.sparse_sq + jq : 0;
     const int j = row_ok ? (row0 + my_r) / a.H : 0;
     const int last_visible = L - a.Sq + j;  // query j sees tokens [0, last_visible]
 
@@ -118,14 +131,28 @@ __global__ __launch_bounds__(kThreads) void decode_simt_kernel(DecodeArgs a) {
       for (int r = 0; r < kRows; ++r) acc[i][r] = 0.f;
 
     for (int tt0 = t0; tt0 < t1; tt0 += kTok) {
-      __syncthreads();  // sK / sP / sRow are free; sQ is written
-      load_tile<FMT>(a, b, tt0, t1, sK);
+      __syncthreads();  // sK / sP / sRow / sPos are free; sQ is written
+      if (tid < kTok) {
+        const int t = tt0 + tid;
+        int p = -1;
+        if (t < t1) {
+          if (!a.sparse_sq) {
+            p = t;
+          } else {
+            p = a.topk[(int64_t)b * a.topk_width + t];
+            if (p < 0 || p > sparse_visible) p = -1;
+          }
+        }
+        sPos[tid] = p;
+      }
       __syncthreads();
-      const int t = tt0 + my_t;
+      load_tile<FMT>(a, sb, sPos, sK);
+      __syncthreads();
       float s = 0.f;
       for (int k = 0; k < n; ++k) s = fmaf(sQ[my_r][k], sK[my_t][k], s);
       s *= a.scale_log2;
-      const bool valid = row_ok && t < t1 && t <= last_visible;
+      const int t = sPos[my_t];
+      const bool valid = row_ok && t >= 0 && (a.sparse_sq || t <= last_visible);
       if (!valid) s = -INFINITY;
       float tmax = s;
 #pragma unroll

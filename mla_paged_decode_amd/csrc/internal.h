@@ -55,6 +55,13 @@ struct DecodeArgs {
   int plan_in_kernel;     // balanced: the decode kernel computes tile_start
   float* o;               // [B][R][dc]
   float* lse;             // [B][R] or null
+  // Sparse top-k mode (vector-ALU kernel, uniform splits): B counts
+  // (sequence, query token) pairs, R = H, and pair b attends to the cached
+  // tokens listed in topk[b][0 .. topk_width) of sequence b / sparse_sq
+  // (query token b % sparse_sq).  sparse_sq = 0: dense.
+  const int32_t* topk;
+  int topk_width;
+  int sparse_sq;
 };
 
 // Workspace layout shared by the size query and the launch.

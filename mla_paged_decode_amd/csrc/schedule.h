@@ -233,7 +233,7 @@ struct UnitIter {
       const int S = a.num_splits;
       u.b = blockIdx.x / S;
       const int s = blockIdx.x % S;
-      u.L = max(lens[u.b], 0);
+      u.L = a.sparse_sq ? a.topk_width : max(lens[u.b], 0);  // sparse: slots of the index list
       const int chunk = ((u.L + S - 1) / S + kPlanTile - 1) / kPlanTile * kPlanTile;
       u.t0 = min(u.L, s * chunk);
       u.t1 = min(u.L, u.t0 + chunk);

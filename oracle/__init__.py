@@ -14,6 +14,7 @@ from .reference import (  # noqa: F401
     e8m0_value,
     latent_attention,
     mla_decode,
+    mla_decode_sparse,
     out_proj,
     row_bytes,
     sequence_rows,

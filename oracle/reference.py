@@ -188,6 +188,45 @@ def mla_decode(inp, seqs: Optional[Iterable[int]] = None,
     return out, lse
 
 
+def mla_decode_sparse(inp, topk: np.ndarray, seqs: Optional[Iterable[int]] = None):
+    """Unabsorbed MLA decode over listed tokens (the sparse top-k path of the
+    vLLM API page for vllm.models.glm5next.common.model: a per-token buffer of
+    top-k cached-token indices, padded, padded slots masked).  Query j of
+    sequence b attends to the cached tokens topk[b, j, :] (logical positions);
+    entries < 0 or past its causal limit L - Sq + j are padding.  Each listed
+    entry is one score (a position listed twice counts twice).  A query with
+    no listed token gets out = 0, lse = -inf.
+
+    Returns out float64 [B*Sq, H, d_v] and lse float64 [B*Sq, H] (NaN for
+    sequences not selected)."""
+    wl = inp.wl
+    B, Sq, H = wl.batch, wl.q_per_seq, wl.heads
+    dn, dc, dv = wl.d_nope, wl.d_latent, wl.d_v
+    topk = np.asarray(topk).reshape(B, Sq, -1)
+    q = to_f64(inp.q, wl.q_dtype)
+    W = to_f64(inp.w_kv_b, wl.w_dtype)
+    out = np.full((B * Sq, H, dv), np.nan)
+    lse = np.full((B * Sq, H), np.nan)
+    for b in (range(B) if seqs is None else list(seqs)):
+        L = int(inp.seq_lens[b])
+        rows = sequence_rows(inp, b, max(L, 0))
+        C, KR = rows[:, :dc], rows[:, dc:]
+        for h in range(H):
+            W_UK, W_UV = W[h, :dn, :], W[h, dn:, :]
+            K = np.concatenate([C @ W_UK.T, KR], axis=1)
+            V = C @ W_UV.T
+            for j in range(Sq):
+                n = b * Sq + j
+                limit = L - Sq + j
+                idx = [int(t) for t in topk[b, j] if 0 <= t <= limit]
+                if not idx:
+                    out[n, h], lse[n, h] = 0.0, -math.inf
+                    continue
+                s = wl.softmax_scale * (K[idx] @ q[n, h])
+                out[n, h], lse[n, h] = _softmax_attend(s, V[idx])
+    return out, lse
+
+
 # ---- the three steps of the absorbed form, each by its own definition ----
 
 def absorb_q(q: np.ndarray, w: np.ndarray, d_nope: int):

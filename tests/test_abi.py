@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -157,3 +157,37 @@ def test_cache_write_rejects_before_launch(kw, status, fragment):
 def test_cache_write_without_rows_or_pages_is_a_no_op():
     mla.mla_cache_write(GLM, 0, 0, 0, 0, MLA_KV_BF16, 4, 16, rows_dtype=MLA_F32, stream=0)
     mla.mla_cache_write(GLM, 8, FAKE, FAKE, FAKE, MLA_KV_BF16, 0, 16, rows_dtype=MLA_F32, stream=0)
+
+
+def sparse_params(**kw):
+    base = dict(dims=GLM, batch=2, q_per_seq=1, q_abs=FAKE, kv_pool=FAKE, kv_format=MLA_KV_BF16, num_pages=8,
+                page_block=64, block_table=FAKE, max_blocks_per_seq=4, seq_lens=FAKE, softmax_scale=0.0625,
+                num_splits=2, workspace=FAKE, workspace_bytes=1 << 30, o_latent=FAKE, lse=None,
+                q_abs_dtype=MLA_F32)
+    base.update(kw)
+    return make_decode_params(**base)
+
+
+@pytest.mark.parametrize("kw,width,status,fragment", [
+    (dict(num_splits=0), 128, 3, "num_splits"),
+    (dict(kernel=MLA_KERNEL_MFMA), 128, 3, "kernel"),
+    (dict(), 0, 2, "topk_width"),
+    (dict(page_block=96), 128, 3, "page_block"),
+    (dict(workspace_bytes=16), 128, 5, "workspace_bytes"),
+])
+def test_sparse_decode_rejects_before_launch(kw, width, status, fragment):
+    with pytest.raises(MlaError) as e:
+        mla.mla_decode_sparse_paged(sparse_params(**kw), FAKE, width, stream=0)
+    assert e.value.status == status
+    assert fragment in e.value.message
+
+
+def test_sparse_decode_null_index_list_and_workspace_size():
+    with pytest.raises(MlaError) as e:
+        mla.mla_decode_sparse_paged(sparse_params(), 0, 128, stream=0)
+    assert e.value.status == 1 and "topk_indices" in e.value.message
+    # every (sequence, query token) pair is a sequence of H rows, padded to 16
+    n1 = mla.mla_decode_sparse_workspace_size(sparse_params(q_per_seq=1), 128)
+    n4 = mla.mla_decode_sparse_workspace_size(sparse_params(q_per_seq=4), 128)
+    assert n4 > 3 * n1 // 2
+    assert n4 >= mla.mla_decode_workspace_size(sparse_params(q_per_seq=4))
