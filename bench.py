@@ -198,7 +198,9 @@ def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int
     us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
     row_bytes = inp.row_bytes
     return {"topk_width": topk_width, "listed_tokens": listed, "num_splits": num_splits,
-            "kernel": "simt", "attention_kernel_us": us, "bytes": listed * row_bytes,
+            "kernel": {1: "simt", 2: "mfma"}[2 if (wl.kv_format == "bf16" and topk_width % 32 == 0
+                                                  and wl.heads <= 64) else 1],
+            "attention_kernel_us": us, "bytes": listed * row_bytes,
             "gbs": listed * row_bytes / (us * 1e-6) / 1e9}
 
 

@@ -140,10 +140,13 @@ mla_status_t check_sparse(const mla_decode_params_t* p, int32_t topk_width) {
     return fail(MLA_ERR_UNSUPPORTED,
                 "num_splits: expected >= 1 (uniform chunks of each index list) for the sparse call, got %d",
                 p->num_splits);
-  if (p->kernel == MLA_KERNEL_MFMA)
+  if (p->kernel == MLA_KERNEL_MFMA &&
+      !mla::decode_mfma_sparse_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope, p->dims.num_heads,
+                                         topk_width))
     return fail(MLA_ERR_UNSUPPORTED,
-                "kernel: expected MLA_KERNEL_AUTO or MLA_KERNEL_SIMT (the sparse call runs on the vector ALUs), got %d",
-                (int)p->kernel);
+                "kernel: the sparse matrix-core kernel needs a bf16 cache, num_heads <= 64 and topk_width a multiple "
+                "of 32 (got kv_format %d, num_heads %d, topk_width %d)",
+                (int)p->kv_format, p->dims.num_heads, topk_width);
   if ((int64_t)p->batch * p->q_per_seq * p->num_splits > 0x7fffffffLL)
     return fail(MLA_ERR_INVALID_SHAPE, "batch * q_per_seq * num_splits: expected < 2^31, got %lld",
                 (long long)p->batch * p->q_per_seq * p->num_splits);
@@ -352,12 +355,16 @@ mla_status_t mla_decode_sparse_paged(const mla_decode_params_t* p, const int32_t
   a.topk = topk_indices;
   a.topk_width = topk_width;
   a.sparse_sq = Sq;
+  const bool use_mfma = p->kernel != MLA_KERNEL_SIMT &&
+                        mla::decode_mfma_sparse_supported(p->kv_format, dc, dr, H, topk_width);
+  a.part_tiled = use_mfma ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
     return hip_fail("kernel_start_event record", e);
-  if ((e = mla::launch_decode_simt(a, p->kv_format, s)) != hipSuccess) return hip_fail("sparse decode launch", e);
+  e = use_mfma ? mla::launch_decode_mfma_sparse(a, s) : mla::launch_decode_simt(a, p->kv_format, s);
+  if (e != hipSuccess) return hip_fail("sparse decode launch", e);
   if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
     return hip_fail("kernel_stop_event record", e);
   if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);

@@ -64,6 +64,38 @@ struct Geo {
   static constexpr int kSrcChunks = kVals / 16;             // stored fp8 16-value chunks per row
 };
 
+// Sparse top-k mode: a tile is 32 consecutive slots of a query's index list;
+// slot k names the cached token list[tt0 + k].  Its physical rows are looked
+// up one tile ahead with scalar loads (counted by lgkmcnt, so the tile
+// transfers' vmcnt accounting is untouched).  Slots that are padding (< 0,
+// past the causal limit, or past the unit's end) read row 0 of the pool,
+// always in bounds, and are cleared in `mask`.
+struct Gather {
+  uint32_t phys[kTile];  // physical row (page * P + offset) per slot
+  uint32_t mask;         // bit k: slot k names a visible token
+};
+
+__device__ __forceinline__ Gather gather_lookup(const DecodeArgs& a, const_i32_ptr list, const_i32_ptr bt, int tt0,
+                                                int t1, int limit) {
+  Gather g;
+  int32_t p[kTile];
+#pragma unroll
+  for (int k = 0; k < kTile; ++k) p[k] = list[tt0 + k];  // in bounds: the list width is a multiple of 32
+  g.mask = 0;
+#pragma unroll
+  for (int k = 0; k < kTile; ++k) {
+    const bool ok = tt0 + k < t1 && p[k] >= 0 && p[k] <= limit;
+    g.mask |= (uint32_t)ok << k;
+    p[k] = ok ? p[k] : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kTile; ++k) {
+    const int32_t pg = bt[p[k] >> a.P_log2];
+    g.phys[k] = (g.mask >> k) & 1 ? (uint32_t)(pg * a.P + (p[k] & (a.P - 1))) : 0u;
+  }
+  return g;
+}
+
 // bf16 tiles go straight from HBM to LDS.  A wave instruction fills 64
 // consecutive 16-B LDS chunks: one token's latent row (lane = swizzled
 // chunk, 1 KB contiguous in HBM), or the RoPE parts of 8 tokens.  Latent rows
@@ -114,6 +146,42 @@ struct DmaStaging {
       return;
     }
     // Last tile of a unit, or a tile across two pages of 16 tokens.
+    load_rows(ts, buf);
+  }
+
+  // Gathered rows (sparse mode): one latent transfer per token and the
+  // RoPE parts of 8 tokens per transfer, as on the per-row path below; the
+  // wave's groups are unrolled with uniform conditions so that the row table
+  // is indexed by constants.
+  __device__ __forceinline__ void load_gather(const Gather& gt, const uint8_t* pool, lds_char* buf) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const uint64_t base = (uint64_t)(uintptr_t)pool;
+#pragma unroll
+    for (int grp = 0; grp < kGroups; ++grp) {
+      if (grp % NW != wave) continue;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = 8 * grp + j;
+        dma16((const void*)(uintptr_t)(base + (uint64_t)gt.phys[k] * kRowBytes), 16u * (lane ^ swz(j)),
+              buf + G::kLatRow * k);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRopeInst; ++r) {
+      if (r % NW != wave) continue;
+      const int t = lane >> 3;  // token 8r + t
+      uint32_t ph = gt.phys[8 * r];
+#pragma unroll
+      for (int x = 1; x < 8; ++x) ph = t == x ? gt.phys[8 * r + x] : ph;
+      const uint64_t addr = base + (uint64_t)ph * kRowBytes + 2 * G::kDc + 16 * ((lane & 7) ^ swz(t));
+      dma16_vaddr((const void*)(uintptr_t)addr, buf + G::kRopeBase + 1024 * r);
+    }
+  }
+
+  __device__ __forceinline__ void load_rows(const TileSrc& ts, lds_char* buf) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < (kGroups + NW - 1) / NW; ++i) {
       const int grp = wave + NW * i;
@@ -215,6 +283,9 @@ struct Staging<kBF16, NW, NBUF> {
   DmaStaging<NW> dma;
   __device__ __forceinline__ void init() { dma.init(); }
   __device__ __forceinline__ void issue(const DecodeArgs&, const TileSrc& ts, lds_char* buf) { dma.load(ts, buf); }
+  __device__ __forceinline__ void issue_gather(const DecodeArgs& a, const Gather& gt, lds_char* buf) {
+    dma.load_gather(gt, a.pool, buf);
+  }
   __device__ __forceinline__ void finish(lds_char*) {}
   // Every wave issues at least kMinOps transfers per tile, so allowing
   // younger * kMinOps outstanding leaves only younger tiles in flight.
@@ -239,7 +310,7 @@ struct Staging<kFP8, NW, NBUF> {
   __device__ __forceinline__ void wait(int) { wait_vmcnt_lgkm0<0>(); }
 };
 
-template <int FMT, bool HILO, int NW, int NBUF>
+template <int FMT, bool HILO, int NW, int NBUF, bool SPARSE = false>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   using G = Geo<FMT>;
   __shared__ __attribute__((aligned(16))) char tiles_mem[NBUF * G::kTileBytes];
@@ -304,7 +375,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     // ring buffer is free here, so kPro = NBUF tiles start at once (one more
     // than in the loop).
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
-    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+    // Sparse: b is a (sequence, query token) pair whose tokens are the ones
+    // its index list names; query token b % sparse_sq sees positions up to
+    // L - Sq + j of sequence b / sparse_sq.
+    const int sb = SPARSE ? uniform(b / a.sparse_sq) : b;
+    const int sparse_limit =
+        SPARSE ? uniform(max(((const_i32_ptr)a.seq_lens)[sb], 0) - a.sparse_sq + b % a.sparse_sq) : 0;
+    const const_i32_ptr list = (const_i32_ptr)(a.topk) + (SPARSE ? (int64_t)b * a.topk_width : 0);
+    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)sb * a.max_blocks;
+    Gather gnext;                      // sparse: rows of the next tile to issue, looked up one tile early
+    uint32_t mask_slot[2] = {0u, 0u};  // sparse: visible-slot mask of the tile in ring buffer 0 / 1
+    static_assert(!SPARSE || NBUF == 2, "sparse masks are kept for a 2-deep ring");
     constexpr int kPro = St::kEarlyIssue ? NBUF : D;
     auto ring_buf = [&](int i) { return tiles + ((ring + i) % NBUF) * G::kTileBytes; };
     TilePages pages_next;  // pages of the next tile to issue, looked up one tile early
@@ -318,12 +399,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
           wait_vmcnt_lgkm0<0>();
           lds_barrier();  // the previous unit's readers of the ring are done
         }
+        if constexpr (!SPARSE) {
 #pragma unroll
-        for (int x = 0; x < kPro; ++x)
-          if (x < ntiles) pages_pro[x] = tile_pages(a, bt, t0 + x * kTile, t1);
+          for (int x = 0; x < kPro; ++x)
+            if (x < ntiles) pages_pro[x] = tile_pages(a, bt, t0 + x * kTile, t1);
+        }
         issued = min(kPro, ntiles);
       }
-      if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+      if constexpr (!SPARSE) {
+        if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+      }
     }
     // First tile of the next unit (pages looked up now, issued after this
     // unit's last tile).
@@ -400,9 +485,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
       if constexpr (HILO) asm volatile("" : "+a"(ql[ks]));
     }
     if (ntiles > 0 && !pre) {
+      if constexpr (SPARSE) {
 #pragma unroll
-      for (int x = 0; x < kPro; ++x)
-        if (x < ntiles) st.issue(a, tile_src(a, pages_pro[x], t1), ring_buf(x));
+        for (int x = 0; x < kPro; ++x)
+          if (x < ntiles) {
+            const Gather gx = gather_lookup(a, list, bt, t0 + x * kTile, t1, sparse_limit);
+            st.issue_gather(a, gx, ring_buf(x));
+            mask_slot[(ring + x) & 1] = gx.mask;
+          }
+        if (issued < ntiles) gnext = gather_lookup(a, list, bt, t0 + issued * kTile, t1, sparse_limit);
+      } else {
+#pragma unroll
+        for (int x = 0; x < kPro; ++x)
+          if (x < ntiles) st.issue(a, tile_src(a, pages_pro[x], t1), ring_buf(x));
+      }
     }
     const int j_q = row_ok ? row / a.H : 0;
     const int last_visible = L - a.Sq + j_q;
@@ -425,9 +521,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
         wait_lgkm0();
         lds_barrier();  // everyone finished tile it-1: its buffer is free
         if (issued <= x && issued < ntiles) {
-          st.issue(a, tile_src(a, pages_next, t1), ring_buf(issued));
-          ++issued;
-          if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+          if constexpr (SPARSE) {
+            st.issue_gather(a, gnext, ring_buf(issued));
+            mask_slot[(ring + issued) & 1] = gnext.mask;
+            ++issued;
+            if (issued < ntiles) gnext = gather_lookup(a, list, bt, t0 + issued * kTile, t1, sparse_limit);
+          } else {
+            st.issue(a, tile_src(a, pages_next, t1), ring_buf(issued));
+            ++issued;
+            if (issued < ntiles) pages_next = tile_pages(a, bt, t0 + issued * kTile, t1);
+          }
         } else if (ahead && !ahead_done && issued <= x) {
           st.issue(a, tile_src(a, pages_ahead, n_t1), ring_buf(ntiles));
           ahead_done = true;
@@ -529,7 +632,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = tt0 + tb * 16 + 4 * g + i;
-          const bool ok = row_ok && t < t1 && t <= last_visible;
+          const bool ok = SPARSE ? row_ok && ((mask_slot[(ring + it) & 1] >> (tb * 16 + 4 * g + i)) & 1u)
+                                 : row_ok && t < t1 && t <= last_visible;
           sv[tb][i] = ok ? s[tb][i] * a.scale_log2 : -INFINITY;
           mx = fmaxf(mx, sv[tb][i]);
         }
@@ -673,6 +777,18 @@ hipError_t launch_nw(const DecodeArgs& a, int nw, hipStream_t s) {
 // row counts still have two waves staging tiles.
 int waves_for(int R) { return max(2, (R + 15) / 16); }
 
+template <bool HILO>
+hipError_t launch_sparse_nw(const DecodeArgs& a, int nw, hipStream_t s) {
+  const unsigned units = (unsigned)(a.B * a.num_splits);
+  switch (nw) {
+    case 2: decode_mfma_kernel<kBF16, HILO, 2, 2, true><<<units, 128, 0, s>>>(a); break;
+    case 3: decode_mfma_kernel<kBF16, HILO, 3, 2, true><<<units, 192, 0, s>>>(a); break;
+    case 4: decode_mfma_kernel<kBF16, HILO, 4, 2, true><<<units, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // fp32 (hi + lo) queries need twice the query registers, which limits them
@@ -683,6 +799,17 @@ bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32) {
   if (!((fmt == kBF16 && dc == 512) || (fmt == kFP8 && dc == 448))) return false;
   const int nw = waves_for(R);
   return nw <= (q_f32 ? 4 : 8);
+}
+
+bool decode_mfma_sparse_supported(int fmt, int dc, int dr, int R, int topk_width) {
+  return fmt == kBF16 && dc == 512 && dr == kDr && R <= 64 && topk_width % kTile == 0 && kRingBf16 == 2;
+}
+
+hipError_t launch_decode_mfma_sparse(const DecodeArgs& a, hipStream_t s) {
+  if (a.num_splits < 1 || !decode_mfma_sparse_supported(kBF16, a.dc, a.dr, a.R, a.topk_width))
+    return hipErrorInvalidValue;
+  const int nw = waves_for(a.R);
+  return a.q_f32 ? launch_sparse_nw<true>(a, nw, s) : launch_sparse_nw<false>(a, nw, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s) {

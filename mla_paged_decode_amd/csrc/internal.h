@@ -81,6 +81,10 @@ bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32);
 hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+// Sparse top-k mode on the matrix cores: bf16 cache, R <= 64, uniform splits,
+// index lists a multiple of 32 wide (tiles never pass the end of a list).
+bool decode_mfma_sparse_supported(int fmt, int dc, int dr, int R, int topk_width);
+hipError_t launch_decode_mfma_sparse(const DecodeArgs& a, hipStream_t s);
 
 struct ProjArgs {
   int N, H, dn, dr, dv, dc;

@@ -170,7 +170,8 @@ def sparse_params(**kw):
 
 @pytest.mark.parametrize("kw,width,status,fragment", [
     (dict(num_splits=0), 128, 3, "num_splits"),
-    (dict(kernel=MLA_KERNEL_MFMA), 128, 3, "kernel"),
+    (dict(kernel=MLA_KERNEL_MFMA), 100, 3, "kernel"),
+    (dict(kernel=MLA_KERNEL_MFMA, kv_format=MLA_KV_F32), 128, 3, "kernel"),
     (dict(), 0, 2, "topk_width"),
     (dict(page_block=96), 128, 3, "page_block"),
     (dict(workspace_bytes=16), 128, 5, "workspace_bytes"),

@@ -37,7 +37,7 @@ def make_lists(inp, frac, width, seed, beyond=0, pad=True):
     return out
 
 
-def run_step(inp, topk, num_splits, q_bf16=False):
+def run_step(inp, topk, num_splits, q_bf16=False, kernel=0):
     import mla_paged_decode_amd as mla
     from mla_paged_decode_amd.step import DeviceBatch
     wl = inp.wl
@@ -53,13 +53,15 @@ def run_step(inp, topk, num_splits, q_bf16=False):
         dims=dev.dims, batch=wl.batch, q_per_seq=wl.q_per_seq, q_abs=q_abs, kv_pool=dev.kv_pool,
         kv_format=dev.kv_format, num_pages=dev.kv_pool.shape[0], page_block=dev.page_block,
         block_table=dev.block_table, max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens,
-        softmax_scale=dev.softmax_scale, num_splits=num_splits, o_latent=o_lat, lse=lse, q_abs_dtype=qd)
+        softmax_scale=dev.softmax_scale, num_splits=num_splits, kernel=kernel, o_latent=o_lat, lse=lse,
+        q_abs_dtype=qd)
     width = topk.shape[-1]
     nbytes = mla.mla_decode_sparse_workspace_size(params, width)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     topk_t = torch.from_numpy(np.ascontiguousarray(topk)).cuda()
-    print(f"sparse {wl.name} B={wl.batch} Sq={wl.q_per_seq} width={width} splits={num_splits}", flush=True)
+    print(f"sparse {wl.name} B={wl.batch} Sq={wl.q_per_seq} width={width} splits={num_splits} kernel={kernel}",
+          flush=True)
     mla.mla_decode_sparse_paged(params, topk_t, width)
     out = torch.full((N, H, wl.d_v), float("nan"), device="cuda")
     mla.mla_out_proj(dev.dims, N, o_lat, dev.w_kv_b, out)
@@ -79,13 +81,46 @@ def check(got, glse, ref, rlse, rows=None, tau=TAU, lse_tol=1e-4):
     assert np.max(np.abs(glse[fin] - rlse[fin]), initial=0.0) <= lse_tol
 
 
+SIMT, MFMA = 1, 2
+# The matrix-core kernel (bf16 cache, hi/lo bf16 products) is held to the
+# pages' bf16 criterion, 1e-2 of the output RMS; it measures ~1e-5.
+BARS = {SIMT: dict(tau=TAU, lse_tol=1e-4), MFMA: dict(tau=1e-2, lse_tol=1e-3)}
+
+
+@pytest.mark.parametrize("kernel", [MFMA, SIMT])
 @pytest.mark.parametrize("num_splits", [1, 3])
-def test_sparse_bf16_single_query(num_splits):
+def test_sparse_bf16_single_query(num_splits, kernel):
     inp = make_inputs(WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=4, lens=("fixed", (300, 1029, 64, 517))))
     topk = make_lists(inp, 0.5, 640, seed=1)
-    got, glse = run_step(inp, topk, num_splits)
+    got, glse = run_step(inp, topk, num_splits, kernel=kernel)
+    ref, rlse = oracle.mla_decode_sparse(inp, topk)
+    check(got, glse, ref, rlse, **BARS[kernel])
+
+
+def test_sparse_bf16_mtp_on_the_matrix_cores():
+    """Four query tokens per sequence, each with its own list (a few entries
+    past its causal limit), gathered on the matrix cores; a second list
+    width (96) checks tiles that end on a list's last slot.  (Single bf16
+    absorbed queries on a bf16 cache are a speed mode beyond the 1e-2 bar on
+    dense decode as well, so they are not held to it here.)"""
+    inp = make_inputs(WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=3, q_per_seq=4,
+                                                                  lens=("fixed", (200, 45, 700))))
+    for width, seed in ((256, 21), (96, 22)):
+        topk = make_lists(inp, 0.3, width, seed=seed, beyond=4)
+        got, glse = run_step(inp, topk, 2, kernel=MFMA)
+        ref, rlse = oracle.mla_decode_sparse(inp, topk)
+        check(got, glse, ref, rlse, **BARS[MFMA])
+
+
+def test_sparse_width_not_a_multiple_of_32_uses_the_vector_alus():
+    import mla_paged_decode_amd as mla
+    inp = make_inputs(WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=2, lens=("fixed", (90, 33))))
+    topk = make_lists(inp, 0.6, 100, seed=23)
+    got, glse = run_step(inp, topk, 2)  # automatic choice
     ref, rlse = oracle.mla_decode_sparse(inp, topk)
     check(got, glse, ref, rlse)
+    with pytest.raises(mla.MlaError, match="topk_width"):
+        run_step(inp, topk, 2, kernel=MFMA)
 
 
 @pytest.mark.parametrize("q_bf16", [False, True])
@@ -107,10 +142,10 @@ def test_sparse_empty_lists_and_empty_sequence():
     inp = make_inputs(WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=3, lens=("fixed", (0, 40, 200))))
     topk = make_lists(inp, 0.3, 128, seed=3)
     topk[2] = -1  # a query whose list is all padding
-    got, glse = run_step(inp, topk, 1)
+    got, glse = run_step(inp, topk, 1)  # matrix cores (bf16 cache, width 128)
     ref, rlse = oracle.mla_decode_sparse(inp, topk)
     assert np.all(ref[[0, 2]] == 0) and np.all(np.isneginf(rlse[[0, 2]]))
-    check(got, glse, ref, rlse)
+    check(got, glse, ref, rlse, **BARS[MFMA])
 
 
 @pytest.mark.slow
@@ -123,4 +158,4 @@ def test_sparse_full_size_sampled():
     got, glse = run_step(inp, topk, 16)
     seqs = [0, 17, 31]
     ref, rlse = oracle.mla_decode_sparse(inp, topk, seqs=seqs)
-    check(got, glse, ref, rlse, rows=seqs)
+    check(got, glse, ref, rlse, rows=seqs, **BARS[MFMA])
