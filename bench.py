@@ -340,7 +340,10 @@ def main() -> int:
     cache_write = cache_write_timing(inp, dev, args.steps)
     sparse = None
     if args.sparse_topk > 0:
-        sparse = sparse_timing(inp, dev, step.q_abs, qd, args.sparse_topk, 16, min(args.steps, 10))
+        # about 512 workgroups (measured: GLM batch best at 16 chunks, 256 sequences at 2-4)
+        pairs = wl.batch * wl.q_per_seq
+        chunks = max(1, min((args.sparse_topk + 31) // 32, round(512 / pairs)))
+        sparse = sparse_timing(inp, dev, step.q_abs, qd, args.sparse_topk, chunks, min(args.steps, 10))
         log(f"[bench] sparse decode over {args.sparse_topk} listed tokens per query: "
             f"{sparse['attention_kernel_us']:.1f} us ({sparse['gbs']:.0f} GB/s)")
     log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
