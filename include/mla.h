@@ -62,11 +62,18 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
  *  MLA_KV_BF16           2 bytes per value   (1,152 B at 512 + 64)
  *  MLA_KV_FP8_E4M3_E8M0  d_latent + d_rope e4m3fn bytes, then one e8m0 byte
  *                        per 32 values; value = e4m3fn * 2^(E - 127)
- *                        (528 B at 448 + 64). */
+ *                        (528 B at 448 + 64).
+ *  MLA_KV_FP4_E2M1_E4M3  (d_latent + d_rope) / 2 bytes of e2m1 codes (value
+ *                        2i in the low nibble of byte i), then one e4m3fn
+ *                        scale byte per 16 values; value = e2m1 * e4m3
+ *                        (288 B at 448 + 64: the model record's fp4 variant;
+ *                        its scale format is this library's reading).  Decode
+ *                        runs on the vector-ALU kernel. */
 typedef enum {
   MLA_KV_F32 = 0,
   MLA_KV_BF16 = 1,
-  MLA_KV_FP8_E4M3_E8M0 = 2
+  MLA_KV_FP8_E4M3_E8M0 = 2,
+  MLA_KV_FP4_E2M1_E4M3 = 3
 } mla_kv_format_t;
 
 typedef enum {
@@ -224,6 +231,11 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens,
  * smallest exponent in [0, 254] with max|value| <= 448 * 2^(E - 127) (127 for
  * an all-zero block), and stores each value / scale as the nearest e4m3fn
  * value, ties to the even code, sign taken from the value (-0 -> 0x80).
+ * MLA_KV_FP4_E2M1_E4M3 (448 + 64 values) quantises each block of 16 values
+ * with the smallest positive e4m3fn scale s for which max|value| <= 6 s (448
+ * if none; 1.0 for an all-zero block) and stores each value as the e2m1 code
+ * nearest to the float32 quotient value / s, ties to the even code, clamped
+ * to +-6, sign taken from the value.
  * Inputs must be finite.  Two rows with the same slot race.  Source: the
  * cache row layouts of the model record "GLM-4.7-Flash" (SERVICEABILITY
  * JOIN: latent plus RoPE key per token; ENGINE KERNEL CONSTRAINTS (2): the

@@ -19,14 +19,15 @@ __all__ = [
     "mla_kv_row_bytes", "mla_absorb_q", "mla_decode_workspace_size",
     "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_cache_write", "mla_abi_version",
     "mla_decode_sparse_paged", "mla_decode_sparse_workspace_size",
-    "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0",
+    "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0", "MLA_KV_FP4_E2M1_E4M3",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
 ]
 
 MLA_F32, MLA_BF16 = 0, 1
-MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0 = 0, 1, 2
+MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0, MLA_KV_FP4_E2M1_E4M3 = 0, 1, 2, 3
 MLA_KERNEL_AUTO, MLA_KERNEL_SIMT, MLA_KERNEL_MFMA = 0, 1, 2
-KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0}
+KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0,
+             "fp4_e2m1_e4m3": MLA_KV_FP4_E2M1_E4M3}
 
 STATUS = {
     0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_INVALID_SHAPE",

@@ -58,12 +58,14 @@ mla_status_t check_dims(const mla_dims_t* d, int d_latent_required) {
 
 bool valid_dtype(int t) { return t == MLA_F32 || t == MLA_BF16; }
 
-int latent_for_format(int fmt) { return fmt == MLA_KV_FP8_E4M3_E8M0 ? 448 : 512; }
+int latent_for_format(int fmt) { return fmt == MLA_KV_FP8_E4M3_E8M0 || fmt == MLA_KV_FP4_E2M1_E4M3 ? 448 : 512; }
+
+bool valid_format(int f) { return f >= MLA_KV_F32 && f <= MLA_KV_FP4_E2M1_E4M3; }
 
 mla_status_t check_decode_scalars(const mla_decode_params_t* p) {
   if (!p) return fail(MLA_ERR_NULL_POINTER, "params: expected non-null, got NULL");
-  if (p->kv_format != MLA_KV_F32 && p->kv_format != MLA_KV_BF16 && p->kv_format != MLA_KV_FP8_E4M3_E8M0)
-    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16) or 2 (fp8 e4m3+e8m0), got %d",
+  if (!valid_format(p->kv_format))
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16), 2 (fp8 e4m3+e8m0) or 3 (fp4 e2m1+e4m3), got %d",
                 (int)p->kv_format);
   mla_status_t st = check_dims(&p->dims, latent_for_format(p->kv_format));
   if (st) return st;
@@ -181,6 +183,7 @@ size_t mla_kv_row_bytes(const mla_dims_t* dims, mla_kv_format_t format) {
     case MLA_KV_F32: return 4 * n;
     case MLA_KV_BF16: return 2 * n;
     case MLA_KV_FP8_E4M3_E8M0: return n % 32 ? 0 : n + n / 32;
+    case MLA_KV_FP4_E2M1_E4M3: return n % 16 ? 0 : n / 2 + n / 16;
   }
   return 0;
 }
@@ -258,8 +261,8 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, int32_t n_tokens, const void* 
 mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows, const void* rows, mla_dtype_t rows_dtype,
                              const int64_t* slots, void* kv_pool, mla_kv_format_t kv_format, int64_t num_pages,
                              int32_t page_block, void* stream) {
-  if (kv_format != MLA_KV_F32 && kv_format != MLA_KV_BF16 && kv_format != MLA_KV_FP8_E4M3_E8M0)
-    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16) or 2 (fp8 e4m3+e8m0), got %d",
+  if (!valid_format(kv_format))
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16), 2 (fp8 e4m3+e8m0) or 3 (fp4 e2m1+e4m3), got %d",
                 (int)kv_format);
   mla_status_t st = check_dims(dims, latent_for_format(kv_format));
   if (st) return st;

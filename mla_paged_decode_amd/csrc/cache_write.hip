@@ -60,6 +60,34 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float x) {
   return code | sign;
 }
 
+// Value of a finite, positive e4m3fn code (exact in float32).
+__device__ __forceinline__ float e4m3fn_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
+  return e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// fp4 block scale: the smallest positive e4m3fn value s with amax <= 6 s
+// (6 s is exact in float32); 0x7E (448) if none, 0x38 (1.0) for amax = 0.
+// The search starts at the e4m3 code nearest to amax / 6 and moves by whole
+// codes, so the comparison, not the rounding of amax / 6, decides.
+__device__ __forceinline__ uint32_t fp4_scale_code(float amax) {
+  if (!(amax > 0.f)) return 0x38u;
+  const float t = fminf(amax * (1.f / 6.f), 448.f);
+  int c = (int)(e4m3fn_encode(t) & 0x7fu);
+  c = max(c, 1);
+  while (c > 1 && amax <= 6.f * e4m3fn_value((uint32_t)(c - 1))) --c;
+  while (c < 126 && amax > 6.f * e4m3fn_value((uint32_t)c)) ++c;
+  return (uint32_t)c;
+}
+
+// e2m1 code of x: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even
+// code, magnitudes past 6 saturate), sign bit from x.
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  const float a = fabsf(x);
+  const uint32_t code = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.f);
+  return code | ((__float_as_uint(x) >> 28) & 8u);
+}
+
 template <int FMT>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void cache_write_kernel(CacheWriteArgs a) {
   const int lane = threadIdx.x & 63;
@@ -78,6 +106,23 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void cache_write_kernel(CacheWr
   } else if constexpr (FMT == kBF16) {
     for (int i = lane; i < n; i += 64)
       reinterpret_cast<uint16_t*>(dst)[i] = a.rows_f32 ? (uint16_t)f32_to_bf16_bits(rf[i]) : rb[i];
+  } else if constexpr (FMT == kFP4) {
+    // n == 512: lane l holds values 8l..8l+7, half of 16-value block l / 2;
+    // its eight codes are one 4-byte store, and even lanes store the scale.
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = value(8 * lane + i);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    const uint32_t sc = fp4_scale_code(amax);
+    const float s = e4m3fn_value(sc);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed |= e2m1_encode(v[i] / s) << (4 * i);
+    *reinterpret_cast<uint32_t*>(dst + 4 * lane) = packed;
+    if ((lane & 1) == 0) dst[n / 2 + (lane >> 1)] = (uint8_t)sc;
   } else {
     // n == 512: lane l holds values 8l..8l+7 of block l / 4.
     float v[8];
@@ -109,6 +154,7 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
     case kF32: cache_write_kernel<kF32><<<blocks, 64 * kRowsPerBlock, 0, s>>>(a); break;
     case kBF16: cache_write_kernel<kBF16><<<blocks, 64 * kRowsPerBlock, 0, s>>>(a); break;
     case kFP8: cache_write_kernel<kFP8><<<blocks, 64 * kRowsPerBlock, 0, s>>>(a); break;
+    case kFP4: cache_write_kernel<kFP4><<<blocks, 64 * kRowsPerBlock, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -66,6 +66,30 @@ __device__ void load_tile(const DecodeArgs& a, int b, const int* pos, float (*sK
         sK[tk][8 * c + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
       }
     }
+  } else if constexpr (FMT == kFP4) {
+    // 32 e2m1 values per 16-byte chunk (value 2i in the low nibble of byte
+    // i), two 16-value blocks with an e4m3fn scale each.
+    const int per_row = n / 32;
+    for (int idx = threadIdx.x; idx < kTok * per_row; idx += kThreads) {
+      const int tk = idx / per_row, c = idx % per_row;
+      const int t = pos[tk];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      float s0 = 0.f, s1 = 0.f;
+      if (t >= 0) {
+        const uint8_t* row = row_ptr(a, b, t);
+        v = *reinterpret_cast<const uint4*>(row + 16 * c);
+        s0 = e4m3fn_to_f32(row[n / 2 + 2 * c]);
+        s1 = e4m3fn_to_f32(row[n / 2 + 2 * c + 1]);
+      }
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float sc = i < 2 ? s0 : s1;  // values 32c .. 32c+15, then 32c+16 .. 32c+31
+          sK[tk][32 * c + 8 * i + k] = (t >= 0) ? e2m1_to_f32((w[i] >> (4 * k)) & 0xfu) * sc : 0.f;
+        }
+    }
   } else {
     // 16 e4m3 values per 16-byte chunk, all inside one 32-value scale block.
     const int per_row = n / 16;
@@ -210,6 +234,7 @@ hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s) {
   switch (fmt) {
     case kF32: decode_simt_kernel<kF32><<<grid, kThreads, 0, s>>>(a); break;
     case kBF16: decode_simt_kernel<kBF16><<<grid, kThreads, 0, s>>>(a); break;
+    case kFP4: decode_simt_kernel<kFP4><<<grid, kThreads, 0, s>>>(a); break;
     default: decode_simt_kernel<kFP8><<<grid, kThreads, 0, s>>>(a); break;
   }
   return hipGetLastError();

@@ -46,6 +46,14 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
 }
 
 // OCP e8m0 scale byte -> 2^(E - 127); 0xff is NaN.
+// OCP e2m1 (fp4): sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0
+// is subnormal (m / 2).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e == 0 ? 0.5f * (float)m : (1.f + 0.5f * (float)m) * (float)(1u << (e - 1));
+  return (c & 8u) ? -mag : mag;
+}
+
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
   if (e == 0xffu) return __uint_as_float(0x7fc00000u);
   if (e == 0) return 0x1p-127f;

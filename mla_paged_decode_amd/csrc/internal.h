@@ -30,7 +30,7 @@ constexpr int kFp8RowsWorkers = 256;
 // (each workgroup scans seq_lens itself); larger ones use the plan kernel.
 constexpr int kMaxInKernelPlan = 512;
 
-enum KvFormat : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+enum KvFormat : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kFP4 = 3 };
 
 struct DecodeArgs {
   int B, Sq, H, R;        // R = Sq * H query rows per sequence

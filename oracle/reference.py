@@ -49,6 +49,7 @@ from typing import Iterable, Optional
 import numpy as np
 
 FP8_BLOCK = 32
+FP4_BLOCK = 16  # values per e4m3 scale of the 288-byte fp4 row
 
 
 # ---------------------------------------------------------------- formats --
@@ -64,6 +65,9 @@ def row_bytes(kv_format: str, d_latent: int, d_rope: int) -> int:
     if kv_format == "fp8_e4m3_e8m0":
         assert n % FP8_BLOCK == 0
         return n + n // FP8_BLOCK
+    if kv_format == "fp4_e2m1_e4m3":
+        assert n % FP4_BLOCK == 0
+        return n // 2 + n // FP4_BLOCK
     raise ValueError(kv_format)
 
 
@@ -93,7 +97,18 @@ def e8m0_value(code: int) -> float:
     return 2.0 ** (code - 127)
 
 
+def e2m1_value(code: int) -> float:
+    """OCP e2m1 (fp4): 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent 0
+    is subnormal (m/2); magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    s = -1.0 if code & 0x8 else 1.0
+    e, m = (code >> 1) & 0x3, code & 0x1
+    if e == 0:
+        return s * m * 0.5
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
 _E4M3 = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+_E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 _E8M0 = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
 
 
@@ -106,6 +121,12 @@ def decode_rows(rows: np.ndarray, kv_format: str, d_latent: int, d_rope: int) ->
         return rows.view(np.float32).astype(np.float64)
     if kv_format == "bf16":
         return bf16_to_f64(rows.view(np.uint16))
+    if kv_format == "fp4_e2m1_e4m3":
+        codes = rows[..., :n // 2]
+        lo, hi = _E2M1[codes & 0xF], _E2M1[codes >> 4]  # value 2i in the low nibble of byte i
+        vals = np.stack([lo, hi], axis=-1).reshape(rows.shape[:-1] + (n,))
+        scales = _E4M3[rows[..., n // 2:]]
+        return vals * np.repeat(scales, FP4_BLOCK, axis=-1)
     vals = _E4M3[rows[..., :n]]
     scales = _E8M0[rows[..., n:]]
     return vals * np.repeat(scales, FP8_BLOCK, axis=-1)
@@ -344,6 +365,47 @@ def bf16_nearest(x) -> int:
     return sign | best
 
 
+_E4M3_POS_FINITE = _E4M3[1:127]  # codes 1..126, the positive finite values
+
+
+def e4m3_scale_for_fp4(amax: float) -> int:
+    """Scale code of a 16-value fp4 block: the smallest positive e4m3fn value s
+    with amax <= 6 * s (6 is the largest e2m1 magnitude); 448 (0x7E) if none
+    is large enough (the values then saturate at +-6), 1.0 (0x38) for an
+    all-zero block."""
+    if amax == 0.0:
+        return 0x38
+    for c in range(1, 127):
+        if amax <= 6.0 * _E4M3[c]:
+            return c
+    return 0x7E
+
+
+def e2m1_nearest(x: float) -> int:
+    """fp4 code of the e2m1 value nearest to x, ties to the even code, |x|
+    clamped to 6; the sign bit is x's."""
+    mag = min(abs(float(x)), 6.0)
+    best = min(range(8), key=lambda c: (abs(_E2M1[c] - mag), c % 2))
+    return best | (0x8 if math.copysign(1.0, float(x)) < 0 else 0)
+
+
+def encode_row_fp4(vals) -> np.ndarray:
+    """One row (a multiple of 16 values) -> the fp4 row: two e2m1 codes per
+    byte (value 2i in the low nibble), then one e4m3 scale per 16 values.  A
+    value is stored as the nearest e2m1 to fl32(value / scale), the quotient
+    rounded once to float32 as the kernel computes it."""
+    vals = np.asarray(vals, dtype=np.float64)
+    codes, scales = [], []
+    for k in range(vals.size // FP4_BLOCK):
+        block = vals[k * FP4_BLOCK:(k + 1) * FP4_BLOCK]
+        sc = e4m3_scale_for_fp4(float(np.max(np.abs(block))))
+        scales.append(sc)
+        s32 = np.float32(_E4M3[sc])
+        codes.extend(e2m1_nearest(float(np.float32(v) / s32)) for v in block)
+    packed = [codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(len(codes) // 2)]
+    return np.array(packed + scales, dtype=np.uint8)
+
+
 def encode_row(vals, kv_format: str) -> np.ndarray:
     """One row of values (float64, exactly the f32 / bf16 input) -> stored bytes."""
     vals = np.asarray(vals, dtype=np.float64)
@@ -351,6 +413,8 @@ def encode_row(vals, kv_format: str) -> np.ndarray:
         return vals.astype(np.float32).view(np.uint8)
     if kv_format == "bf16":
         return np.array([bf16_nearest(v) for v in vals], dtype=np.uint16).view(np.uint8)
+    if kv_format == "fp4_e2m1_e4m3":
+        return encode_row_fp4(vals)
     assert kv_format == "fp8_e4m3_e8m0" and vals.size % FP8_BLOCK == 0
     codes, scales = [], []
     for k in range(vals.size // FP8_BLOCK):

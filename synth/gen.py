@@ -148,6 +148,8 @@ def stored_row_bytes(kv_format: str, d_latent: int, d_rope: int) -> int:
         return 2 * n
     if kv_format == "fp8_e4m3_e8m0":
         return n + n // FP8_BLOCK
+    if kv_format == "fp4_e2m1_e4m3":  # two 4-bit codes per byte, one scale byte per 16 values
+        return n // 2 + n // 16
     raise ValueError(f"unknown kv format {kv_format!r}")
 
 

@@ -36,6 +36,8 @@ def test_row_bytes_match_page_figures(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "page_invariants.json")))
     assert mla.mla_kv_row_bytes(GLM, MLA_KV_BF16) * g["num_layers"] == g["bf16_bytes_per_token_all_layers"]
     assert mla.mla_kv_row_bytes(FP8, MLA_KV_FP8_E4M3_E8M0) == g["fp8_row_bytes"]
+    # the model record's fp4 variant: 288 bytes per token
+    assert mla.mla_kv_row_bytes(FP8, mla.MLA_KV_FP4_E2M1_E4M3) == 288
     assert mla.mla_kv_row_bytes(GLM, MLA_KV_F32) == 2304
     assert mla.mla_kv_row_bytes(GLM, 7) == 0
 
@@ -66,7 +68,7 @@ def expect_error(fn, status, fragment):
     (dict(dims=Dims(129, 512, 64, 192, 256)), 2, "num_heads: expected 1..128, got 129"),
     (dict(dims=Dims(0, 512, 64, 192, 256)), 2, "num_heads: expected 1..128, got 0"),
     (dict(dims=Dims(20, 512, 64, 100, 256)), 3, "d_nope: expected a multiple of 32"),
-    (dict(kv_format=5), 3, "kv_format: expected 0 (f32), 1 (bf16) or 2"),
+    (dict(kv_format=5), 3, "kv_format: expected 0 (f32), 1 (bf16), 2 (fp8 e4m3+e8m0) or 3"),
     (dict(batch=-1), 2, "batch: expected >= 0, got -1"),
     (dict(num_pages=0), 2, "num_pages: expected >= 1, got 0"),
     (dict(max_blocks_per_seq=0), 2, "max_blocks_per_seq: expected >= 1, got 0"),

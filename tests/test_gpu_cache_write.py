@@ -15,7 +15,8 @@ from oracle.reference import _E4M3
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = {"f32": mla.MLA_KV_F32, "bf16": mla.MLA_KV_BF16, "fp8_e4m3_e8m0": mla.MLA_KV_FP8_E4M3_E8M0}
+FORMATS = {"f32": mla.MLA_KV_F32, "bf16": mla.MLA_KV_BF16, "fp8_e4m3_e8m0": mla.MLA_KV_FP8_E4M3_E8M0,
+           "fp4_e2m1_e4m3": mla.MLA_KV_FP4_E2M1_E4M3}
 
 
 def special_rows(n_vals: int, rng) -> np.ndarray:
@@ -47,7 +48,7 @@ def special_rows(n_vals: int, rng) -> np.ndarray:
 
 
 def run_case(fmt: str, rows_dtype: str, n_rows: int, page_block: int, num_pages: int, seed: int):
-    d_lat = 448 if fmt == "fp8_e4m3_e8m0" else 512
+    d_lat = 448 if fmt.startswith("fp") else 512
     n_vals = d_lat + 64
     rb = oracle.row_bytes(fmt, d_lat, 64)
     rng = np.random.default_rng(seed)
@@ -84,7 +85,7 @@ def test_cache_write_bit_exact(fmt, rows_dtype):
     run_case(fmt, rows_dtype, n_rows=40, page_block=16, num_pages=6, seed=1)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3_e8m0"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_e4m3_e8m0", "fp4_e2m1_e4m3"])
 def test_cache_write_batch_of_new_tokens(fmt):
     """One new token per sequence of a 256-sequence batch into 128-token pages."""
     run_case(fmt, "f32", n_rows=256, page_block=128, num_pages=40, seed=2)

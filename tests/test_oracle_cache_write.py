@@ -103,9 +103,9 @@ def test_fp8_round_trip_error_is_at_most_half_a_step():
             assert np.all(np.abs(dec[32 * k:32 * (k + 1)] - blk) <= 0.5 * step * scale + 1e-300)
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_e4m3_e8m0"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8_e4m3_e8m0", "fp4_e2m1_e4m3"])
 def test_cache_write_places_rows_at_their_slots(fmt):
-    d_lat = 448 if fmt == "fp8_e4m3_e8m0" else 512
+    d_lat = 448 if fmt.startswith("fp") else 512
     rb = oracle.row_bytes(fmt, d_lat, 64)
     P, pages = 16, 5
     pool = np.full((pages, P, rb), 0x5A, dtype=np.uint8)
@@ -121,6 +121,58 @@ def test_cache_write_places_rows_at_their_slots(fmt):
         else:
             assert np.all(flat[s] == 0x5A)
     dec = oracle.decode_rows(flat[[17, 0, 79, 33]], fmt, d_lat, 64)
-    tol = {"f32": 0.0, "bf16": 2.0 ** -8, "fp8_e4m3_e8m0": 2.0 ** -3}[fmt]
+    tol = {"f32": 0.0, "bf16": 2.0 ** -8, "fp8_e4m3_e8m0": 2.0 ** -3, "fp4_e2m1_e4m3": 0.5}[fmt]
     ref = rows[[0, 2, 4, 5]].astype(np.float64)
-    assert np.all(np.abs(dec - ref) <= tol * np.abs(ref) + (0 if fmt != "fp8_e4m3_e8m0" else 2.0 ** -6))
+    slack = {"f32": 0, "bf16": 0, "fp8_e4m3_e8m0": 2.0 ** -6, "fp4_e2m1_e4m3": 0.5}[fmt]
+    assert np.all(np.abs(dec - ref) <= tol * np.abs(ref) + slack)
+
+
+# ----------------------------------------------------------- the fp4 row --
+# The model record gives an fp4 variant of the cache at 288 bytes per token.
+# With 512 values that is 256 bytes of 4-bit codes plus 32 scale bytes, one
+# per 16 values; the codes are read as OCP e2m1 and the scales as e4m3fn.
+
+def test_fp4_row_is_288_bytes():
+    assert oracle.row_bytes("fp4_e2m1_e4m3", 448, 64) == 288
+
+
+def test_every_e2m1_code_encodes_to_itself():
+    for c in range(16):
+        v = oracle.e2m1_value(c)
+        assert oracle.e2m1_nearest(v) == c, c
+
+
+def test_e2m1_midpoints_round_to_the_even_code():
+    mags = [oracle.e2m1_value(c) for c in range(8)]
+    for c in range(7):
+        mid = (mags[c] + mags[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e2m1_nearest(mid) == even
+        assert oracle.e2m1_nearest(-mid) == even | 0x8
+    assert oracle.e2m1_nearest(100.0) == 7  # saturates at 6
+
+
+def test_fp4_scale_is_the_smallest_e4m3_that_fits():
+    for c in (1, 8, 40, 56, 100, 126):
+        s = oracle.e4m3fn_value(c)
+        assert oracle.e4m3_scale_for_fp4(6 * s) == c
+        if c < 126:
+            assert oracle.e4m3_scale_for_fp4(6 * s * (1 + 1e-6)) == c + 1
+    assert oracle.e4m3_scale_for_fp4(0.0) == 0x38
+    assert oracle.e4m3_scale_for_fp4(1e9) == 0x7E
+
+
+def test_fp4_round_trip_error_is_at_most_half_a_step():
+    rng = np.random.default_rng(21)
+    for _ in range(8):
+        r = (rng.standard_normal(512) * np.exp(rng.uniform(-6, 6))).astype(np.float32)
+        enc = oracle.encode_row(r.astype(np.float64), "fp4_e2m1_e4m3")
+        dec = oracle.decode_rows(enc[None], "fp4_e2m1_e4m3", 448, 64)[0]
+        for k in range(32):
+            s = oracle.e4m3fn_value(int(enc[256 + k]))
+            blk = r[16 * k:16 * (k + 1)].astype(np.float64)
+            assert np.max(np.abs(blk)) <= 6 * s
+            mag = np.abs(blk) / s
+            step = np.where(mag < 2, 0.5, np.where(mag < 4, 1.0, 2.0))
+            # half a step, plus the float32 rounding of value / scale
+            assert np.all(np.abs(dec[16 * k:16 * (k + 1)] - blk) <= (0.5 * step + 1e-6 * mag) * s)
