@@ -204,6 +204,55 @@ def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int
             "gbs": listed * row_bytes / (us * 1e-6) / 1e9}
 
 
+def fp4_timing(inp, dev, reps: int):
+    """mla_decode_paged over an fp4 copy of the cache (288-byte rows, same
+    pages and lengths): seeded N(0, 1) rows written for every slot by
+    mla_cache_write, then the attention kernel timed with HIP events the
+    library records on the launch stream.  Only for the 448 + 64 row shape."""
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_amd as mla
+
+    wl = inp.wl
+    if wl.d_latent != 448:
+        return None
+    pages, P = dev.kv_pool.shape[0], dev.kv_pool.shape[1]
+    n = pages * P
+    pool = torch.empty((pages, P, 288), dtype=torch.uint8, device="cuda")
+    rows = torch.randn((n, wl.d_latent + wl.d_rope), generator=torch.Generator().manual_seed(5)).cuda()
+    slots = torch.arange(n, dtype=torch.int64, device="cuda")
+    mla.mla_cache_write(dev.dims, n, rows, slots, pool, mla.MLA_KV_FP4_E2M1_E4M3, pages, P)
+    del rows, slots
+    N, H = wl.n_tokens, wl.heads
+    q_abs = torch.empty((N, H, wl.d_latent + wl.d_rope), device="cuda")
+    mla.mla_absorb_q(dev.dims, N, dev.q, dev.w_kv_b, q_abs)
+    o_lat = torch.empty((N, H, wl.d_latent), device="cuda")
+    params = mla.make_decode_params(
+        dims=dev.dims, batch=wl.batch, q_per_seq=wl.q_per_seq, q_abs=q_abs, kv_pool=pool,
+        kv_format=mla.MLA_KV_FP4_E2M1_E4M3, num_pages=pages, page_block=P, block_table=dev.block_table,
+        max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens, softmax_scale=dev.softmax_scale,
+        num_splits=0, o_latent=o_lat, lse=None, q_abs_dtype=mla.MLA_F32)
+    nbytes = mla.mla_decode_workspace_size(params)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
+    mla.mla_decode_paged(params)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for e in evs:
+        params.kernel_start_event, params.kernel_stop_event = e[0].cuda_event, e[1].cuda_event
+        mla.mla_decode_paged(params)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+    nbytes = int(np.sum(inp.seq_lens.astype(np.int64))) * 288
+    used = mla.mla_decode_select_kernel(params)
+    return {"row_bytes": 288, "kernel": {1: "simt", 2: "mfma"}[used], "attention_kernel_us": us,
+            "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +397,10 @@ def main() -> int:
             f"{sparse['attention_kernel_us']:.1f} us ({sparse['gbs']:.0f} GB/s)")
     log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
 
+    fp4 = fp4_timing(inp, dev, min(args.steps, 5))
+    if fp4 is not None:
+        log(f"[bench] fp4 cache copy: attention kernel {fp4['attention_kernel_us']:.1f} us ({fp4['gbs']:.0f} GB/s)")
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -393,6 +446,7 @@ def main() -> int:
         "cpu_baseline": base,
         "cache_write": cache_write,
         "sparse_decode": sparse,
+        "fp4_decode": fp4,
     }
     print(json.dumps(line), flush=True)
     return 0
