@@ -207,8 +207,9 @@ def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int
 def fp4_timing(inp, dev, reps: int):
     """mla_decode_paged over an fp4 copy of the cache (288-byte rows, same
     pages and lengths): seeded N(0, 1) rows written for every slot by
-    mla_cache_write, then the attention kernel timed with HIP events the
-    library records on the launch stream.  Only for the 448 + 64 row shape."""
+    mla_cache_write, bf16 absorbed queries, then the attention kernel timed
+    with HIP events the library records on the launch stream.  Only for the
+    448 + 64 row shape."""
     import numpy as np
     import torch
 
@@ -225,14 +226,14 @@ def fp4_timing(inp, dev, reps: int):
     mla.mla_cache_write(dev.dims, n, rows, slots, pool, mla.MLA_KV_FP4_E2M1_E4M3, pages, P)
     del rows, slots
     N, H = wl.n_tokens, wl.heads
-    q_abs = torch.empty((N, H, wl.d_latent + wl.d_rope), device="cuda")
+    q_abs = torch.empty((N, H, wl.d_latent + wl.d_rope), dtype=torch.bfloat16, device="cuda")
     mla.mla_absorb_q(dev.dims, N, dev.q, dev.w_kv_b, q_abs)
     o_lat = torch.empty((N, H, wl.d_latent), device="cuda")
     params = mla.make_decode_params(
         dims=dev.dims, batch=wl.batch, q_per_seq=wl.q_per_seq, q_abs=q_abs, kv_pool=pool,
         kv_format=mla.MLA_KV_FP4_E2M1_E4M3, num_pages=pages, page_block=P, block_table=dev.block_table,
         max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens, softmax_scale=dev.softmax_scale,
-        num_splits=0, o_latent=o_lat, lse=None, q_abs_dtype=mla.MLA_F32)
+        num_splits=0, o_latent=o_lat, lse=None, q_abs_dtype=mla.MLA_BF16)
     nbytes = mla.mla_decode_workspace_size(params)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes

@@ -41,10 +41,17 @@ constexpr int kVals = kDc + kDr;               // 512 values per row
 constexpr int kKs = kVals / 32;                // 16 QK k-steps
 constexpr int kKsLat = kDc / 32;               // 14 over the latent
 constexpr int kDb = kDc / 16;                  // 28 PV column blocks
-constexpr int kRowBytes = kVals + kVals / 32;  // 528
-constexpr int kRawChunks = kTile * kRowBytes / 16;           // 1056 16-B chunks per tile
-constexpr int kRawInst = (kRawChunks + 63) / 64;             // 17 wave loads per tile
-constexpr int kRawBuf = kRawInst * 1024;                     // raw buffer stride
+// Stored row of each format: fp8 528 B (512 e4m3, then 16 e8m0 scales), fp4
+// 288 B (256 B of e2m1 pairs, value 2i in the low nibble of byte i, then 32
+// e4m3 scales, one per 16 values).
+template <int FMT>
+struct RawRow {
+  static constexpr int kRowBytes = FMT == kFP8 ? kVals + kVals / 32 : kVals / 2 + kVals / 16;  // 528 / 288
+  static constexpr int kChunksPerRow = kRowBytes / 16;      // 33 / 18 16-B chunks
+  static constexpr int kRawChunks = kTile * kChunksPerRow;  // per tile
+  static constexpr int kRawInst = (kRawChunks + 63) / 64;   // 17 / 9 wave loads per tile
+  static constexpr int kRawBuf = kRawInst * 1024;           // raw buffer stride
+};
 constexpr int kRaw = 4;                                      // raw ring depth
 // Converted bf16 tile, as in the bf16 kernel: latent rows (56 chunks) then
 // the RoPE rows (8 chunks), chunks XOR-swizzled by token.
@@ -54,9 +61,12 @@ constexpr int kRopeBase = kTile * kLatRow;         // 28672
 constexpr int kTileBytes = kRopeBase + kTile * kRopeRow;  // 32768
 
 // Raw tile loads: wave w issues instructions w, w + NW, ...; instruction k
-// covers chunks 64k .. 64k + 63 of the tile (row q / 33, chunk q % 33).
-template <int NW>
+// covers chunks 64k .. 64k + 63 of the tile (row q / kChunksPerRow, chunk
+// q % kChunksPerRow).
+template <int FMT, int NW>
 struct RawStaging {
+  using RR = RawRow<FMT>;
+  static constexpr int kRowBytes = RR::kRowBytes, kRawChunks = RR::kRawChunks, kRawInst = RR::kRawInst;
   static constexpr int kMinOps = kRawInst / NW;  // fewest loads any wave issues per tile
 
   __device__ __forceinline__ static void load(const TileSrc& ts, lds_char* buf) {
@@ -80,7 +90,7 @@ struct RawStaging {
       const int k = wave + NW * i;
       if (NW * i + NW <= kRawInst || k < kRawInst) {
         const int q = min(64 * k + lane, kRawChunks - 1);
-        const int row = min(q / 33, ts.n - 1), c = q % 33;
+        const int row = min(q / RR::kChunksPerRow, ts.n - 1), c = q % RR::kChunksPerRow;
         const uint64_t base = row < ts.kb ? ts.base0 : ts.base1;
         dma16_vaddr((const void*)(uintptr_t)(base + (uint64_t)(row * kRowBytes + 16 * c)), buf + 1024 * k);
       }
@@ -88,13 +98,39 @@ struct RawStaging {
   }
 };
 
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
 // Decode a raw tile into the bf16 tile: unit u = (token u / 32, value chunk
 // u % 32 of 16 values), spread over all threads of the workgroup.
-template <int NW>
+template <int FMT, int NW>
 __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile) {
+  constexpr int kRowBytes = RawRow<FMT>::kRowBytes;
   for (int u = threadIdx.x; u < kTile * 32; u += 64 * NW) {
     const int tok = u >> 5, c = u & 31;
     const lds_char* src = raw + tok * kRowBytes;
+    if constexpr (FMT == kFP4) {
+      // 16 e2m1 codes (8 bytes) and their e4m3 scale: an e2m1 value times an
+      // e4m3 scale has at most 5 significant bits, so the bf16 value is the
+      // upper half of the exact fp32 product.
+      const u32x2 v = *(const lds_u32x2*)(src + 8 * c);
+      const float scale = e4m3fn_to_f32((uint32_t)(uint8_t)src[kVals / 2 + c]);
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t byte = (v[i >> 2] >> (8 * (i & 3))) & 0xffu;
+        o[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, e2m1_to_f32(byte >> 4) * scale),
+                                     __builtin_bit_cast(uint32_t, e2m1_to_f32(byte & 0xfu) * scale), 0x07060302u);
+      }
+      const int c0 = 2 * c;
+      lds_char* d0 = c0 < kDc / 8 ? tile + lds_off(tok, c0, kLatRow)
+                                  : tile + kRopeBase + lds_off(tok, c0 - kDc / 8, kRopeRow);
+      lds_char* d1 = c0 < kDc / 8 ? tile + lds_off(tok, c0 + 1, kLatRow)
+                                  : tile + kRopeBase + lds_off(tok, c0 + 1 - kDc / 8, kRopeRow);
+      *(lds_u32x4*)d0 = u32x4{o[0], o[1], o[2], o[3]};
+      *(lds_u32x4*)d1 = u32x4{o[4], o[5], o[6], o[7]};
+      continue;
+    }
     const u32x4 v = *(const lds_u32x4*)(src + 16 * c);
     const float scale = e8m0_to_f32((uint32_t)(uint8_t)src[kVals + (c >> 1)]);
     // e4m3 * 2^(E-127) is exact in bf16, so the bf16 value is the upper half
@@ -124,8 +160,10 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
 // the PV column blocks [w*kDb/NW, (w+1)*kDb/NW) for all RB row blocks.  P
 // goes from the row owners to all waves through LDS, so each transposed V
 // read feeds RB MFMAs and every V column block is read once per tile.
-template <int NW, int RB>
+template <int FMT, int NW, int RB>
 __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
+  constexpr int kRawBuf = RawRow<FMT>::kRawBuf;
+  using Raw = RawStaging<FMT, NW>;
   static_assert(RB >= 1 && RB <= NW, "row blocks are owned by distinct waves");
   constexpr int kCols = (kDb + NW - 1) / NW;  // most column blocks a wave owns
   __shared__ __attribute__((aligned(16))) char tile_mem[kTileBytes];
@@ -194,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
       lds_barrier();  // the previous unit's readers of the tile, ring and P are done
 #pragma unroll
       for (int x = 0; x < D; ++x)
-        if (x < ntiles) RawStaging<NW>::load(tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), raws + (x % kRaw) * kRawBuf);
+        if (x < ntiles) Raw::load(tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), raws + (x % kRaw) * kRawBuf);
       if (D < ntiles) pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
     }
 
@@ -204,17 +242,17 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
     // tile it-1.
     auto step = [&](int it) __attribute__((always_inline)) {
       const int younger = min(D - 1, ntiles - 1 - it);
-      constexpr int M = RawStaging<NW>::kMinOps;
+      constexpr int M = Raw::kMinOps;
       if (younger >= 2) wait_vmcnt_lgkm0<2 * M>();
       else if (younger == 1) wait_vmcnt_lgkm0<M>();
       else wait_vmcnt_lgkm0<0>();
       lds_barrier();  // tile `it` landed; everyone finished tile it-1
       const int x = it + D;
       if (x < ntiles) {
-        RawStaging<NW>::load(tile_src(a, pages_next, t1), raws + (x % kRaw) * kRawBuf);
+        Raw::load(tile_src(a, pages_next, t1), raws + (x % kRaw) * kRawBuf);
         if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
       }
-      decode_tile<NW>(raws + (it % kRaw) * kRawBuf, tile);
+      decode_tile<FMT, NW>(raws + (it % kRaw) * kRawBuf, tile);
       wait_lgkm0();
       lds_barrier();  // the bf16 tile is complete
     };
@@ -428,19 +466,28 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 // eight waves, two per SIMD, of which the first RB own row blocks; all eight
 // split the PV columns, which keeps the SIMDs' matrix work close to even.
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32) {
-  return fmt == kFP8 && dc == kDc && dr == kDr && !q_f32 && R >= 1 && R <= 128;
+  return (fmt == kFP8 || fmt == kFP4) && dc == kDc && dr == kDr && !q_f32 && R >= 1 && R <= 128;
 }
 
-hipError_t launch_decode_fp8_rows(const DecodeArgs& a, hipStream_t s) {
+template <int FMT>
+hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
   const unsigned units = a.num_splits > 0 ? (unsigned)(a.B * a.num_splits) : (unsigned)a.workers;
   switch ((a.R + 15) / 16) {
 #define MLA_CASE(N) \
-  case N: decode_fp8_kernel<(N < 2 ? 2 : N <= 4 ? N : 8), N><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); break;
+  case N:           \
+    decode_fp8_kernel<FMT, (N < 2 ? 2 : N <= 4 ? N : 8), N><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); \
+    break;
     MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
 #undef MLA_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8_rows(const DecodeArgs& a, int fmt, hipStream_t s) {
+  if (fmt == kFP4) return launch_rows<kFP4>(a, s);
+  if (fmt == kFP8) return launch_rows<kFP8>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mla

@@ -126,7 +126,6 @@ struct DmaStaging {
   }
 
   __device__ __forceinline__ void load(const TileSrc& ts, lds_char* buf) const {
-    const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     if (ts.n == kTile && ts.kb >= kTile) {  // whole tile, one page: rows are consecutive
 #pragma unroll
@@ -813,7 +812,7 @@ hipError_t launch_decode_mfma_sparse(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s) {
-  if (decode_fp8_rows_supported(fmt, a.dc, a.dr, a.R, a.q_f32)) return launch_decode_fp8_rows(a, s);
+  if (decode_fp8_rows_supported(fmt, a.dc, a.dr, a.R, a.q_f32)) return launch_decode_fp8_rows(a, fmt, s);
   const int nw = waves_for(a.R);
   if (nw > (a.q_f32 ? 4 : 8)) return hipErrorInvalidValue;
   if (fmt == kBF16) return a.q_f32 ? launch_nw<kBF16, true>(a, nw, s) : launch_nw<kBF16, false>(a, nw, s);
