@@ -110,18 +110,25 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
     const int tok = u >> 5, c = u & 31;
     const lds_char* src = raw + tok * kRowBytes;
     if constexpr (FMT == kFP4) {
-      // 16 e2m1 codes (8 bytes) and their e4m3 scale: an e2m1 value times an
-      // e4m3 scale has at most 5 significant bits, so the bf16 value is the
-      // upper half of the exact fp32 product.
+      // 16 e2m1 codes (8 bytes) and their e4m3 scale.  The hardware converts
+      // a byte's two codes (low nibble first) with a unit scale; an e2m1 value
+      // times an e4m3 scale has at most 6 significant bits, so the bf16 value
+      // is the upper half of the exact fp32 product.
       const u32x2 v = *(const lds_u32x2*)(src + 8 * c);
       const float scale = e4m3fn_to_f32((uint32_t)(uint8_t)src[kVals / 2 + c]);
+      const f32x2 p[8] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[0], 1.0f, 0),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[0], 1.0f, 1),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[0], 1.0f, 2),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[0], 1.0f, 3),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[1], 1.0f, 0),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[1], 1.0f, 1),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[1], 1.0f, 2),
+                          __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v[1], 1.0f, 3)};
       uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t byte = (v[i >> 2] >> (8 * (i & 3))) & 0xffu;
-        o[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, e2m1_to_f32(byte >> 4) * scale),
-                                     __builtin_bit_cast(uint32_t, e2m1_to_f32(byte & 0xfu) * scale), 0x07060302u);
-      }
+      for (int i = 0; i < 8; ++i)
+        o[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, p[i][1] * scale),
+                                     __builtin_bit_cast(uint32_t, p[i][0] * scale), 0x07060302u);
       const int c0 = 2 * c;
       lds_char* d0 = c0 < kDc / 8 ? tile + lds_off(tok, c0, kLatRow)
                                   : tile + kRopeBase + lds_off(tok, c0 - kDc / 8, kRopeRow);
