@@ -75,13 +75,28 @@ def cpu_baseline(wl, target_s: float):
 COUNTER_SOURCES = ["decode_mfma.hip", "decode_fp8.hip", "decode_common.h", "schedule.h", "internal.h", "device_common.h"]
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the attention kernel's sources (counters go stale when it changes)."""
+def code_without_comments(text: str) -> str:
+    """C++ source with its comments, trailing blanks and blank lines removed
+    (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
+def kernel_source_digest(read=None) -> str:
+    """sha256 over the attention kernel's sources, comments left out (counters
+    go stale when the code changes, not when a comment does).  `read(name)`
+    returns a source's text; by default the file in csrc/."""
     import hashlib
+    if read is None:
+        def read(f):
+            with open(os.path.join(ROOT, "mla_paged_decode_amd", "csrc", f), encoding="utf-8") as fh:
+                return fh.read()
     h = hashlib.sha256()
     for f in COUNTER_SOURCES:
-        with open(os.path.join(ROOT, "mla_paged_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_without_comments(read(f)).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

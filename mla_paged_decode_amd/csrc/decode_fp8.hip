@@ -1,15 +1,18 @@
-// Split-KV paged MLA decode for the fp8 cache on the matrix cores (gfx950),
-// for up to 128 query rows per sequence (several query tokens per sequence,
-// as in a multi-token-prediction verify step).
+// Split-KV paged MLA decode for the quantised caches on the matrix cores
+// (gfx950), for up to 128 query rows per sequence (several query tokens per
+// sequence, as in a multi-token-prediction verify step).
 //
-// The cached row is 528 B: 512 e4m3 values (448 latent, then 64 RoPE) and 16
+// The fp8 row is 528 B: 512 e4m3 values (448 latent, then 64 RoPE) and 16
 // e8m0 scales, one per 32 values (the GLM-4.7-Flash model record, ENGINE
-// KERNEL CONSTRAINTS item (2)).  Per tile of 32 tokens:
-//   1. the raw rows (one contiguous 16.5 KB block when the tile lies in one
-//      page) go from HBM to an LDS ring with direct-to-LDS loads, kRaw - 1
-//      tiles ahead of the one being computed;
-//   2. all waves decode the raw tile into a bf16 tile, value * 2^(E-127),
-//      which is exact (3 mantissa bits fit bf16's 7, the exponents fit);
+// KERNEL CONSTRAINTS item (2)).  The fp4 row is 288 B (the same record's
+// fp4 variant): 512 e2m1 codes and 32 e4m3 scales, one per 16 values.  Per
+// tile of 32 tokens:
+//   1. the raw rows (one contiguous block when the tile lies in one page) go
+//      from HBM to an LDS ring with direct-to-LDS loads, kRaw - 1 tiles
+//      ahead of the one being computed;
+//   2. all waves decode the raw tile into a bf16 tile, which is exact: an
+//      e4m3 value times 2^(E-127) has 4 significant bits, an e2m1 value
+//      times an e4m3 scale at most 6, and bf16 holds 8;
 //   3. QK^T and PV run on v_mfma_f32_16x16x32_bf16 with the operand layouts
 //      and swizzled bf16 tile of the bf16 kernel.  QK^T and the softmax are
 //      split by 16-row blocks (one per wave); PV is split by column blocks,
