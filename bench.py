@@ -166,6 +166,19 @@ def cache_write_timing(inp, dev, reps: int):
     return {"rows": n, "us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
 
 
+def sparse_on_matrix_cores(wl, q_abs_dtype, topk_width: int) -> bool:
+    """The library's sparse kernel choice: matrix cores for whole 32-slot
+    tiles with a bf16 cache (up to 64 heads), or an fp8 / fp4 cache of the
+    448 + 64 row with bf16 queries (up to 128 heads)."""
+    import mla_paged_decode_amd as mla
+    if topk_width % 32:
+        return False
+    if wl.kv_format == "bf16":
+        return wl.d_latent == 512 and wl.heads <= 64
+    return (wl.kv_format in ("fp8_e4m3_e8m0", "fp4_e2m1_e4m3") and wl.d_latent == 448
+            and q_abs_dtype == mla.MLA_BF16 and wl.heads <= 128)
+
+
 def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int, reps: int):
     """mla_decode_sparse_paged over topk_width listed tokens per query (a
     seeded random half of the visible positions, -1 padded): the attention
@@ -213,8 +226,7 @@ def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int
     us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
     row_bytes = inp.row_bytes
     return {"topk_width": topk_width, "listed_tokens": listed, "num_splits": num_splits,
-            "kernel": {1: "simt", 2: "mfma"}[2 if (wl.kv_format == "bf16" and topk_width % 32 == 0
-                                                  and wl.heads <= 64) else 1],
+            "kernel": "mfma" if sparse_on_matrix_cores(wl, q_abs_dtype, topk_width) else "simt",
             "attention_kernel_us": us, "bytes": listed * row_bytes,
             "gbs": listed * row_bytes / (us * 1e-6) / 1e9}
 

@@ -133,6 +133,20 @@ WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
 
 namespace {
 
+// Sparse matrix-core kernels: the bf16 one (rows straight to LDS) and the
+// quantised-row one (fp8 / fp4 rows decoded to bf16 in LDS).
+bool sparse_bf16_mfma(const mla_decode_params_t* p, int32_t topk_width) {
+  return mla::decode_mfma_sparse_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope, p->dims.num_heads,
+                                           topk_width);
+}
+bool sparse_rows_mfma(const mla_decode_params_t* p, int32_t topk_width) {
+  return mla::decode_fp8_rows_sparse_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope, p->dims.num_heads,
+                                               p->q_abs_dtype == MLA_F32, topk_width);
+}
+bool sparse_mfma_ok(const mla_decode_params_t* p, int32_t topk_width) {
+  return sparse_bf16_mfma(p, topk_width) || sparse_rows_mfma(p, topk_width);
+}
+
 mla_status_t check_sparse(const mla_decode_params_t* p, int32_t topk_width) {
   mla_status_t st = check_decode_scalars(p);
   if (st) return st;
@@ -142,13 +156,12 @@ mla_status_t check_sparse(const mla_decode_params_t* p, int32_t topk_width) {
     return fail(MLA_ERR_UNSUPPORTED,
                 "num_splits: expected >= 1 (uniform chunks of each index list) for the sparse call, got %d",
                 p->num_splits);
-  if (p->kernel == MLA_KERNEL_MFMA &&
-      !mla::decode_mfma_sparse_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope, p->dims.num_heads,
-                                         topk_width))
+  if (p->kernel == MLA_KERNEL_MFMA && !sparse_mfma_ok(p, topk_width))
     return fail(MLA_ERR_UNSUPPORTED,
-                "kernel: the sparse matrix-core kernel needs a bf16 cache, num_heads <= 64 and topk_width a multiple "
-                "of 32 (got kv_format %d, num_heads %d, topk_width %d)",
-                (int)p->kv_format, p->dims.num_heads, topk_width);
+                "kernel: the sparse matrix-core kernels need topk_width a multiple of 32 and either a bf16 cache "
+                "with num_heads <= 64, or an fp8 / fp4 cache with bf16 q_abs and num_heads <= 128 (got kv_format "
+                "%d, q_abs_dtype %d, num_heads %d, topk_width %d)",
+                (int)p->kv_format, (int)p->q_abs_dtype, p->dims.num_heads, topk_width);
   if ((int64_t)p->batch * p->q_per_seq * p->num_splits > 0x7fffffffLL)
     return fail(MLA_ERR_INVALID_SHAPE, "batch * q_per_seq * num_splits: expected < 2^31, got %lld",
                 (long long)p->batch * p->q_per_seq * p->num_splits);
@@ -358,15 +371,17 @@ mla_status_t mla_decode_sparse_paged(const mla_decode_params_t* p, const int32_t
   a.topk = topk_indices;
   a.topk_width = topk_width;
   a.sparse_sq = Sq;
-  const bool use_mfma = p->kernel != MLA_KERNEL_SIMT &&
-                        mla::decode_mfma_sparse_supported(p->kv_format, dc, dr, H, topk_width);
+  const bool use_rows = p->kernel != MLA_KERNEL_SIMT && sparse_rows_mfma(p, topk_width);
+  const bool use_mfma = use_rows || (p->kernel != MLA_KERNEL_SIMT && sparse_bf16_mfma(p, topk_width));
   a.part_tiled = use_mfma ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
     return hip_fail("kernel_start_event record", e);
-  e = use_mfma ? mla::launch_decode_mfma_sparse(a, s) : mla::launch_decode_simt(a, p->kv_format, s);
+  e = use_rows   ? mla::launch_decode_fp8_rows_sparse(a, p->kv_format, s)
+      : use_mfma ? mla::launch_decode_mfma_sparse(a, s)
+                 : mla::launch_decode_simt(a, p->kv_format, s);
   if (e != hipSuccess) return hip_fail("sparse decode launch", e);
   if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
     return hip_fail("kernel_stop_event record", e);

@@ -99,6 +99,27 @@ struct RawStaging {
       }
     }
   }
+
+  // Gathered rows (sparse mode): lane j < 32 of a table register holds the
+  // physical row of slot j, and each lane fetches its chunk's row from that
+  // table with a cross-lane permute.
+  __device__ __forceinline__ static void load_gather(const Gather& gt, const uint8_t* pool, lds_char* buf) {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    int table = 0;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) table = lane == j ? (int)gt.phys[j] : table;
+#pragma unroll
+    for (int i = 0; i < (kRawInst + NW - 1) / NW; ++i) {
+      const int k = wave + NW * i;
+      if (NW * i + NW <= kRawInst || k < kRawInst) {
+        const int q = min(64 * k + lane, kRawChunks - 1);
+        const int row = q / RR::kChunksPerRow, c = q % RR::kChunksPerRow;
+        const uint32_t phys = (uint32_t)__builtin_amdgcn_ds_bpermute(row << 2, table);
+        dma16_vaddr(pool + (uint64_t)phys * kRowBytes + 16 * c, buf + 1024 * k);
+      }
+    }
+  }
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
@@ -106,12 +127,15 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // Decode a raw tile into the bf16 tile: unit u = (token u / 32, value chunk
 // u % 32 of 16 values), spread over all threads of the workgroup.
-template <int FMT, int NW>
-__device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile) {
+// In sparse mode a slot outside `vis` (padding) is written as zeros, so that
+// whatever its gathered row holds, its P = 0 weight multiplies a finite value.
+template <int FMT, int NW, bool SPARSE>
+__device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile, uint32_t vis) {
   constexpr int kRowBytes = RawRow<FMT>::kRowBytes;
   for (int u = threadIdx.x; u < kTile * 32; u += 64 * NW) {
     const int tok = u >> 5, c = u & 31;
     const lds_char* src = raw + tok * kRowBytes;
+    const bool zero = SPARSE && !((vis >> tok) & 1u);
     if constexpr (FMT == kFP4) {
       // 16 e2m1 codes (8 bytes) and their e4m3 scale.  The hardware converts
       // a byte's two codes (low nibble first) with a unit scale; an e2m1 value
@@ -130,8 +154,9 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
       uint32_t o[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        o[i] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, p[i][1] * scale),
-                                     __builtin_bit_cast(uint32_t, p[i][0] * scale), 0x07060302u);
+        o[i] = zero ? 0u
+                    : __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, p[i][1] * scale),
+                                            __builtin_bit_cast(uint32_t, p[i][0] * scale), 0x07060302u);
       const int c0 = 2 * c;
       lds_char* d0 = c0 < kDc / 8 ? tile + lds_off(tok, c0, kLatRow)
                                   : tile + kRopeBase + lds_off(tok, c0 - kDc / 8, kRopeRow);
@@ -150,10 +175,12 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
     for (int i = 0; i < 4; ++i) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], false);
       const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[i], true);
-      o[2 * i + 0] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[1] * scale),
-                                           __builtin_bit_cast(uint32_t, lo[0] * scale), 0x07060302u);
-      o[2 * i + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi[1] * scale),
-                                           __builtin_bit_cast(uint32_t, hi[0] * scale), 0x07060302u);
+      o[2 * i + 0] = zero ? 0u
+                          : __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[1] * scale),
+                                                  __builtin_bit_cast(uint32_t, lo[0] * scale), 0x07060302u);
+      o[2 * i + 1] = zero ? 0u
+                          : __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi[1] * scale),
+                                                  __builtin_bit_cast(uint32_t, hi[0] * scale), 0x07060302u);
     }
     const int c0 = 2 * c;  // first bf16 chunk of these 16 values
     lds_char* d0 = c0 < kDc / 8 ? tile + lds_off(tok, c0, kLatRow)
@@ -170,7 +197,12 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile)
 // the PV column blocks [w*kDb/NW, (w+1)*kDb/NW) for all RB row blocks.  P
 // goes from the row owners to all waves through LDS, so each transposed V
 // read feeds RB MFMAs and every V column block is read once per tile.
-template <int FMT, int NW, int RB>
+//
+// Sparse mode (SPARSE): a unit is one (sequence, query token) pair and its
+// tiles are 32 consecutive slots of that query's index list, gathered as in
+// the bf16 kernel's sparse mode; the slots' visibility masks ride with the
+// raw ring in LDS.
+template <int FMT, int NW, int RB, bool SPARSE = false>
 __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   constexpr int kRawBuf = RawRow<FMT>::kRawBuf;
   using Raw = RawStaging<FMT, NW>;
@@ -184,6 +216,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
   __shared__ int32_t s_first;
+  __shared__ uint32_t s_mask[kRaw];  // sparse: visible-slot mask per raw ring buffer
   lds_char* const tile = (lds_char*)tile_mem;
   lds_char* const raws = (lds_char*)raw_mem;
   lds_char* const pbuf = (lds_char*)p_mem;
@@ -214,7 +247,22 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
     const int b = uniform(unit.b), L = uniform(unit.L), t0 = uniform(unit.t0), t1 = uniform(unit.t1);
     const int64_t slot = unit.slot;
     const int ntiles = uniform((t1 - t0 + kTile - 1) / kTile);
-    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)b * a.max_blocks;
+    // Sparse: unit b is query token b % sparse_sq of sequence b / sparse_sq,
+    // which sees positions up to L - Sq + j of that sequence.
+    const int sb = SPARSE ? uniform(b / a.sparse_sq) : b;
+    const int sparse_limit =
+        SPARSE ? uniform(max(((const_i32_ptr)a.seq_lens)[sb], 0) - a.sparse_sq + b % a.sparse_sq) : 0;
+    const const_i32_ptr list = (const_i32_ptr)(a.topk) + (SPARSE ? (int64_t)b * a.topk_width : 0);
+    const const_i32_ptr bt = (const_i32_ptr)(a.block_table) + (int64_t)sb * a.max_blocks;
+    // Issue the raw rows of tile x (sparse: gathered, with its mask).
+    auto issue = [&](int x, const TilePages& tp, const Gather& gt) __attribute__((always_inline)) {
+      if constexpr (SPARSE) {
+        Raw::load_gather(gt, a.pool, raws + (x % kRaw) * kRawBuf);
+        if (threadIdx.x == 0) s_mask[x % kRaw] = gt.mask;
+      } else {
+        Raw::load(tile_src(a, tp, t1), raws + (x % kRaw) * kRawBuf);
+      }
+    };
 
     // ---- queries (bf16, B-operand layout) of the owned row block ----
     // Loaded and waited for before any tile transfer, so that later waits
@@ -238,12 +286,19 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
     float m = -INFINITY, lsum = 0.f;  // the owner's row statistics (base 2)
 
     TilePages pages_next;
+    Gather gnext;  // sparse: rows of the next tile to issue, looked up one tile early
     if (ntiles > 0) {
       lds_barrier();  // the previous unit's readers of the tile, ring and P are done
 #pragma unroll
       for (int x = 0; x < D; ++x)
-        if (x < ntiles) Raw::load(tile_src(a, tile_pages(a, bt, t0 + x * kTile, t1), t1), raws + (x % kRaw) * kRawBuf);
-      if (D < ntiles) pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
+        if (x < ntiles) {
+          if constexpr (SPARSE) issue(x, pages_next, gather_lookup(a, list, bt, t0 + x * kTile, t1, sparse_limit));
+          else issue(x, tile_pages(a, bt, t0 + x * kTile, t1), gnext);
+        }
+      if (D < ntiles) {
+        if constexpr (SPARSE) gnext = gather_lookup(a, list, bt, t0 + D * kTile, t1, sparse_limit);
+        else pages_next = tile_pages(a, bt, t0 + D * kTile, t1);
+      }
     }
 
     // One pipeline step: tile `it` has landed in the ring (everyone's part),
@@ -259,10 +314,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
       lds_barrier();  // tile `it` landed; everyone finished tile it-1
       const int x = it + D;
       if (x < ntiles) {
-        Raw::load(tile_src(a, pages_next, t1), raws + (x % kRaw) * kRawBuf);
-        if (x + 1 < ntiles) pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+        issue(x, pages_next, gnext);
+        if (x + 1 < ntiles) {
+          if constexpr (SPARSE) gnext = gather_lookup(a, list, bt, t0 + (x + 1) * kTile, t1, sparse_limit);
+          else pages_next = tile_pages(a, bt, t0 + (x + 1) * kTile, t1);
+        }
       }
-      decode_tile<FMT, NW>(raws + (it % kRaw) * kRawBuf, tile);
+      decode_tile<FMT, NW, SPARSE>(raws + (it % kRaw) * kRawBuf, tile, SPARSE ? s_mask[it % kRaw] : ~0u);
       wait_lgkm0();
       lds_barrier();  // the bf16 tile is complete
     };
@@ -319,13 +377,15 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 
         // ---- online softmax of the owned rows ----
         const int last_visible = L - a.Sq + (row_ok ? row / a.H : 0);
+        const uint32_t vis = SPARSE ? s_mask[it % kRaw] : ~0u;
         float sv[2][4], mx = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = tt0 + tb * 16 + 4 * g + i;
-            const bool ok = row_ok && t < t1 && t <= last_visible;
+            const bool ok = SPARSE ? row_ok && ((vis >> (tb * 16 + 4 * g + i)) & 1u)
+                                   : row_ok && t < t1 && t <= last_visible;
             sv[tb][i] = ok ? s[tb][i] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[tb][i]);
           }
@@ -497,6 +557,34 @@ hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_fp8_rows(const DecodeArgs& a, int fmt, hipStream_t s) {
   if (fmt == kFP4) return launch_rows<kFP4>(a, s);
   if (fmt == kFP8) return launch_rows<kFP8>(a, s);
+  return hipErrorInvalidValue;
+}
+
+// Sparse mode: each index list is read in whole 32-slot tiles.
+bool decode_fp8_rows_sparse_supported(int fmt, int dc, int dr, int R, int q_f32, int topk_width) {
+  return decode_fp8_rows_supported(fmt, dc, dr, R, q_f32) && topk_width % kTile == 0;
+}
+
+template <int FMT>
+hipError_t launch_rows_sparse(const DecodeArgs& a, hipStream_t s) {
+  const unsigned units = (unsigned)(a.B * a.num_splits);
+  switch ((a.R + 15) / 16) {
+#define MLA_CASE(N) \
+  case N:           \
+    decode_fp8_kernel<FMT, (N < 2 ? 2 : N <= 4 ? N : 8), N, true><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); \
+    break;
+    MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
+#undef MLA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp8_rows_sparse(const DecodeArgs& a, int fmt, hipStream_t s) {
+  if (a.num_splits < 1 || !decode_fp8_rows_sparse_supported(fmt, a.dc, a.dr, a.R, a.q_f32, a.topk_width))
+    return hipErrorInvalidValue;
+  if (fmt == kFP4) return launch_rows_sparse<kFP4>(a, s);
+  if (fmt == kFP8) return launch_rows_sparse<kFP8>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -64,38 +64,6 @@ struct Geo {
   static constexpr int kSrcChunks = kVals / 16;             // stored fp8 16-value chunks per row
 };
 
-// Sparse top-k mode: a tile is 32 consecutive slots of a query's index list;
-// slot k names the cached token list[tt0 + k].  Its physical rows are looked
-// up one tile ahead with scalar loads (counted by lgkmcnt, so the tile
-// transfers' vmcnt accounting is untouched).  Slots that are padding (< 0,
-// past the causal limit, or past the unit's end) read row 0 of the pool,
-// always in bounds, and are cleared in `mask`.
-struct Gather {
-  uint32_t phys[kTile];  // physical row (page * P + offset) per slot
-  uint32_t mask;         // bit k: slot k names a visible token
-};
-
-__device__ __forceinline__ Gather gather_lookup(const DecodeArgs& a, const_i32_ptr list, const_i32_ptr bt, int tt0,
-                                                int t1, int limit) {
-  Gather g;
-  int32_t p[kTile];
-#pragma unroll
-  for (int k = 0; k < kTile; ++k) p[k] = list[tt0 + k];  // in bounds: the list width is a multiple of 32
-  g.mask = 0;
-#pragma unroll
-  for (int k = 0; k < kTile; ++k) {
-    const bool ok = tt0 + k < t1 && p[k] >= 0 && p[k] <= limit;
-    g.mask |= (uint32_t)ok << k;
-    p[k] = ok ? p[k] : 0;
-  }
-#pragma unroll
-  for (int k = 0; k < kTile; ++k) {
-    const int32_t pg = bt[p[k] >> a.P_log2];
-    g.phys[k] = (g.mask >> k) & 1 ? (uint32_t)(pg * a.P + (p[k] & (a.P - 1))) : 0u;
-  }
-  return g;
-}
-
 // bf16 tiles go straight from HBM to LDS.  A wave instruction fills 64
 // consecutive 16-B LDS chunks: one token's latent row (lane = swizzled
 // chunk, 1 KB contiguous in HBM), or the RoPE parts of 8 tokens.  Latent rows

@@ -76,10 +76,14 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s);
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
-// fp8 cache with bf16 queries: one 16-row block per wave (decode_fp8.hip);
-// launch_decode_mfma dispatches to it when it applies.
+// fp8 or fp4 cache with bf16 queries: one 16-row block per wave
+// (decode_fp8.hip); launch_decode_mfma dispatches to it when it applies.
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32);
 hipError_t launch_decode_fp8_rows(const DecodeArgs& a, int fmt, hipStream_t s);
+// The same kernel in sparse top-k mode: uniform splits, index lists a
+// multiple of 32 wide.
+bool decode_fp8_rows_sparse_supported(int fmt, int dc, int dr, int R, int q_f32, int topk_width);
+hipError_t launch_decode_fp8_rows_sparse(const DecodeArgs& a, int fmt, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Sparse top-k mode on the matrix cores: bf16 cache, R <= 64, uniform splits,
 // index lists a multiple of 32 wide (tiles never pass the end of a list).

@@ -2,8 +2,10 @@
 
 The whole step runs on the GPU (absorb -> sparse decode -> out_proj) and is
 compared element by element with the unabsorbed oracle over the listed
-tokens.  The sparse call runs on the fp32 vector-ALU kernel, so the bar is
-1e-4 of the output RMS, as for the other fp32 path.
+tokens.  On the fp32 vector-ALU kernel the bar is 1e-4 of the output RMS, as
+for the other fp32 path; the matrix-core kernels take the bars of their dense
+counterparts (1e-2 for the bf16 cache, 5e-2 for the fp8 and fp4 caches with
+bf16 queries).
 """
 import math
 
@@ -136,6 +138,40 @@ def test_sparse_fp8_mtp_masks_past_the_causal_limit(q_bf16):
         check(got, glse, ref, rlse, tau=5e-2, lse_tol=1e-2)
     else:
         check(got, glse, ref, rlse)
+
+
+@pytest.mark.parametrize("heads,sq,width,splits", [(20, 4, 256, 2), (40, 1, 96, 1), (100, 1, 128, 3), (16, 8, 64, 1)])
+def test_sparse_fp8_rows_on_the_matrix_cores(heads, sq, width, splits):
+    """fp8 cache, bf16 absorbed queries: rows gathered through the index
+    list into the raw ring and decoded to bf16 in LDS (2, 3 and 7 row
+    blocks; lists with padding, entries past the causal limit, an empty
+    sequence and an all-padding list).  Held to the fp8 bar, 5e-2 of the
+    output RMS."""
+    inp = make_inputs(WORKLOADS["fp8_mtp4_b64_h20_ctx16k"].with_(batch=4, heads=heads, q_per_seq=sq,
+                                                                 lens=("fixed", (130, 0, 301, 64))))
+    topk = make_lists(inp, 0.4, width, seed=heads + width, beyond=3)
+    topk[3, 0] = -1
+    got, glse = run_step(inp, topk, splits, q_bf16=True, kernel=MFMA)
+    ref, rlse = oracle.mla_decode_sparse(inp, topk)
+    assert np.all(ref[sq:2 * sq] == 0) and np.all(np.isneginf(rlse[sq:2 * sq]))
+    check(got, glse, ref, rlse, tau=5e-2, lse_tol=1e-2)
+
+
+def test_sparse_fp4_rows_on_the_matrix_cores():
+    """The same gathered path over the 288-byte fp4 row (a pool the oracle's
+    encoder wrote)."""
+    from synth.gen import Inputs
+    base = make_inputs(WORKLOADS["fp8_mtp4_b64_h20_ctx16k"].with_(batch=3, q_per_seq=2, kv_format="f32",
+                                                                  lens=("fixed", (200, 45, 530))))
+    vals = oracle.decode_rows(base.kv_pool, "f32", base.wl.d_latent, base.wl.d_rope)
+    pool = np.stack([oracle.encode_row(v, "fp4_e2m1_e4m3") for v in vals.reshape(-1, vals.shape[-1])])
+    pool = pool.reshape(base.kv_pool.shape[0], base.kv_pool.shape[1], 288)
+    inp = Inputs(wl=base.wl.with_(kv_format="fp4_e2m1_e4m3"), q=base.q, w_kv_b=base.w_kv_b, kv_pool=pool,
+                 block_table=base.block_table, seq_lens=base.seq_lens)
+    topk = make_lists(inp, 0.5, 160, seed=31, beyond=2)
+    got, glse = run_step(inp, topk, 2, q_bf16=True, kernel=MFMA)
+    ref, rlse = oracle.mla_decode_sparse(inp, topk)
+    check(got, glse, ref, rlse, tau=5e-2, lse_tol=1e-2)
 
 
 def test_sparse_empty_lists_and_empty_sequence():
