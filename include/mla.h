@@ -195,12 +195,14 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
  * Every other parameter means what it means for mla_decode_paged, except:
  * num_splits >= 1 cuts each index list into that many uniform chunks (0 is
  * rejected), and the workspace size comes from
- * mla_decode_sparse_workspace_size.  Kernel: the matrix-core one (rows
- * gathered through the index list) for a bf16 cache with num_heads <= 64 and
- * topk_width a multiple of 32 (the pages pad the list to 128), unless
- * MLA_KERNEL_SIMT is asked for; the fp32 vector-ALU one otherwise
- * (MLA_KERNEL_MFMA where it does not apply is rejected).  Errors: see the
- * conventions above. */
+ * mla_decode_sparse_workspace_size.  Kernel: a matrix-core one (rows
+ * gathered through the index list) when topk_width is a multiple of 32 (the
+ * pages pad the list to 128) and either the cache is bf16 with num_heads <=
+ * 64, or it is fp8 / fp4 (448 + 64 row) with bf16 q_abs and num_heads <= 128
+ * (padding slots then contribute exact zeros, whatever the row they are
+ * pointed at holds); unless MLA_KERNEL_SIMT is asked for.  The fp32
+ * vector-ALU one otherwise (MLA_KERNEL_MFMA where none applies is
+ * rejected).  Errors: see the conventions above. */
 mla_status_t mla_decode_sparse_workspace_size(const mla_decode_params_t* p, int32_t topk_width, size_t* bytes);
 mla_status_t mla_decode_sparse_paged(const mla_decode_params_t* p, const int32_t* topk_indices,
                                      int32_t topk_width, void* stream);
