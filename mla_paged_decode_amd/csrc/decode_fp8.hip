@@ -17,8 +17,9 @@
 //      and swizzled bf16 tile of the bf16 kernel.  QK^T and the softmax are
 //      split by 16-row blocks (one per wave); PV is split by column blocks,
 //      each wave covering all rows, with P handed over through LDS.
-// One workgroup of ceil(R / 16) waves (at least 2) runs per CU: 256 balanced
-// workers.  The per-tile cost is bound by LDS instructions (about 8 cycles
+// One workgroup of ceil(R / 16) waves (at least 2) runs per CU, 256 balanced
+// workers; with at most two row blocks two run per CU (512 workers, a
+// shallower ring).  The per-tile cost is bound by LDS instructions (about 8 cycles
 // per wave instruction), which the column split keeps to one transposed
 // read per V chunk per tile.
 //
@@ -55,7 +56,11 @@ struct RawRow {
   static constexpr int kRawInst = (kRawChunks + 63) / 64;   // 17 / 9 wave loads per tile
   static constexpr int kRawBuf = kRawInst * 1024;           // raw buffer stride
 };
-constexpr int kRaw = 4;                                      // raw ring depth
+// Raw ring depth: 4 buffers (3 tiles in flight) for one workgroup per CU;
+// with at most two row blocks (two waves) two workgroups share a CU, each
+// with 2 buffers (1 tile in flight), so that all four SIMDs have a wave.
+template <int RB>
+constexpr int raw_depth() { return RB <= 2 ? 2 : 4; }
 // Converted bf16 tile, as in the bf16 kernel: latent rows (56 chunks) then
 // the RoPE rows (8 chunks), chunks XOR-swizzled by token.
 constexpr int kLatRow = kDc * 2;                   // 896
@@ -205,6 +210,7 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile,
 template <int FMT, int NW, int RB, bool SPARSE = false>
 __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
   constexpr int kRawBuf = RawRow<FMT>::kRawBuf;
+  constexpr int kRaw = raw_depth<RB>();
   using Raw = RawStaging<FMT, NW>;
   static_assert(RB >= 1 && RB <= NW, "row blocks are owned by distinct waves");
   constexpr int kCols = (kDb + NW - 1) / NW;  // most column blocks a wave owns
@@ -535,6 +541,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 // least two), each with a whole SIMD's registers.  Five to eight row blocks:
 // eight waves, two per SIMD, of which the first RB own row blocks; all eight
 // split the PV columns, which keeps the SIMDs' matrix work close to even.
+// Two workgroups per CU where the ring is 2 deep (at most two row blocks).
+int fp8_rows_workers(int R) { return (R + 15) / 16 <= 2 ? 512 : 256; }
+
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32) {
   return (fmt == kFP8 || fmt == kFP4) && dc == kDc && dr == kDr && !q_f32 && R >= 1 && R <= 128;
 }
