@@ -249,6 +249,51 @@ mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows,
                              void* kv_pool, mla_kv_format_t kv_format,
                              int64_t num_pages, int32_t page_block, void* stream);
 
+/* Unabsorbed prefill (chunked prefill): a chunk of Sq new tokens per
+ * sequence, already appended as the last Sq of its L cached tokens, attends
+ * causally to the whole cache with per-head keys and values rebuilt through
+ * kv_b_proj (DeepSeek-V2 multi-head latent attention in its unabsorbed
+ * form, as the GLM-4.7-Flash model record uses it; the pages name chunked
+ * prefill for MLA beside the decode kernel).  For sequence b, query i in
+ * [0, Sq) (position L - Sq + i) and head h, over tokens t <= L - Sq + i:
+ *   k_t = [W_UK[h] c_t ; k^R_t],  v_t = W_UV[h] c_t   (W_UK = rows [0, d_nope)
+ *                                  and W_UV = rows [d_nope, d_nope + d_v) of
+ *                                  w_kv_b[h])
+ *   s_t = softmax_scale * q[b][i][h] . k_t,   out = sum_t softmax(s)_t v_t,
+ *   lse = log sum_t exp(s_t); no visible token: out = 0, lse = -inf.
+ * Computed in fp32 on the vector ALUs: the keys and values of every token
+ * slot a sequence can hold (max_blocks_per_seq * page_block) are rebuilt
+ * into the workspace, then each (query, head) runs online softmax over them. */
+typedef struct {
+  mla_dims_t dims;      /* d_nope + d_rope <= 256, d_v <= 256 */
+  int32_t batch;        /* B >= 0 */
+  int32_t q_per_seq;    /* Sq >= 1 new tokens per sequence */
+  const void* q;        /* [B][Sq][H][d_nope + d_rope], q_dtype, 16-B aligned */
+  mla_dtype_t q_dtype;  /* F32 or BF16 */
+  const void* w_kv_b;   /* [H][d_nope + d_v][d_latent], w_dtype, 16-B aligned */
+  mla_dtype_t w_dtype;  /* F32 or BF16 */
+  const void* kv_pool;  /* [num_pages][page_block][row_bytes], any kv_format */
+  mla_kv_format_t kv_format;
+  int64_t num_pages;
+  int32_t page_block;          /* 16, 32, 64 or 128 */
+  const int32_t* block_table;  /* [B][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;  /* max_blocks_per_seq * page_block <= 2^24 */
+  const int32_t* seq_lens;     /* [B] cached tokens, the chunk included */
+  float softmax_scale;
+  void* workspace;             /* mla_prefill_workspace_size() bytes, 16-B aligned,
+                                  no initialisation needed */
+  size_t workspace_bytes;
+  float* out;                  /* out: [B][Sq][H][d_v], F32 */
+  float* lse;                  /* out (optional, may be NULL): [B][Sq][H] */
+} mla_prefill_params_t;
+
+/* Workspace bytes of mla_prefill_paged: 4 * B * max_blocks_per_seq *
+ * page_block * (H * (d_nope + d_v) + d_rope), each part rounded up to 256.
+ * Host scalars only. */
+mla_status_t mla_prefill_workspace_size(const mla_prefill_params_t* p, size_t* bytes);
+/* Errors: see the conventions above; every check runs before any launch. */
+mla_status_t mla_prefill_paged(const mla_prefill_params_t* p, void* stream);
+
 const char* mla_status_string(mla_status_t status);
 /* Message of the last failed call on this thread ("" if none). */
 const char* mla_last_error_message(void);

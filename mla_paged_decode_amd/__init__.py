@@ -79,6 +79,30 @@ class DecodeParams(ctypes.Structure):
     ]
 
 
+class PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("dims", Dims),
+        ("batch", ctypes.c_int32),
+        ("q_per_seq", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("q_dtype", ctypes.c_int),
+        ("w_kv_b", ctypes.c_void_p),
+        ("w_dtype", ctypes.c_int),
+        ("kv_pool", ctypes.c_void_p),
+        ("kv_format", ctypes.c_int),
+        ("num_pages", ctypes.c_int64),
+        ("page_block", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("out", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
 # Must equal MLA_ABI_VERSION of include/mla.h (the parameter struct layout).
 ABI_VERSION = 2
 
@@ -112,6 +136,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_sparse_paged.restype = st
         L.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeParams), vp]
         L.mla_decode_paged.restype = st
+        L.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams), ctypes.POINTER(ctypes.c_size_t)]
+        L.mla_prefill_workspace_size.restype = st
+        L.mla_prefill_paged.argtypes = [ctypes.POINTER(PrefillParams), vp]
+        L.mla_prefill_paged.restype = st
         L.mla_status_string.argtypes = [st]
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_error_message.argtypes = []
@@ -238,3 +266,27 @@ def mla_decode_sparse_workspace_size(params: DecodeParams, topk_width: int) -> i
 def mla_decode_sparse_paged(params: DecodeParams, topk_indices, topk_width: int, stream=None) -> None:
     """Decode over the cached tokens named by topk_indices [B][Sq][topk_width] int32."""
     _check(lib().mla_decode_sparse_paged(ctypes.byref(params), _ptr(topk_indices), topk_width, _stream(stream)))
+
+
+def make_prefill_params(*, dims, batch, q_per_seq, q, w_kv_b, kv_pool, kv_format, num_pages, page_block,
+                        block_table, max_blocks_per_seq, seq_lens, softmax_scale, out, lse=None,
+                        workspace=None, workspace_bytes=0, q_dtype=None, w_dtype=None) -> PrefillParams:
+    """Fill the C prefill parameter struct (pointers from tensors or raw ints)."""
+    return PrefillParams(
+        dims=_dims(dims), batch=batch, q_per_seq=q_per_seq,
+        q=_ptr(q), q_dtype=_dtype_code(q, q_dtype), w_kv_b=_ptr(w_kv_b), w_dtype=_dtype_code(w_kv_b, w_dtype),
+        kv_pool=_ptr(kv_pool), kv_format=kv_format, num_pages=num_pages, page_block=page_block,
+        block_table=_ptr(block_table), max_blocks_per_seq=max_blocks_per_seq, seq_lens=_ptr(seq_lens),
+        softmax_scale=softmax_scale, workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
+        out=_ptr(out), lse=_ptr(lse))
+
+
+def mla_prefill_workspace_size(params: PrefillParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().mla_prefill_workspace_size(ctypes.byref(params), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_prefill_paged(params: PrefillParams, stream=None) -> None:
+    """Unabsorbed causal prefill of the last q_per_seq cached tokens of every sequence."""
+    _check(lib().mla_prefill_paged(ctypes.byref(params), _stream(stream)))

@@ -30,6 +30,7 @@ SOURCES = [
     "proj_simt.hip",
     "proj_mfma.hip",
     "cache_write.hip",
+    "prefill_simt.hip",
 ]
 
 FLAGS = [

@@ -168,6 +168,52 @@ mla_status_t check_sparse(const mla_decode_params_t* p, int32_t topk_width) {
   return MLA_OK;
 }
 
+mla_status_t check_prefill(const mla_prefill_params_t* p) {
+  if (!p) return fail(MLA_ERR_NULL_POINTER, "params: expected non-null, got NULL");
+  if (!valid_format(p->kv_format))
+    return fail(MLA_ERR_UNSUPPORTED, "kv_format: expected 0 (f32), 1 (bf16), 2 (fp8 e4m3+e8m0) or 3 (fp4 e2m1+e4m3), got %d",
+                (int)p->kv_format);
+  mla_status_t st = check_dims(&p->dims, latent_for_format(p->kv_format));
+  if (st) return st;
+  if (!mla::prefill_supported(p->dims.d_latent, p->dims.d_rope, p->dims.d_nope, p->dims.d_v))
+    return fail(MLA_ERR_UNSUPPORTED, "dims: the prefill needs d_nope + d_rope <= 256 and d_v <= 256, got %d + %d and %d",
+                p->dims.d_nope, p->dims.d_rope, p->dims.d_v);
+  if (p->batch < 0) return fail(MLA_ERR_INVALID_SHAPE, "batch: expected >= 0, got %d", p->batch);
+  if (p->q_per_seq < 1) return fail(MLA_ERR_INVALID_SHAPE, "q_per_seq: expected >= 1, got %d", p->q_per_seq);
+  if ((int64_t)p->batch * p->q_per_seq > 0x7fffffffLL)
+    return fail(MLA_ERR_INVALID_SHAPE, "batch * q_per_seq: expected < 2^31, got %lld",
+                (long long)p->batch * p->q_per_seq);
+  const int P = p->page_block;
+  if (P != 16 && P != 32 && P != 64 && P != 128)
+    return fail(MLA_ERR_UNSUPPORTED, "page_block: expected one of {16,32,64,128}, got %d", P);
+  if (p->num_pages < 1)
+    return fail(MLA_ERR_INVALID_SHAPE, "num_pages: expected >= 1, got %lld", (long long)p->num_pages);
+  if (p->max_blocks_per_seq < 1 || (int64_t)p->max_blocks_per_seq * P > (1 << 24))
+    return fail(MLA_ERR_INVALID_SHAPE, "max_blocks_per_seq: expected 1..%d for page_block %d, got %d", (1 << 24) / P, P,
+                p->max_blocks_per_seq);
+  if (!valid_dtype(p->q_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "q_dtype: expected 0 (f32) or 1 (bf16), got %d", (int)p->q_dtype);
+  if (!valid_dtype(p->w_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "w_dtype: expected 0 (f32) or 1 (bf16), got %d", (int)p->w_dtype);
+  if (!std::isfinite(p->softmax_scale))
+    return fail(MLA_ERR_INVALID_SHAPE, "softmax_scale: expected a finite value, got %g", (double)p->softmax_scale);
+  return MLA_OK;
+}
+
+// Workspace of the prefill: rebuilt no-RoPE keys, RoPE keys and values of
+// every token slot a sequence can hold, fp32.
+size_t prefill_workspace(const mla_prefill_params_t* p, int64_t* kn_off, int64_t* kr_off, int64_t* v_off) {
+  const int64_t slots = (int64_t)p->batch * p->max_blocks_per_seq * p->page_block;
+  const int64_t H = p->dims.num_heads;
+  const int64_t kn = slots * H * p->dims.d_nope * 4, kr = slots * p->dims.d_rope * 4;
+  const int64_t v = slots * H * p->dims.d_v * 4;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  if (kn_off) *kn_off = 0;
+  if (kr_off) *kr_off = up(kn);
+  if (v_off) *v_off = up(kn) + up(kr);
+  return (size_t)(up(kn) + up(kr) + up(v));
+}
+
 }  // namespace
 
 extern "C" {
@@ -305,6 +351,66 @@ mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows, const void*
   if (a.n_slots == 0) return ok();
   hipError_t e = mla::launch_cache_write(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("mla_cache_write launch", e);
+  return ok();
+}
+
+mla_status_t mla_prefill_workspace_size(const mla_prefill_params_t* p, size_t* bytes) {
+  if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
+  mla_status_t st = check_prefill(p);
+  if (st) return st;
+  *bytes = prefill_workspace(p, nullptr, nullptr, nullptr);
+  return ok();
+}
+
+mla_status_t mla_prefill_paged(const mla_prefill_params_t* p, void* stream) {
+  mla_status_t st = check_prefill(p);
+  if (st) return st;
+  if (p->batch == 0) return ok();
+  const struct {
+    const void* ptr;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{p->q, "q", 16},           {p->w_kv_b, "w_kv_b", 16},        {p->kv_pool, "kv_pool", 16},
+              {p->block_table, "block_table", 4}, {p->seq_lens, "seq_lens", 4}, {p->workspace, "workspace", 16},
+              {p->out, "out", 16}};
+  for (const auto& x : ptrs) {
+    if (!x.ptr) return fail(MLA_ERR_NULL_POINTER, "%s: expected non-null, got NULL", x.name);
+    if (!aligned(x.ptr, x.align))
+      return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
+  }
+  if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
+  int64_t kn_off, kr_off, v_off;
+  const size_t need = prefill_workspace(p, &kn_off, &kr_off, &v_off);
+  if (p->workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", need, p->workspace_bytes);
+  mla::PrefillArgs a{};
+  a.B = p->batch;
+  a.Sq = p->q_per_seq;
+  a.H = p->dims.num_heads;
+  a.dn = p->dims.d_nope;
+  a.dr = p->dims.d_rope;
+  a.dv = p->dims.d_v;
+  a.dc = p->dims.d_latent;
+  a.P = p->page_block;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.Lcap = (int64_t)p->max_blocks_per_seq * p->page_block;
+  a.q = p->q;
+  a.q_f32 = p->q_dtype == MLA_F32;
+  a.w = p->w_kv_b;
+  a.w_f32 = p->w_dtype == MLA_F32;
+  a.pool = static_cast<const uint8_t*>(p->kv_pool);
+  a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
+  a.block_table = p->block_table;
+  a.seq_lens = p->seq_lens;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  char* ws = static_cast<char*>(p->workspace);
+  a.kn = reinterpret_cast<float*>(ws + kn_off);
+  a.kr = reinterpret_cast<float*>(ws + kr_off);
+  a.v = reinterpret_cast<float*>(ws + v_off);
+  a.out = p->out;
+  a.lse = p->lse;
+  const hipError_t e = mla::launch_prefill(a, p->kv_format, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("prefill launch", e);
   return ok();
 }
 

@@ -122,4 +122,27 @@ struct CacheWriteArgs {
 };
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 
+// Unabsorbed prefill (prefill_simt.hip).
+struct PrefillArgs {
+  int B, Sq, H, dn, dr, dv, dc;
+  int P, max_blocks;
+  int64_t Lcap;               // token capacity per sequence: max_blocks * P
+  const void* q;              // [B*Sq][H][dn + dr]
+  int q_f32;
+  const void* w;              // [H][dn + dv][dc]
+  int w_f32;
+  const uint8_t* pool;
+  int64_t row_bytes;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float scale_log2;
+  float* kn;                  // workspace: [B][Lcap][H][dn]
+  float* kr;                  // workspace: [B][Lcap][dr]
+  float* v;                   // workspace: [B][Lcap][H][dv]
+  float* out;                 // [B*Sq][H][dv]
+  float* lse;                 // [B*Sq][H] or null
+};
+bool prefill_supported(int dc, int dr, int dn, int dv);
+hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s);
+
 }  // namespace mla

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -194,3 +194,43 @@ def test_sparse_decode_null_index_list_and_workspace_size():
     n4 = mla.mla_decode_sparse_workspace_size(sparse_params(q_per_seq=4), 128)
     assert n4 > 3 * n1 // 2
     assert n4 >= mla.mla_decode_workspace_size(sparse_params(q_per_seq=4))
+
+
+def prefill_params(**kw):
+    base = dict(dims=GLM, batch=2, q_per_seq=64, q=FAKE, w_kv_b=FAKE, kv_pool=FAKE, kv_format=MLA_KV_BF16,
+                num_pages=8, page_block=64, block_table=FAKE, max_blocks_per_seq=4, seq_lens=FAKE,
+                softmax_scale=0.0625, out=FAKE, lse=None, workspace=FAKE, workspace_bytes=1 << 30,
+                q_dtype=MLA_F32, w_dtype=MLA_F32)
+    base.update(kw)
+    return mla.make_prefill_params(**base)
+
+
+@pytest.mark.parametrize("kw,status,fragment", [
+    (dict(q_per_seq=0), 2, "q_per_seq"),
+    (dict(kv_format=7), 3, "kv_format"),
+    (dict(dims=Dims(20, 512, 64, 256, 256)), 3, "d_nope + d_rope"),
+    (dict(dims=FP8), 3, "d_latent"),
+    (dict(page_block=48), 3, "page_block"),
+    (dict(q_dtype=4), 3, "q_dtype"),
+    (dict(w_dtype=4), 3, "w_dtype"),
+    (dict(max_blocks_per_seq=0), 2, "max_blocks_per_seq"),
+    (dict(softmax_scale=float("inf")), 2, "softmax_scale"),
+    (dict(q=0), 1, "q"),
+    (dict(out=0), 1, "out"),
+    (dict(workspace=0), 1, "workspace"),
+    (dict(w_kv_b=FAKE + 8), 4, "w_kv_b"),
+    (dict(workspace_bytes=1024), 5, "workspace_bytes"),
+])
+def test_prefill_rejects_before_launch(kw, status, fragment):
+    with pytest.raises(MlaError) as e:
+        mla.mla_prefill_paged(prefill_params(**kw), stream=0)
+    assert e.value.status == status
+    assert fragment in e.value.message
+
+
+def test_prefill_workspace_size_and_empty_batch():
+    p = prefill_params()
+    slots = 2 * 4 * 64
+    want = 4 * slots * 20 * 192 + 4 * slots * 64 + 4 * slots * 20 * 256  # every part a multiple of 256 here
+    assert mla.mla_prefill_workspace_size(p) == want
+    mla.mla_prefill_paged(prefill_params(batch=0, q=0, out=0, workspace=0), stream=0)  # no-op, no launch
