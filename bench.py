@@ -281,6 +281,55 @@ def fp4_timing(inp, dev, reps: int):
             "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9}
 
 
+def prefill_timing(inp, dev, chunk: int, n_seqs: int, reps: int):
+    """mla_prefill_paged over the first n_seqs sequences of the batch, each
+    treating its last `chunk` cached tokens as the new chunk (seeded N(0, 1)
+    queries): time per call (both kernels, torch events on the stream) and
+    the algorithmic fp32 flops, K/V rebuild 2 L H (d_nope + d_v) d_latent per
+    sequence plus attention 2 H (d_nope + d_rope + d_v) per visible
+    (query, token) pair.  Only for d_nope + d_rope <= 256 and d_v <= 256."""
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_amd as mla
+
+    wl = inp.wl
+    if chunk <= 0 or wl.d_nope + wl.d_rope > 256 or wl.d_v > 256:
+        return None
+    B = min(n_seqs, wl.batch)
+    lens = inp.seq_lens[:B].astype(np.int64)
+    if int(lens.min()) < chunk or int(lens.sum()) > 65536:  # keep the leg to a fraction of a second
+        return None
+    H = wl.heads
+    g = torch.Generator().manual_seed(9)
+    q = torch.randn((B * chunk, H, wl.d_nope + wl.d_rope), generator=g).cuda()
+    out = torch.empty((B * chunk, H, wl.d_v), device="cuda")
+    params = mla.make_prefill_params(
+        dims=dev.dims, batch=B, q_per_seq=chunk, q=q, w_kv_b=dev.w_kv_b, kv_pool=dev.kv_pool,
+        kv_format=dev.kv_format, num_pages=dev.kv_pool.shape[0], page_block=dev.page_block,
+        block_table=dev.block_table[:B].contiguous(), max_blocks_per_seq=dev.block_table.shape[1],
+        seq_lens=dev.seq_lens[:B].contiguous(), softmax_scale=dev.softmax_scale, out=out)
+    nbytes = mla.mla_prefill_workspace_size(params)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
+    mla.mla_prefill_paged(params)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        mla.mla_prefill_paged(params)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    expand = 2.0 * float(lens.sum()) * H * (wl.d_nope + wl.d_v) * wl.d_latent
+    pairs = float(sum(int(L - chunk + i + 1) for L in lens for i in range(chunk)))
+    attn = 2.0 * pairs * H * (wl.d_nope + wl.d_rope + wl.d_v)
+    tflops = (expand + attn) / (us * 1e-6) / 1e12
+    return {"sequences": B, "chunk": chunk, "context": [int(x) for x in lens], "us": us,
+            "flops": expand + attn, "tflops": tflops, "peak_fp32_vector_tflops": 157.3,
+            "frac": tflops / 157.3, "kernel": "simt_fp32"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,6 +346,8 @@ def main() -> int:
                     help="total bytes of rotated cache copies (>= 4x the Infinity Cache)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-chunk", type=int, default=256,
+                    help="also time mla_prefill_paged with this many new tokens on 4 sequences (0: skip)")
     ap.add_argument("--sparse-topk", type=int, default=2048,
                     help="also time mla_decode_sparse_paged over this many listed tokens per query (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -429,6 +480,11 @@ def main() -> int:
     if fp4 is not None:
         log(f"[bench] fp4 cache copy: attention kernel {fp4['attention_kernel_us']:.1f} us ({fp4['gbs']:.0f} GB/s)")
 
+    prefill = prefill_timing(inp, dev, args.prefill_chunk, 4, 3)
+    if prefill is not None:
+        log(f"[bench] prefill of {prefill['chunk']} new tokens on {prefill['sequences']} sequences: "
+            f"{prefill['us'] / 1e3:.2f} ms ({prefill['tflops']:.1f} TFLOP/s fp32)")
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
@@ -475,6 +531,7 @@ def main() -> int:
         "cache_write": cache_write,
         "sparse_decode": sparse,
         "fp4_decode": fp4,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
     return 0
