@@ -12,9 +12,10 @@
 //      latent rows are decoded to fp32 into LDS and multiplied by the head's
 //      kv_b_proj rows; K (no-RoPE part), the shared RoPE key and V go to the
 //      workspace as fp32;
-//   2. prefill_attn_kernel: one wave per (query token, head); a 64-token
-//      block's scores (one token per lane), an online-softmax update, and
-//      the value rows accumulated with each lane owning 4 output columns.
+//   2. prefill_attn_kernel: per (16 queries, head) a workgroup walks the
+//      keys in blocks of 16 staged in LDS once for all 16 queries: one score
+//      per thread, an online-softmax update per query, and each thread
+//      accumulating 16 output columns of its query.
 // Every product is an fp32 FMA; this is the full-precision first path of the
 // prefill, not a matrix-core one.
 #include <cmath>
@@ -108,72 +109,111 @@ __global__ __launch_bounds__(kExpandThreads) void prefill_expand_kernel(PrefillA
   }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Attention: a workgroup takes 16 consecutive queries of one (sequence,
+// head) and walks the keys in blocks of 16, staged in LDS once for all 16
+// queries.  Thread (qi, k) = (tid / 16, tid % 16) scores query qi against
+// key k of the block, then owns output columns 16k .. 16k + 15 of query qi.
+constexpr int kQB = 16;      // queries per workgroup
+constexpr int kKB = 16;      // keys per block
+constexpr int kRow = 260;    // LDS row stride in floats: float4 rows 4 banks apart
+
+__device__ __forceinline__ float group16_max(float v) {
+  for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+__device__ __forceinline__ float group16_sum(float v) {
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
 
-__global__ __launch_bounds__(64) void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ float sq[kMaxQk];
-  __shared__ float sp[64];
-  const int bq = blockIdx.x, h = blockIdx.y;
-  const int b = bq / a.Sq, i = bq % a.Sq;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kQB * kKB) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) float sQ[kQB][kRow];
+  __shared__ __attribute__((aligned(16))) float sK[kKB][kRow];
+  __shared__ __attribute__((aligned(16))) float sV[kKB][kRow];
+  __shared__ float sP[kQB][kKB + 1];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int nqb = (a.Sq + kQB - 1) / kQB;
+  const int b = blockIdx.x / nqb, i0 = (blockIdx.x % nqb) * kQB;
   const int L = (int)min((int64_t)max(a.seq_lens[b], 0), a.Lcap);
-  const int last = L - a.Sq + i;  // visible positions t <= last
   const int nqk = a.dn + a.dr;
-  const int64_t qoff = ((int64_t)bq * a.H + h) * nqk;
-  for (int d = lane; d < nqk; d += 64)
-    sq[d] = a.q_f32 ? static_cast<const float*>(a.q)[qoff + d]
-                    : bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qoff + d]);
-  __syncthreads();
-
-  float o[kMaxV / 64] = {0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;  // base-2 running maximum and sum
-  for (int t0 = 0; t0 <= last; t0 += 64) {
-    const int t = t0 + lane;
-    float s = -INFINITY;
-    if (t <= last) {
-      const float* kn = a.kn + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dn;
-      const float* kr = a.kr + ((int64_t)b * a.Lcap + t) * a.dr;
-      float dot = 0.f;
-      for (int d = 0; d < a.dn; ++d) dot = fmaf(sq[d], kn[d], dot);
-      for (int d = 0; d < a.dr; ++d) dot = fmaf(sq[a.dn + d], kr[d], dot);
-      s = dot * a.scale_log2;
+  for (int idx = tid; idx < kQB * nqk; idx += kQB * kKB) {
+    const int r = idx / nqk, d = idx % nqk, i = i0 + r;
+    const int64_t off = (((int64_t)b * a.Sq + i) * a.H + h) * nqk + d;
+    float x = 0.f;
+    if (i < a.Sq) x = a.q_f32 ? static_cast<const float*>(a.q)[off] : bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[off]);
+    sQ[r][d] = x;
+  }
+  const int qi = tid >> 4, k = tid & 15;
+  const int my_last = L - a.Sq + i0 + qi;  // this query sees t <= my_last
+  const int blk_last = min(L - 1, L - a.Sq + min(i0 + kQB, a.Sq) - 1);  // the block's last visible key
+  float o[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = 0.f;
+  float m = -INFINITY, l = 0.f;  // base 2, the same in the 16 threads of a query
+  const int nk4 = nqk / 4, nv4 = a.dv / 4;
+  for (int t0 = 0; t0 <= blk_last; t0 += kKB) {
+    __syncthreads();  // the previous block's readers are done (and the queries are in)
+    for (int idx = tid; idx < kKB * nk4; idx += kQB * kKB) {
+      const int r = idx / nk4, c4 = idx % nk4, t = t0 + r;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t <= blk_last)
+        x = 4 * c4 < a.dn ? reinterpret_cast<const float4*>(a.kn + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dn)[c4]
+                          : reinterpret_cast<const float4*>(a.kr + ((int64_t)b * a.Lcap + t) * a.dr)[c4 - a.dn / 4];
+      *reinterpret_cast<float4*>(&sK[r][4 * c4]) = x;
     }
-    const float m_new = fmaxf(m, wave_max(s));  // finite: t0 <= last
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
-    const float p = t <= last ? exp2f(s - m_new) : 0.f;
-    l = l * alpha + wave_sum(p);
-#pragma unroll
-    for (int k = 0; k < kMaxV / 64; ++k) o[k] *= alpha;
-    sp[lane] = p;
+    for (int idx = tid; idx < kKB * nv4; idx += kQB * kKB) {
+      const int r = idx / nv4, c4 = idx % nv4, t = t0 + r;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t <= blk_last) x = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c4];
+      *reinterpret_cast<float4*>(&sV[r][4 * c4]) = x;
+    }
     __syncthreads();
-    const int nt = min(64, last + 1 - t0);
-    for (int tt = 0; tt < nt; ++tt) {
-      const float pt = sp[tt];
-      const float* vr = a.v + (((int64_t)b * a.Lcap + t0 + tt) * a.H + h) * a.dv;
+
+    const int t = t0 + k;
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll 4
+    for (int c4 = 0; c4 < nk4; ++c4) {
+      const float4 x = *reinterpret_cast<const float4*>(&sQ[qi][4 * c4]);
+      const float4 y = *reinterpret_cast<const float4*>(&sK[k][4 * c4]);
+      d0 = fmaf(x.x, y.x, d0), d1 = fmaf(x.y, y.y, d1), d2 = fmaf(x.z, y.z, d2), d3 = fmaf(x.w, y.w, d3);
+    }
+    const float sc = t <= my_last ? ((d0 + d1) + (d2 + d3)) * a.scale_log2 : -INFINITY;
+    const float m_new = fmaxf(m, group16_max(sc));
+    float alpha = 1.f, p = 0.f;
+    if (m_new != -INFINITY) {  // uniform over the query's 16 threads
+      alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+      p = sc == -INFINITY ? 0.f : exp2f(sc - m_new);
+    }
+    l = l * alpha + group16_sum(p);
+    m = m_new;
+    sP[qi][k] = p;
 #pragma unroll
-      for (int k = 0; k < kMaxV / 64; ++k) {
-        const int d = lane + 64 * k;
-        if (d < a.dv) o[k] = fmaf(pt, vr[d], o[k]);
+    for (int c = 0; c < 16; ++c) o[c] *= alpha;
+    __syncthreads();  // P of the block is in LDS
+
+#pragma unroll 4
+    for (int tt = 0; tt < kKB; ++tt) {
+      const float pt = sP[qi][tt];
+      const float4* vr = reinterpret_cast<const float4*>(&sV[tt][16 * k]);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 y = vr[c4];
+        o[4 * c4 + 0] = fmaf(pt, y.x, o[4 * c4 + 0]);
+        o[4 * c4 + 1] = fmaf(pt, y.y, o[4 * c4 + 1]);
+        o[4 * c4 + 2] = fmaf(pt, y.z, o[4 * c4 + 2]);
+        o[4 * c4 + 3] = fmaf(pt, y.w, o[4 * c4 + 3]);
       }
     }
-    __syncthreads();  // sp is rewritten by the next block
-    m = m_new;
   }
+  const int i = i0 + qi;
+  if (i >= a.Sq) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* dst = a.out + ((int64_t)bq * a.H + h) * a.dv;
+  float* dst = a.out + (((int64_t)b * a.Sq + i) * a.H + h) * a.dv;
 #pragma unroll
-  for (int k = 0; k < kMaxV / 64; ++k) {
-    const int d = lane + 64 * k;
-    if (d < a.dv) dst[d] = o[k] * inv;
-  }
-  if (a.lse && lane == 0) a.lse[(int64_t)bq * a.H + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  for (int c = 0; c < 16; ++c)
+    if (16 * k + c < a.dv) dst[16 * k + c] = o[c] * inv;
+  if (a.lse && k == 0) a.lse[((int64_t)b * a.Sq + i) * a.H + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -194,7 +234,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prefill_attn_kernel<<<dim3((unsigned)(a.B * a.Sq), (unsigned)a.H), 64, 0, s>>>(a);
+  const unsigned qblocks = (unsigned)((a.Sq + kQB - 1) / kQB);
+  prefill_attn_kernel<<<dim3((unsigned)a.B * qblocks, (unsigned)a.H), kQB * kKB, 0, s>>>(a);
   return hipGetLastError();
 }
 
