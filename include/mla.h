@@ -261,9 +261,11 @@ mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows,
  *                                  w_kv_b[h])
  *   s_t = softmax_scale * q[b][i][h] . k_t,   out = sum_t softmax(s)_t v_t,
  *   lse = log sum_t exp(s_t); no visible token: out = 0, lse = -inf.
- * Computed in fp32 on the vector ALUs: the keys and values of every token
- * slot a sequence can hold (max_blocks_per_seq * page_block) are rebuilt
- * into the workspace, then each (query, head) runs online softmax over them. */
+ * The keys and values of every token slot a sequence can hold
+ * (max_blocks_per_seq * page_block) are rebuilt into the workspace in fp32
+ * (bf16 weights: on the matrix cores, fp32 accumulation; f32 weights: fp32
+ * vector ALUs), then each (query, head) runs online softmax over them in
+ * fp32 on the vector ALUs. */
 typedef struct {
   mla_dims_t dims;      /* d_nope + d_rope <= 256, d_v <= 256 */
   int32_t batch;        /* B >= 0 */

@@ -31,6 +31,7 @@ SOURCES = [
     "proj_mfma.hip",
     "cache_write.hip",
     "prefill_simt.hip",
+    "prefill_mfma.hip",
 ]
 
 FLAGS = [

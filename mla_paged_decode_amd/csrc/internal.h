@@ -144,5 +144,8 @@ struct PrefillArgs {
 };
 bool prefill_supported(int dc, int dr, int dn, int dv);
 hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s);
+// The K/V rebuild on the matrix cores (prefill_mfma.hip): bf16 weights.
+bool prefill_expand_mfma_supported(const PrefillArgs& a);
+hipError_t launch_prefill_expand_mfma(const PrefillArgs& a, int fmt, hipStream_t s);
 
 }  // namespace mla

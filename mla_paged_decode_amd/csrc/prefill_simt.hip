@@ -225,7 +225,10 @@ bool prefill_supported(int dc, int dr, int dn, int dv) {
 hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s) {
   if (a.B == 0 || a.Sq == 0) return hipSuccess;
   const dim3 eg((unsigned)((a.Lcap + kExpandTok - 1) / kExpandTok), (unsigned)a.B, (unsigned)a.H);
-  switch (fmt) {
+  if (prefill_expand_mfma_supported(a)) {
+    const hipError_t e = launch_prefill_expand_mfma(a, fmt, s);
+    if (e != hipSuccess) return e;
+  } else switch (fmt) {
     case kF32: prefill_expand_kernel<kF32><<<eg, kExpandThreads, 0, s>>>(a); break;
     case kBF16: prefill_expand_kernel<kBF16><<<eg, kExpandThreads, 0, s>>>(a); break;
     case kFP8: prefill_expand_kernel<kFP8><<<eg, kExpandThreads, 0, s>>>(a); break;

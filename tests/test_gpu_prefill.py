@@ -54,16 +54,22 @@ def check(got, glse, ref, rlse):
     assert np.max(np.abs(glse[fin] - rlse[fin]), initial=0.0) <= 1e-4
 
 
-@pytest.mark.parametrize("name,sq,lens", [
-    ("glm_b32_h20_ctx4096_bf16", 37, (37, 300, 129)),
-    ("glm_b32_h20_ctx4096_bf16", 64, (64, 1000)),
-    ("tiny_b2_h4_f32", 16, (16, 77)),
-    ("fp8_mtp4_b64_h20_ctx16k", 24, (24, 200, 65)),
+@pytest.mark.parametrize("name,sq,lens,kv", [
+    ("glm_b32_h20_ctx4096_bf16", 37, (37, 300, 129), None),
+    ("glm_b32_h20_ctx4096_bf16", 64, (64, 1000), None),
+    ("glm_b32_h20_ctx4096_bf16", 20, (20, 170), "f32"),
+    ("tiny_b2_h4_f32", 16, (16, 77), None),
+    ("fp8_mtp4_b64_h20_ctx16k", 24, (24, 200, 65), None),
 ])
-def test_prefill_matches_oracle(name, sq, lens):
+def test_prefill_matches_oracle(name, sq, lens, kv):
     """Chunks that are the whole sequence (L = Sq) and chunks after a
-    cached context, block boundaries of 64 and ragged tails."""
+    cached context, block boundaries and ragged tails.  bf16 weights rebuild
+    K and V on the matrix cores (bf16, fp8 and fp4 latents exact in bf16, an
+    f32 latent split into hi + lo); f32 weights (the tiny case) on the
+    vector ALUs."""
     wl = WORKLOADS[name].with_(batch=len(lens), q_per_seq=sq, lens=("fixed", lens))
+    if kv is not None:
+        wl = wl.with_(kv_format=kv)
     inp = make_inputs(wl, poison_tail=True)
     got, glse = run_prefill(inp)
     ref, rlse = oracle.mla_decode(inp)
