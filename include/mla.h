@@ -264,8 +264,9 @@ mla_status_t mla_cache_write(const mla_dims_t* dims, int32_t n_rows,
  * The keys and values of every token slot a sequence can hold
  * (max_blocks_per_seq * page_block) are rebuilt into the workspace in fp32
  * (bf16 weights: on the matrix cores, fp32 accumulation; f32 weights: fp32
- * vector ALUs), then each (query, head) runs online softmax over them in
- * fp32 on the vector ALUs. */
+ * vector ALUs), then each (query, head) runs online softmax over them: on
+ * the matrix cores for 256-wide keys and values, with every operand split
+ * into bf16 hi + lo (fp32-level accuracy), else on the fp32 vector ALUs. */
 typedef struct {
   mla_dims_t dims;      /* d_nope + d_rope <= 256, d_v <= 256 */
   int32_t batch;        /* B >= 0 */

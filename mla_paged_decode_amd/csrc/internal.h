@@ -147,5 +147,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s);
 // The K/V rebuild on the matrix cores (prefill_mfma.hip): bf16 weights.
 bool prefill_expand_mfma_supported(const PrefillArgs& a);
 hipError_t launch_prefill_expand_mfma(const PrefillArgs& a, int fmt, hipStream_t s);
+// The causal attention on the matrix cores: keys and values 256 wide.
+bool prefill_attn_mfma_supported(const PrefillArgs& a);
+hipError_t launch_prefill_attn_mfma(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -132,6 +132,188 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_expand_mfma_kernel(Prefil
   }
 }
 
+// Causal attention of the chunk on the matrix cores, for 256-wide keys
+// (d_nope + d_rope) and values.  A workgroup of 4 waves takes 64
+// consecutive queries of one (sequence, head), 16 per wave, and walks the
+// keys in blocks of 32 staged in LDS once for all of them.  Every fp32
+// operand is split into bf16 hi + lo and each product takes three MFMAs
+// (hi.hi + hi.lo + lo.hi), which keeps the result at fp32-level accuracy:
+//   S = Q K^T: A = the wave's queries (registers), B = K rows (LDS);
+//   online softmax per query row in the S layout (lane = key, 4 rows);
+//   P goes through LDS to the A layout; O += P V with V transposed in LDS.
+constexpr int kAQ = 16;        // queries per wave
+constexpr int kAKeys = 32;     // keys per block
+constexpr int kAD = 256;       // key and value width
+constexpr int kKRowB = kAD * 2 + 16;      // K tile row stride (bytes)
+constexpr int kVRowB = kAKeys * 2 + 16;   // transposed V tile row stride (bytes)
+constexpr int kPRowB = kAKeys * 2 + 16;   // P tile row stride (bytes)
+
+__device__ __forceinline__ bf16x8 lds_b8(const char* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char kh[kAKeys * kKRowB];
+  __shared__ __attribute__((aligned(16))) char kl[kAKeys * kKRowB];
+  __shared__ __attribute__((aligned(16))) char vth[kAD * kVRowB];
+  __shared__ __attribute__((aligned(16))) char vtl[kAD * kVRowB];
+  __shared__ __attribute__((aligned(16))) char ph[kWaves][kAQ * kPRowB];
+  __shared__ __attribute__((aligned(16))) char pl[kWaves][kAQ * kPRowB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int h = blockIdx.y;
+  const int nqb = (a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves);
+  const int b = blockIdx.x / nqb;
+  const int iw = (blockIdx.x % nqb) * kAQ * kWaves + kAQ * wave;  // the wave's first query
+  const int L = (int)min((int64_t)max(a.seq_lens[b], 0), a.Lcap);
+  const int ig_end = min(a.Sq, (blockIdx.x % nqb + 1) * kAQ * kWaves);
+  const int blk_last = min(L - 1, L - a.Sq + ig_end - 1);  // the workgroup's last visible key
+
+  // A operand: query row iw + li, dims 32 ks + 8 g .. + 7, as hi and lo.
+  bf16x8 qh[kAD / 32], ql[kAD / 32];
+  {
+    const int i = iw + li;
+    const int64_t off = (((int64_t)b * a.Sq + min(i, a.Sq - 1)) * a.H + h) * kAD;
+#pragma unroll
+    for (int ks = 0; ks < kAD / 32; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = off + 32 * ks + 8 * g + j;
+        x[j] = a.q_f32 ? static_cast<const float*>(a.q)[e] : bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[e]);
+        if (i >= a.Sq) x[j] = 0.f;
+      }
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) split_bf16x2(x[2 * j], x[2 * j + 1], hw[j], lw[j]);
+      qh[ks] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      ql[ks] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+    }
+  }
+
+  f32x4 o[kAD / 16];
+#pragma unroll
+  for (int d = 0; d < kAD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];  // per query row 4 g + r, base 2
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = -INFINITY, l[r] = 0.f;
+
+  for (int t0 = 0; t0 <= blk_last; t0 += kAKeys) {
+    __syncthreads();  // the previous block's readers are done
+    // K rows (hi, lo): key r, dims 4c .. 4c + 3
+    for (int idx = tid; idx < kAKeys * (kAD / 4); idx += 64 * kWaves) {
+      const int r = idx / (kAD / 4), c = idx % (kAD / 4), t = t0 + r;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t <= blk_last)
+        x = 4 * c < a.dn ? reinterpret_cast<const float4*>(a.kn + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dn)[c]
+                         : reinterpret_cast<const float4*>(a.kr + ((int64_t)b * a.Lcap + t) * a.dr)[c - a.dn / 4];
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(x.x, x.y, h0, l0);
+      split_bf16x2(x.z, x.w, h1, l1);
+      *reinterpret_cast<uint2*>(kh + r * kKRowB + 8 * c) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(kl + r * kKRowB + 8 * c) = make_uint2(l0, l1);
+    }
+    // V transposed (hi, lo): keys 2 rp, 2 rp + 1 and dims 4c .. 4c + 3
+    for (int idx = tid; idx < (kAKeys / 2) * (kAD / 4); idx += 64 * kWaves) {
+      const int rp = idx / (kAD / 4), c = idx % (kAD / 4), t = t0 + 2 * rp;
+      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+      if (t <= blk_last) x0 = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c];
+      if (t + 1 <= blk_last)
+        x1 = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t + 1) * a.H + h) * a.dv)[c];
+      const float v0[4] = {x0.x, x0.y, x0.z, x0.w}, v1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hw, lw;
+        split_bf16x2(v0[j], v1[j], hw, lw);
+        *reinterpret_cast<uint32_t*>(vth + (4 * c + j) * kVRowB + 4 * rp) = hw;
+        *reinterpret_cast<uint32_t*>(vtl + (4 * c + j) * kVRowB + 4 * rp) = lw;
+      }
+    }
+    __syncthreads();
+
+    // S = Q K^T for keys t0 + 16 nt + li (lane) and queries iw + 4 g + r
+    f32x4 sc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* krh = kh + (16 * nt + li) * kKRowB + 16 * g;
+      const char* krl = kl + (16 * nt + li) * kKRowB + 16 * g;
+#pragma unroll
+      for (int ks = 0; ks < kAD / 32; ++ks) {
+        const bf16x8 bh = lds_b8(krh + 64 * ks), bl = lds_b8(krl + 64 * ks);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], bh, acc, 0, 0, 0);
+      }
+      sc[nt] = acc;
+    }
+    float pv[2][4], alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int last = L - a.Sq + iw + 4 * g + r;  // query's last visible key
+      float s0 = t0 + li <= last ? sc[0][r] * a.scale_log2 : -INFINITY;
+      float s1 = t0 + 16 + li <= last ? sc[1][r] * a.scale_log2 : -INFINITY;
+      float mx = fmaxf(s0, s1);
+      for (int o2 = 8; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+      const float m_new = fmaxf(m[r], mx);
+      float al = 1.f, p0 = 0.f, p1 = 0.f;
+      if (m_new != -INFINITY) {
+        al = m[r] == -INFINITY ? 0.f : exp2f(m[r] - m_new);
+        p0 = s0 == -INFINITY ? 0.f : exp2f(s0 - m_new);
+        p1 = s1 == -INFINITY ? 0.f : exp2f(s1 - m_new);
+      }
+      float ps = p0 + p1;
+      for (int o2 = 8; o2 >= 1; o2 >>= 1) ps += __shfl_xor(ps, o2);
+      l[r] = l[r] * al + ps;
+      m[r] = m_new;
+      alpha[r] = al;
+      pv[0][r] = p0;
+      pv[1][r] = p1;
+    }
+    // P (hi, lo) into the wave's tile: row 4 g + r, keys li and 16 + li
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t hb = f32_to_bf16_bits(pv[nt][r]);
+        const uint32_t lb = f32_to_bf16_bits(pv[nt][r] - __uint_as_float(hb << 16));
+        const int off = (4 * g + r) * kPRowB + 2 * (16 * nt + li);
+        *reinterpret_cast<uint16_t*>(ph[wave] + off) = (uint16_t)hb;
+        *reinterpret_cast<uint16_t*>(pl[wave] + off) = (uint16_t)lb;
+      }
+#pragma unroll
+    for (int d = 0; d < kAD / 16; ++d)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[d][r] *= alpha[r];
+    __syncthreads();  // P tiles written
+
+    // O += P V: A = P (row li, keys 8 g ..), B = V^T rows (dim 16 d + li)
+    const bf16x8 pah = lds_b8(ph[wave] + li * kPRowB + 16 * g);
+    const bf16x8 pal = lds_b8(pl[wave] + li * kPRowB + 16 * g);
+#pragma unroll
+    for (int d = 0; d < kAD / 16; ++d) {
+      const bf16x8 vh = lds_b8(vth + (16 * d + li) * kVRowB + 16 * g);
+      const bf16x8 vl = lds_b8(vtl + (16 * d + li) * kVRowB + 16 * g);
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vh, o[d], 0, 0, 0);
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vl, o[d], 0, 0, 0);
+      o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vh, o[d], 0, 0, 0);
+    }
+  }
+
+  // out[query iw + 4 g + r][16 d + li] = O / l; lse by lane li = 0
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = iw + 4 * g + r;
+    if (i >= a.Sq) continue;
+    const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+    float* dst = a.out + (((int64_t)b * a.Sq + i) * a.H + h) * a.dv;
+#pragma unroll
+    for (int d = 0; d < kAD / 16; ++d) dst[16 * d + li] = o[d][r] * inv;
+    if (a.lse && li == 0)
+      a.lse[((int64_t)b * a.Sq + i) * a.H + h] = l[r] > 0.f ? (m[r] + log2f(l[r])) * 0.693147180559945309f : -INFINITY;
+  }
+}
+
 template <int FMT>
 hipError_t launch_fmt(const PrefillArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.Lcap + kTokBlk * kBlocks - 1) / (kTokBlk * kBlocks)),
@@ -148,6 +330,17 @@ hipError_t launch_fmt(const PrefillArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool prefill_attn_mfma_supported(const PrefillArgs& a) {
+  return a.dn + a.dr == kAD && a.dv == kAD && a.dn % 4 == 0;
+}
+
+hipError_t launch_prefill_attn_mfma(const PrefillArgs& a, hipStream_t s) {
+  if (!prefill_attn_mfma_supported(a)) return hipErrorInvalidValue;
+  const unsigned qb = (unsigned)((a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves));
+  prefill_attn_mfma_kernel<<<dim3((unsigned)a.B * qb, (unsigned)a.H), 64 * kWaves, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 bool prefill_expand_mfma_supported(const PrefillArgs& a) {
   return !a.w_f32 && a.dc % 32 == 0 && a.dc <= 512 && (a.dn + a.dv) % kCols == 0 && a.dr % 4 == 0;

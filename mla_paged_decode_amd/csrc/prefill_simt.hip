@@ -1,4 +1,7 @@
-// Unabsorbed MLA prefill over the paged latent cache, fp32 on the vector ALUs.
+// Unabsorbed MLA prefill over the paged latent cache: the fp32 vector-ALU
+// kernels, and the launcher (which takes the matrix-core kernels of
+// prefill_mfma.hip where they apply: the K/V rebuild for bf16 weights, the
+// attention for 256-wide keys and values).
 //
 // A chunk of Sq new tokens per sequence (already appended, the last Sq of
 // the L cached tokens) attends causally to the whole cache in the
@@ -237,6 +240,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (prefill_attn_mfma_supported(a)) return launch_prefill_attn_mfma(a, s);
   const unsigned qblocks = (unsigned)((a.Sq + kQB - 1) / kQB);
   prefill_attn_kernel<<<dim3((unsigned)a.B * qblocks, (unsigned)a.H), kQB * kKB, 0, s>>>(a);
   return hipGetLastError();

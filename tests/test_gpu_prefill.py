@@ -66,10 +66,22 @@ def test_prefill_matches_oracle(name, sq, lens, kv):
     cached context, block boundaries and ragged tails.  bf16 weights rebuild
     K and V on the matrix cores (bf16, fp8 and fp4 latents exact in bf16, an
     f32 latent split into hi + lo); f32 weights (the tiny case) on the
-    vector ALUs."""
+    vector ALUs.  The attention (256-wide keys and values) runs on the matrix
+    cores with every operand split into bf16 hi + lo."""
     wl = WORKLOADS[name].with_(batch=len(lens), q_per_seq=sq, lens=("fixed", lens))
     if kv is not None:
         wl = wl.with_(kv_format=kv)
+    inp = make_inputs(wl, poison_tail=True)
+    got, glse = run_prefill(inp)
+    ref, rlse = oracle.mla_decode(inp)
+    check(got, glse, ref, rlse)
+
+
+def test_prefill_narrow_heads_on_the_vector_alus():
+    """Keys and values narrower than 256 (d_nope 128, d_v 128): the
+    attention runs on the vector-ALU kernel."""
+    wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=2, heads=6, d_nope=128, d_v=128, q_per_seq=40,
+                                                      lens=("fixed", (40, 333)))
     inp = make_inputs(wl, poison_tail=True)
     got, glse = run_prefill(inp)
     ref, rlse = oracle.mla_decode(inp)
