@@ -200,7 +200,9 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
  * pages pad the list to 128) and either the cache is bf16 with num_heads <=
  * 64, or it is fp8 / fp4 (448 + 64 row) with bf16 q_abs and num_heads <= 128
  * (padding slots then contribute exact zeros, whatever the row they are
- * pointed at holds); unless MLA_KERNEL_SIMT is asked for.  The fp32
+ * pointed at holds; on the bf16 kernel they read slot 0 of page 0, which
+ * must then hold finite values, as a zero weight cannot cancel a NaN);
+ * unless MLA_KERNEL_SIMT is asked for.  The fp32
  * vector-ALU one otherwise (MLA_KERNEL_MFMA where none applies is
  * rejected).  Errors: see the conventions above. */
 mla_status_t mla_decode_sparse_workspace_size(const mla_decode_params_t* p, int32_t topk_width, size_t* bytes);
