@@ -198,38 +198,64 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
 #pragma unroll
   for (int r = 0; r < 4; ++r) m[r] = -INFINITY, l[r] = 0.f;
 
+  // A block's K and V rows are loaded into registers one block ahead, so
+  // that their transfer overlaps the previous block's products: thread tid
+  // holds K chunks (key r, dims 4c .. 4c + 3) for idx = tid + 256 j and V
+  // chunks (keys 2 rp, 2 rp + 1, dims 4c .. 4c + 3) likewise.
+  constexpr int kKPer = kAKeys * (kAD / 4) / (64 * kWaves);        // 8
+  constexpr int kVPer = (kAKeys / 2) * (kAD / 4) / (64 * kWaves);  // 4
+  float4 kx[kKPer], vx0[kVPer], vx1[kVPer];
+  auto load_block = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int idx = tid + 64 * kWaves * j;
+      const int r = idx / (kAD / 4), c = idx % (kAD / 4), t = min(t0 + r, blk_last);
+      kx[j] = 4 * c < a.dn ? reinterpret_cast<const float4*>(a.kn + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dn)[c]
+                           : reinterpret_cast<const float4*>(a.kr + ((int64_t)b * a.Lcap + t) * a.dr)[c - a.dn / 4];
+    }
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int idx = tid + 64 * kWaves * j;
+      const int rp = idx / (kAD / 4), c = idx % (kAD / 4);
+      const int t = min(t0 + 2 * rp, blk_last), t1 = min(t0 + 2 * rp + 1, blk_last);
+      vx0[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c];
+      vx1[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t1) * a.H + h) * a.dv)[c];
+    }
+  };
+  if (blk_last >= 0) load_block(0);
+
   for (int t0 = 0; t0 <= blk_last; t0 += kAKeys) {
     __syncthreads();  // the previous block's readers are done
-    // K rows (hi, lo): key r, dims 4c .. 4c + 3
-    for (int idx = tid; idx < kAKeys * (kAD / 4); idx += 64 * kWaves) {
-      const int r = idx / (kAD / 4), c = idx % (kAD / 4), t = t0 + r;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t <= blk_last)
-        x = 4 * c < a.dn ? reinterpret_cast<const float4*>(a.kn + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dn)[c]
-                         : reinterpret_cast<const float4*>(a.kr + ((int64_t)b * a.Lcap + t) * a.dr)[c - a.dn / 4];
+    // K rows (hi, lo) and V transposed (hi, lo) into LDS; keys past the
+    // workgroup's last visible one were loaded clamped and are zeroed here.
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int idx = tid + 64 * kWaves * j;
+      const int r = idx / (kAD / 4), c = idx % (kAD / 4);
+      const float4 x = t0 + r <= blk_last ? kx[j] : make_float4(0.f, 0.f, 0.f, 0.f);
       uint32_t h0, l0, h1, l1;
       split_bf16x2(x.x, x.y, h0, l0);
       split_bf16x2(x.z, x.w, h1, l1);
       *reinterpret_cast<uint2*>(kh + r * kKRowB + 8 * c) = make_uint2(h0, h1);
       *reinterpret_cast<uint2*>(kl + r * kKRowB + 8 * c) = make_uint2(l0, l1);
     }
-    // V transposed (hi, lo): keys 2 rp, 2 rp + 1 and dims 4c .. 4c + 3
-    for (int idx = tid; idx < (kAKeys / 2) * (kAD / 4); idx += 64 * kWaves) {
-      const int rp = idx / (kAD / 4), c = idx % (kAD / 4), t = t0 + 2 * rp;
-      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-      if (t <= blk_last) x0 = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c];
-      if (t + 1 <= blk_last)
-        x1 = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t + 1) * a.H + h) * a.dv)[c];
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int idx = tid + 64 * kWaves * j;
+      const int rp = idx / (kAD / 4), c = idx % (kAD / 4);
+      const float4 x0 = t0 + 2 * rp <= blk_last ? vx0[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x1 = t0 + 2 * rp + 1 <= blk_last ? vx1[j] : make_float4(0.f, 0.f, 0.f, 0.f);
       const float v0[4] = {x0.x, x0.y, x0.z, x0.w}, v1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int q = 0; q < 4; ++q) {
         uint32_t hw, lw;
-        split_bf16x2(v0[j], v1[j], hw, lw);
-        *reinterpret_cast<uint32_t*>(vth + (4 * c + j) * kVRowB + 4 * rp) = hw;
-        *reinterpret_cast<uint32_t*>(vtl + (4 * c + j) * kVRowB + 4 * rp) = lw;
+        split_bf16x2(v0[q], v1[q], hw, lw);
+        *reinterpret_cast<uint32_t*>(vth + (4 * c + q) * kVRowB + 4 * rp) = hw;
+        *reinterpret_cast<uint32_t*>(vtl + (4 * c + q) * kVRowB + 4 * rp) = lw;
       }
     }
     __syncthreads();
+    if (t0 + kAKeys <= blk_last) load_block(t0 + kAKeys);  // in flight during this block's products
 
     // S = Q K^T for keys t0 + 16 nt + li (lane) and queries iw + 4 g + r
     f32x4 sc[2];
