@@ -293,7 +293,10 @@ typedef struct {
 } mla_prefill_params_t;
 
 /* Workspace bytes of mla_prefill_paged: 4 * B * max_blocks_per_seq *
- * page_block * (H * (d_nope + d_v) + d_rope), each part rounded up to 256.
+ * page_block * (H * (d_nope + d_v) + d_rope) for the rebuilt keys and
+ * values, plus, when the matrix-core attention splits each query block's
+ * keys into S ranges (S chosen from B, Sq, H and the capacity), 4 * B * Sq *
+ * H * S * (d_v + 1) for the partial results; each part rounded up to 256.
  * Host scalars only. */
 mla_status_t mla_prefill_workspace_size(const mla_prefill_params_t* p, size_t* bytes);
 /* Errors: see the conventions above; every check runs before any launch. */

@@ -200,18 +200,35 @@ mla_status_t check_prefill(const mla_prefill_params_t* p) {
   return MLA_OK;
 }
 
+struct PrefillLayout {
+  int splits;
+  int64_t kn_off, kr_off, v_off, part_o_off, part_lse_off;
+  size_t total;
+};
+
 // Workspace of the prefill: rebuilt no-RoPE keys, RoPE keys and values of
-// every token slot a sequence can hold, fp32.
-size_t prefill_workspace(const mla_prefill_params_t* p, int64_t* kn_off, int64_t* kr_off, int64_t* v_off) {
-  const int64_t slots = (int64_t)p->batch * p->max_blocks_per_seq * p->page_block;
-  const int64_t H = p->dims.num_heads;
+// every token slot a sequence can hold (fp32), then, when the attention
+// splits each query block's keys, the per-split partial outputs and
+// log-sum-exps.
+PrefillLayout prefill_workspace(const mla_prefill_params_t* p) {
+  PrefillLayout w{};
+  const int64_t Lcap = (int64_t)p->max_blocks_per_seq * p->page_block;
+  const int64_t slots = (int64_t)p->batch * Lcap;
+  const int64_t H = p->dims.num_heads, N = (int64_t)p->batch * p->q_per_seq;
+  w.splits = mla::prefill_attn_splits(p->batch, p->q_per_seq, p->dims.num_heads, Lcap, p->dims.d_nope,
+                                      p->dims.d_rope, p->dims.d_v);
   const int64_t kn = slots * H * p->dims.d_nope * 4, kr = slots * p->dims.d_rope * 4;
   const int64_t v = slots * H * p->dims.d_v * 4;
+  const int64_t po = w.splits > 1 ? N * H * w.splits * p->dims.d_v * 4 : 0;
+  const int64_t pl = w.splits > 1 ? N * H * w.splits * 4 : 0;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  if (kn_off) *kn_off = 0;
-  if (kr_off) *kr_off = up(kn);
-  if (v_off) *v_off = up(kn) + up(kr);
-  return (size_t)(up(kn) + up(kr) + up(v));
+  w.kn_off = 0;
+  w.kr_off = up(kn);
+  w.v_off = w.kr_off + up(kr);
+  w.part_o_off = w.v_off + up(v);
+  w.part_lse_off = w.part_o_off + up(po);
+  w.total = (size_t)(w.part_lse_off + up(pl));
+  return w;
 }
 
 }  // namespace
@@ -358,7 +375,7 @@ mla_status_t mla_prefill_workspace_size(const mla_prefill_params_t* p, size_t* b
   if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
   mla_status_t st = check_prefill(p);
   if (st) return st;
-  *bytes = prefill_workspace(p, nullptr, nullptr, nullptr);
+  *bytes = prefill_workspace(p).total;
   return ok();
 }
 
@@ -379,10 +396,10 @@ mla_status_t mla_prefill_paged(const mla_prefill_params_t* p, void* stream) {
       return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
   }
   if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
-  int64_t kn_off, kr_off, v_off;
-  const size_t need = prefill_workspace(p, &kn_off, &kr_off, &v_off);
-  if (p->workspace_bytes < need)
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", need, p->workspace_bytes);
+  const PrefillLayout w = prefill_workspace(p);
+  if (p->workspace_bytes < w.total)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
+                p->workspace_bytes);
   mla::PrefillArgs a{};
   a.B = p->batch;
   a.Sq = p->q_per_seq;
@@ -404,9 +421,12 @@ mla_status_t mla_prefill_paged(const mla_prefill_params_t* p, void* stream) {
   a.seq_lens = p->seq_lens;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   char* ws = static_cast<char*>(p->workspace);
-  a.kn = reinterpret_cast<float*>(ws + kn_off);
-  a.kr = reinterpret_cast<float*>(ws + kr_off);
-  a.v = reinterpret_cast<float*>(ws + v_off);
+  a.kn = reinterpret_cast<float*>(ws + w.kn_off);
+  a.kr = reinterpret_cast<float*>(ws + w.kr_off);
+  a.v = reinterpret_cast<float*>(ws + w.v_off);
+  a.splits = w.splits;
+  a.part_o = w.splits > 1 ? reinterpret_cast<float*>(ws + w.part_o_off) : nullptr;
+  a.part_lse = w.splits > 1 ? reinterpret_cast<float*>(ws + w.part_lse_off) : nullptr;
   a.out = p->out;
   a.lse = p->lse;
   const hipError_t e = mla::launch_prefill(a, p->kv_format, static_cast<hipStream_t>(stream));

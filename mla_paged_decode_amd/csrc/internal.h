@@ -141,6 +141,9 @@ struct PrefillArgs {
   float* v;                   // workspace: [B][Lcap][H][dv]
   float* out;                 // [B*Sq][H][dv]
   float* lse;                 // [B*Sq][H] or null
+  int splits;                 // matrix-core attention: key ranges per query block (1: none)
+  float* part_o;              // workspace, splits > 1: [B*Sq][H][splits][dv], normalised
+  float* part_lse;            // workspace, splits > 1: [B*Sq][H][splits]
 };
 bool prefill_supported(int dc, int dr, int dn, int dv);
 hipError_t launch_prefill(const PrefillArgs& a, int fmt, hipStream_t s);
@@ -149,6 +152,9 @@ bool prefill_expand_mfma_supported(const PrefillArgs& a);
 hipError_t launch_prefill_expand_mfma(const PrefillArgs& a, int fmt, hipStream_t s);
 // The causal attention on the matrix cores: keys and values 256 wide.
 bool prefill_attn_mfma_supported(const PrefillArgs& a);
+// Key ranges per query block of the matrix-core attention (host only; 1 if
+// that kernel does not apply): enough workgroups to fill the chip.
+int prefill_attn_splits(int B, int Sq, int H, int64_t Lcap, int dn, int dr, int dv);
 hipError_t launch_prefill_attn_mfma(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -9,6 +9,7 @@
 // are decoded from the cache row into a bf16 tile in LDS (the A operand).
 // bf16, fp8 and fp4 latents are exact in bf16; an f32 latent is split into
 // bf16 hi + lo parts, two products per k-step, as the fp32 projections do.
+#include <algorithm>
 #include <cmath>
 
 #include "decode_common.h"
@@ -163,11 +164,17 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
   const int h = blockIdx.y;
   const int nqb = (a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves);
-  const int b = blockIdx.x / nqb;
-  const int iw = (blockIdx.x % nqb) * kAQ * kWaves + kAQ * wave;  // the wave's first query
+  const int split = blockIdx.x % a.splits, qblk = blockIdx.x / a.splits;
+  const int b = qblk / nqb, qb = qblk % nqb;
+  const int iw = qb * kAQ * kWaves + kAQ * wave;  // the wave's first query
   const int L = (int)min((int64_t)max(a.seq_lens[b], 0), a.Lcap);
-  const int ig_end = min(a.Sq, (blockIdx.x % nqb + 1) * kAQ * kWaves);
-  const int blk_last = min(L - 1, L - a.Sq + ig_end - 1);  // the workgroup's last visible key
+  const int ig_end = min(a.Sq, (qb + 1) * kAQ * kWaves);
+  // Keys the workgroup's queries see: [0, n_keys); this split takes
+  // [k_begin, blk_last] of them, a whole number of key blocks.
+  const int n_keys = max(0, min(L, L - a.Sq + ig_end));
+  const int chunk = ((n_keys + a.splits - 1) / a.splits + kAKeys - 1) / kAKeys * kAKeys;
+  const int k_begin = split * chunk;
+  const int blk_last = min(n_keys, k_begin + chunk) - 1;  // this split's last key
 
   // A operand: query row iw + li, dims 32 ks + 8 g .. + 7, as hi and lo.
   bf16x8 qh[kAD / 32], ql[kAD / 32];
@@ -222,9 +229,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       vx1[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t1) * a.H + h) * a.dv)[c];
     }
   };
-  if (blk_last >= 0) load_block(0);
+  if (k_begin <= blk_last) load_block(k_begin);
 
-  for (int t0 = 0; t0 <= blk_last; t0 += kAKeys) {
+  for (int t0 = k_begin; t0 <= blk_last; t0 += kAKeys) {
     __syncthreads();  // the previous block's readers are done
     // K rows (hi, lo) and V transposed (hi, lo) into LDS; keys past the
     // workgroup's last visible one were loaded clamped and are zeroed here.
@@ -326,18 +333,46 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
     }
   }
 
-  // out[query iw + 4 g + r][16 d + li] = O / l; lse by lane li = 0
+  // out[query iw + 4 g + r][16 d + li] = O / l and its lse (lane li = 0);
+  // with several splits, this split's normalised partial and lse instead.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = iw + 4 * g + r;
     if (i >= a.Sq) continue;
     const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
-    float* dst = a.out + (((int64_t)b * a.Sq + i) * a.H + h) * a.dv;
+    const float ls = l[r] > 0.f ? (m[r] + log2f(l[r])) * 0.693147180559945309f : -INFINITY;
+    const int64_t row = ((int64_t)b * a.Sq + i) * a.H + h;
+    if (a.splits == 1) {
+      float* dst = a.out + row * a.dv;
 #pragma unroll
-    for (int d = 0; d < kAD / 16; ++d) dst[16 * d + li] = o[d][r] * inv;
-    if (a.lse && li == 0)
-      a.lse[((int64_t)b * a.Sq + i) * a.H + h] = l[r] > 0.f ? (m[r] + log2f(l[r])) * 0.693147180559945309f : -INFINITY;
+      for (int d = 0; d < kAD / 16; ++d) dst[16 * d + li] = o[d][r] * inv;
+      if (a.lse && li == 0) a.lse[row] = ls;
+    } else {
+      float* dst = a.part_o + (row * a.splits + split) * a.dv;
+#pragma unroll
+      for (int d = 0; d < kAD / 16; ++d) dst[16 * d + li] = o[d][r] * inv;
+      if (li == 0) a.part_lse[row * a.splits + split] = ls;
+    }
   }
+}
+
+// Merge of the key splits (log-sum-exp rule): one workgroup per (query,
+// head), thread d owns output column d.
+__global__ __launch_bounds__(kAD) void prefill_merge_kernel(PrefillArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * a.H + blockIdx.y;
+  const float* lse = a.part_lse + row * a.splits;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, lse[s]);
+  float z = 0.f, acc = 0.f;
+  const int d = threadIdx.x;
+  if (mx != -INFINITY)
+    for (int s = 0; s < a.splits; ++s) {
+      const float w = lse[s] == -INFINITY ? 0.f : expf(lse[s] - mx);
+      z += w;
+      if (d < a.dv) acc = fmaf(w, a.part_o[(row * a.splits + s) * a.dv + d], acc);
+    }
+  if (d < a.dv) a.out[row * a.dv + d] = z > 0.f ? acc / z : 0.f;
+  if (a.lse && d == 0) a.lse[row] = z > 0.f ? mx + logf(z) : -INFINITY;
 }
 
 template <int FMT>
@@ -361,10 +396,31 @@ bool prefill_attn_mfma_supported(const PrefillArgs& a) {
   return a.dn + a.dr == kAD && a.dv == kAD && a.dn % 4 == 0;
 }
 
+// One 85-KB workgroup per CU: 256 run at once on MI355X.  The split count
+// minimises the rounds of the grid per unit of work (ties go to fewer
+// splits), with at least 128 keys of capacity per split.
+int prefill_attn_splits(int B, int Sq, int H, int64_t Lcap, int dn, int dr, int dv) {
+  if (dn + dr != kAD || dv != kAD || dn % 4) return 1;
+  constexpr int kSlots = 256;
+  const int64_t wgs = (int64_t)B * ((Sq + kAQ * kWaves - 1) / (kAQ * kWaves)) * H;
+  const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(16, Lcap / 128));
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= smax; ++sp) {
+    const double cost = (double)((wgs * sp + kSlots - 1) / kSlots) / sp;
+    if (cost < best_cost - 1e-9) best_cost = cost, best = sp;
+  }
+  return best;
+}
+
 hipError_t launch_prefill_attn_mfma(const PrefillArgs& a, hipStream_t s) {
-  if (!prefill_attn_mfma_supported(a)) return hipErrorInvalidValue;
+  if (!prefill_attn_mfma_supported(a) || a.splits < 1 || (a.splits > 1 && (!a.part_o || !a.part_lse)))
+    return hipErrorInvalidValue;
   const unsigned qb = (unsigned)((a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves));
-  prefill_attn_mfma_kernel<<<dim3((unsigned)a.B * qb, (unsigned)a.H), 64 * kWaves, 0, s>>>(a);
+  prefill_attn_mfma_kernel<<<dim3((unsigned)a.B * qb * (unsigned)a.splits, (unsigned)a.H), 64 * kWaves, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  prefill_merge_kernel<<<dim3((unsigned)(a.B * a.Sq), (unsigned)a.H), kAD, 0, s>>>(a);
   return hipGetLastError();
 }
 

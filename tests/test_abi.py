@@ -231,6 +231,12 @@ def test_prefill_rejects_before_launch(kw, status, fragment):
 def test_prefill_workspace_size_and_empty_batch():
     p = prefill_params()
     slots = 2 * 4 * 64
-    want = 4 * slots * 20 * 192 + 4 * slots * 64 + 4 * slots * 20 * 256  # every part a multiple of 256 here
-    assert mla.mla_prefill_workspace_size(p) == want
+    kv = 4 * slots * 20 * 192 + 4 * slots * 64 + 4 * slots * 20 * 256  # every part a multiple of 256 here
+    # 2 sequences x 1 block of 64 queries x 20 heads = 40 workgroups: two key
+    # splits (capacity 256 tokens allows at most 2), with their partials
+    splits, n = 2, 2 * 64
+    assert mla.mla_prefill_workspace_size(p) == kv + 4 * n * 20 * splits * 256 + 4 * n * 20 * splits
+    # narrow heads run the vector-ALU attention: no partials
+    narrow = prefill_params(dims=Dims(20, 512, 64, 128, 128))
+    assert mla.mla_prefill_workspace_size(narrow) == 4 * slots * 20 * 128 * 2 + 4 * slots * 64
     mla.mla_prefill_paged(prefill_params(batch=0, q=0, out=0, workspace=0), stream=0)  # no-op, no launch
