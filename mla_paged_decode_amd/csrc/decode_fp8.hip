@@ -17,11 +17,12 @@
 //      and swizzled bf16 tile of the bf16 kernel.  QK^T and the softmax are
 //      split by 16-row blocks (one per wave); PV is split by column blocks,
 //      each wave covering all rows, with P handed over through LDS.
-// One workgroup of ceil(R / 16) waves (at least 2) runs per CU, 256 balanced
-// workers; with at most two row blocks two run per CU (512 workers, a
-// shallower ring).  The per-tile cost is bound by LDS instructions (about 8 cycles
-// per wave instruction), which the column split keeps to one transposed
-// read per V chunk per tile.
+// Up to four row blocks a workgroup has four waves, else eight.  One
+// workgroup runs per CU (256 balanced workers); with at most two row blocks
+// two run per CU (512 workers, a shallower ring, at most 256 registers per
+// wave).  The per-tile cost is bound by LDS instructions (about 8 cycles per
+// wave instruction), which the column split keeps to one transposed read
+// per V chunk per tile.
 //
 // Online softmax, the rescale-free main loop and the partial layout follow
 // the bf16 kernel: per row a reference maximum kept while scores stay
@@ -57,8 +58,8 @@ struct RawRow {
   static constexpr int kRawBuf = kRawInst * 1024;           // raw buffer stride
 };
 // Raw ring depth: 4 buffers (3 tiles in flight) for one workgroup per CU;
-// with at most two row blocks (two waves) two workgroups share a CU, each
-// with 2 buffers (1 tile in flight), so that all four SIMDs have a wave.
+// with at most two row blocks two workgroups share a CU, each with 2
+// buffers (1 tile in flight), so that every SIMD has two waves.
 template <int RB>
 constexpr int raw_depth() { return RB <= 2 ? 2 : 4; }
 // Converted bf16 tile, as in the bf16 kernel: latent rows (56 chunks) then
@@ -208,7 +209,7 @@ __device__ __forceinline__ void decode_tile(const lds_char* raw, lds_char* tile,
 // the bf16 kernel's sparse mode; the slots' visibility masks ride with the
 // raw ring in LDS.
 template <int FMT, int NW, int RB, bool SPARSE = false>
-__global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * NW, raw_depth<RB>() == 2 ? 2 : 1) void decode_fp8_kernel(DecodeArgs a) {
   constexpr int kRawBuf = RawRow<FMT>::kRawBuf;
   constexpr int kRaw = raw_depth<RB>();
   using Raw = RawStaging<FMT, NW>;
@@ -537,11 +538,13 @@ __global__ __launch_bounds__(64 * NW) void decode_fp8_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// One workgroup per CU.  Up to four row blocks: one wave per row block (at
-// least two), each with a whole SIMD's registers.  Five to eight row blocks:
-// eight waves, two per SIMD, of which the first RB own row blocks; all eight
-// split the PV columns, which keeps the SIMDs' matrix work close to even.
-// Two workgroups per CU where the ring is 2 deep (at most two row blocks).
+// Up to four row blocks: four waves, of which the first RB own row blocks
+// (one workgroup per CU, a whole SIMD's registers per wave, for three or
+// four row blocks; two workgroups per CU for one or two).  Five to eight row
+// blocks: eight waves, two per SIMD.  All waves split the PV columns, which
+// keeps the SIMDs' matrix work close to even.  Measured on 64 sequences of
+// 16k fp8 tokens with one query token: two waves per workgroup and two
+// workgroups per CU 302 us, four waves 231 us.
 int fp8_rows_workers(int R) { return (R + 15) / 16 <= 2 ? 512 : 256; }
 
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32) {
@@ -554,7 +557,7 @@ hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
   switch ((a.R + 15) / 16) {
 #define MLA_CASE(N) \
   case N:           \
-    decode_fp8_kernel<FMT, (N < 2 ? 2 : N <= 4 ? N : 8), N><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); \
+    decode_fp8_kernel<FMT, (N <= 4 ? 4 : 8), N><<<units, 64 * (N <= 4 ? 4 : 8), 0, s>>>(a); \
     break;
     MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
 #undef MLA_CASE
@@ -580,7 +583,7 @@ hipError_t launch_rows_sparse(const DecodeArgs& a, hipStream_t s) {
   switch ((a.R + 15) / 16) {
 #define MLA_CASE(N) \
   case N:           \
-    decode_fp8_kernel<FMT, (N < 2 ? 2 : N <= 4 ? N : 8), N, true><<<units, 64 * (N < 2 ? 2 : N <= 4 ? N : 8), 0, s>>>(a); \
+    decode_fp8_kernel<FMT, (N <= 4 ? 4 : 8), N, true><<<units, 64 * (N <= 4 ? 4 : 8), 0, s>>>(a); \
     break;
     MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
 #undef MLA_CASE
