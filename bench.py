@@ -356,8 +356,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
-              f"multi-GPU path: sequences would shard across GPUs with no exchange, see the design notes.",
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
+              f"multi-GPU path; sequences would shard across GPUs with no exchange.",
               file=sys.stderr)
         return 2
 
