@@ -65,7 +65,7 @@ def lse_tol(kernel):
 
 def skip_unsupported(kernel, wl):
     if kernel == MFMA and wl.kv_format == "f32":
-        pytest.skip("the matrix-core kernel takes bf16 and fp8 caches")
+        pytest.skip("the matrix-core kernels take bf16, fp8 and fp4 caches, not f32")
 
 
 def run_step(inp, *, kernel, num_splits=0, q_abs_dtype=None, q_abs=None):
