@@ -304,11 +304,13 @@ def prefill_timing(inp, dev, chunk: int, n_seqs: int, reps: int):
     g = torch.Generator().manual_seed(9)
     q = torch.randn((B * chunk, H, wl.d_nope + wl.d_rope), generator=g).cuda()
     out = torch.empty((B * chunk, H, wl.d_v), device="cuda")
+    bt = dev.block_table[:B].contiguous()  # kept alive: the struct holds raw pointers
+    sl = dev.seq_lens[:B].contiguous()
     params = mla.make_prefill_params(
         dims=dev.dims, batch=B, q_per_seq=chunk, q=q, w_kv_b=dev.w_kv_b, kv_pool=dev.kv_pool,
         kv_format=dev.kv_format, num_pages=dev.kv_pool.shape[0], page_block=dev.page_block,
-        block_table=dev.block_table[:B].contiguous(), max_blocks_per_seq=dev.block_table.shape[1],
-        seq_lens=dev.seq_lens[:B].contiguous(), softmax_scale=dev.softmax_scale, out=out)
+        block_table=bt, max_blocks_per_seq=dev.block_table.shape[1], seq_lens=sl,
+        softmax_scale=dev.softmax_scale, out=out)
     nbytes = mla.mla_prefill_workspace_size(params)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
