@@ -1,23 +1,28 @@
 """Benchmark: MLA decode over a paged latent cache on one MI355X.
 
 One step = one decode step of one attention layer for the whole batch:
-mla_absorb_q -> mla_decode_paged (plan, split-KV kernel, LSE merge) ->
+mla_absorb_q -> mla_decode_paged (split-KV attention and LSE merge) ->
 mla_out_proj, on synthetic seeded inputs already resident in HBM.  The
 timed steps are replayed from HIP graphs (as a serving loop would run
 them); the per-kernel roofline comes from a second, eager pass.
 
-The default workload is one GLM-4.7-Flash layer: batch 32, 20 heads, 4096
-cached tokens per sequence, bf16 latent cache (512 + 64 values per token),
-page block 64, permuted block table.  Its 151 MB cache would sit in the
-256 MB Infinity Cache if one buffer were reused, so the step cycles through
-several copies of the cache (as successive layers would), each at its own
-address, totalling more than the cache size.
+The default workload is the largest one that the metric's target names:
+256 sequences of one GLM-4.7-Flash layer (20 heads, bf16 latent cache of
+512 + 64 values per token, page block 128), context lengths uniform in
+[512, 8192], about 10% of block-table entries on a shared prefix.  The same
+JSON line carries sub-records for the long-context workload (4 sequences,
+65,536 to 202,752 tokens; balanced split and its literal 32 chunks) and the
+fp8 cache with 4 MTP query tokens, each with its attention-kernel and
+decode-call (merge included) fractions of the 8 TB/s HBM peak.  A cache
+smaller than 4x the 256 MB Infinity Cache is cycled through several copies,
+each at its own address, so that no step is served from it.
 
 Output: one JSON line with query-tokens/s for the whole step, the achieved
-HBM bandwidth of the decode call (latent bytes read / its average duration),
-the roofline of its dominant kernel, the split-KV attention kernel (latent
-bytes read / its average duration; HIP events the library records on the
-launch stream around that launch alone), and the CPU oracle timed on a
+HBM bandwidth of the decode call (latent bytes read / its average
+duration), the roofline of its dominant kernel (the split-KV attention
+kernel: latent bytes read / its average duration, HIP events the library
+records on the launch stream around that launch alone), MFMA utilisation
+from the committed counter summaries, and the C++ CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -42,33 +47,50 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, target_s: float):
-    """The oracle (unabsorbed, float64) on whole sequences of the same
-    workload until about target_s seconds of work have run."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    import oracle
+
+def cpu_baseline(wl, target_s: float):
+    """The C++ oracle (unabsorbed definition, double precision, OpenMP over
+    (sequence, head) pairs on every host core) on whole sequences of the same
+    workload, one sequence per call, until about target_s seconds of work
+    have run."""
+    import numpy as np
+
+    from oracle import native
     from synth import make_inputs
 
     inp = make_inputs(wl)
+    native.lib()
+    threads = native.max_threads()
     t0 = time.perf_counter()
     done = 0
     for b in range(wl.batch):
-        oracle.mla_decode(inp, seqs=[b])
+        native.mla_decode(inp, seqs=[b], threads=threads)
         done += 1
         if time.perf_counter() - t0 >= target_s:
             break
     dt = time.perf_counter() - t0
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     qtok = done * wl.q_per_seq
+    tokens = int(np.sum(inp.seq_lens[:done].astype(np.int64)))
     return {
         "value": qtok / dt,
         "unit": "query-tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {wl.batch} sequences of {wl.name} ({int(np.sum(inp.seq_lens[:done]))} "
-                  f"cached tokens), unabsorbed float64 numpy oracle, {dt:.1f} s",
+        "nproc": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "latent_gbs": tokens * inp.row_bytes / dt / 1e9,
+        "sample": f"{done} of {wl.batch} sequences of {wl.name} ({tokens} cached tokens), unabsorbed "
+                  f"double-precision C++ oracle (oracle/mla_oracle.cpp), {threads} OpenMP threads, {dt:.1f} s",
     }
 
 
@@ -106,11 +128,10 @@ def counter_file(workload: str, splits: int) -> str:
     return os.path.join(ROOT, "profiles", f"decode_mfma_{workload}{tag}_counters.txt")
 
 
-def counter_traffic(workload: str, splits: int = 0):
-    """HBM bytes per attention-kernel launch from the committed counter
-    summary of this workload (FETCH_SIZE + WRITE_SIZE, each scaled by the
-    same counter's reading for a plain copy of known size), or None if there
-    is none or the kernel has changed since the counters were taken."""
+def counter_summary(workload: str, splits: int = 0):
+    """The committed counter summary of this workload's attention kernel as
+    a dict of its "key: value" lines, or None if there is none or the kernel
+    has changed since the counters were taken."""
     path = counter_file(workload, splits)
     if not os.path.exists(path):
         return None
@@ -122,10 +143,43 @@ def counter_traffic(workload: str, splits: int = 0):
                 kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256") != kernel_source_digest():
         return None
+    return kv
+
+
+def counter_traffic(workload: str, splits: int = 0):
+    """HBM bytes per attention-kernel launch (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the same counter's reading for a plain copy of known size), or
+    None if the counters are missing or stale."""
+    kv = counter_summary(workload, splits)
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
     except (KeyError, ValueError):
         return None
+
+
+# MI355X: 8 XCDs, each with its own GRBM (so GRBM_GUI_ACTIVE sums 8 clocks
+# per GPU cycle), and 256 CUs x 4 SIMDs, each with one matrix core.
+N_XCD, N_SIMD = 8, 1024
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def mfma_utilisation(workload: str, splits: int = 0):
+    """Matrix-core utilisation of the attention kernel from the committed
+    counters: SQ_VALU_MFMA_BUSY_CYCLES / (GPU cycles x SIMDs), GPU cycles =
+    GRBM_GUI_ACTIVE / XCDs; also the executed bf16 MFMA flops
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) per dispatch.  None if the counters
+    are missing or stale."""
+    kv = counter_summary(workload, splits)
+    if not kv:
+        return None
+    try:
+        busy = float(kv["mfma_busy_cycles_per_dispatch"])
+        gui = float(kv["grbm_gui_active_per_dispatch"])
+        flops = float(kv["mfma_flops_executed_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+    return {"busy_frac": busy / (gui / N_XCD * N_SIMD), "flops_executed": flops,
+            "source": os.path.relpath(counter_file(workload, splits), ROOT)}
 
 
 def cache_write_timing(inp, dev, reps: int):
@@ -327,19 +381,96 @@ def prefill_timing(inp, dev, chunk: int, n_seqs: int, reps: int):
     pairs = float(sum(int(L - chunk + i + 1) for L in lens for i in range(chunk)))
     attn = 2.0 * pairs * H * (wl.d_nope + wl.d_rope + wl.d_v)
     tflops = (expand + attn) / (us * 1e-6) / 1e12
+    # Both contractions run on the bf16 matrix cores: the rebuild as one bf16
+    # product per term (bf16 weights and latent), the attention as three per
+    # term (hi * hi + hi * lo + lo * hi, for fp32-level accuracy).  The
+    # fraction counts the matrix-core flops so executed against the bf16 peak.
+    mfma_flops = expand + 3.0 * attn
     return {"sequences": B, "chunk": chunk, "context": [int(x) for x in lens], "us": us,
-            "flops": expand + attn, "tflops": tflops, "peak_fp32_vector_tflops": 157.3,
-            "frac": tflops / 157.3, "kernel": "simt_fp32"}
+            "flops": expand + attn, "flops_rebuild": expand, "flops_attention": attn, "tflops": tflops,
+            "mfma_flops_executed": mfma_flops, "peak_bf16_mfma_tflops": BF16_MFMA_PEAK_TFLOPS,
+            "frac": mfma_flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "kernel": "mfma"}
+
+
+def decode_timing(wl, splits: int, qd: int, kernel: int, reps: int, cache_bytes: float, warmup: int = 3):
+    """Eager decode calls on one workload: per call, the decode call
+    (mla_decode_paged: attention and merge; torch events around it) and the
+    attention kernel alone (HIP events the library records on the launch
+    stream).  Calls cycle through copies of the cache, each at its own
+    address, so that together they exceed the Infinity Cache."""
+    import numpy as np
+    import torch
+
+    import mla_paged_decode_amd as mla
+    from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
+    from synth import make_inputs
+
+    inp = make_inputs(wl)
+    mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
+    dev = DeviceBatch.upload(inp)
+    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel)
+    pool_bytes = dev.kv_pool.numel()
+    copies = max(1, math.ceil(cache_bytes / pool_bytes))
+    pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
+    step.absorb()
+    for i in range(warmup):
+        step.params.kv_pool = pools[i % copies].data_ptr()
+        step.decode()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(reps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        step.params.kv_pool = pools[i % copies].data_ptr()
+        e[0].record()
+        step.params.kernel_start_event, step.params.kernel_stop_event = e[2].cuda_event, e[3].cuda_event
+        step.decode()
+        e[1].record()
+    step.params.kernel_start_event = step.params.kernel_stop_event = None
+    torch.cuda.synchronize()
+    call_us = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e3
+    kern_us = sum(e[2].elapsed_time(e[3]) for e in evs) / reps * 1e3
+    latent = int(np.sum(inp.seq_lens.astype(np.int64))) * inp.row_bytes
+    used = mla.mla_decode_select_kernel(step.params)
+    rec = {
+        "workload": wl.name, "num_splits": splits, "batch": wl.batch, "q_per_seq": wl.q_per_seq,
+        "kv_format": wl.kv_format, "kernel": {1: "simt", 2: "mfma"}[used],
+        "q_abs": "f32" if qd == mla.MLA_F32 else "bf16", "cache_copies": copies,
+        "latent_bytes": latent, "unique_bytes": pool_bytes,
+        "attention_kernel_us": kern_us, "decode_call_us": call_us,
+        "attention_frac": latent / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "decode_frac": latent / (call_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "decode_query_tokens_per_s": wl.n_tokens / (call_us * 1e-6),
+        "traffic": counter_traffic(wl.name, splits),
+        "mfma": mfma_utilisation(wl.name, splits),
+    }
+    del step, pools, dev
+    torch.cuda.empty_cache()
+    return rec
+
+
+def parse_extra(spec: str):
+    out = []
+    for item in filter(None, (x.strip() for x in spec.split(","))):
+        name, _, sp = item.partition(":")
+        out.append((name, int(sp) if sp else None))
+    return out
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="glm_b32_h20_ctx4096_bf16")
-    ap.add_argument("--num-splits", type=int, default=None,
-                    help="split-KV chunks per sequence (0 = balanced; default: the workload's)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ragged_b256_h20_ctx512_8k_bf16")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="split-KV chunks per sequence (0 = balanced, the default; -1: the workload's own)")
+    ap.add_argument("--extra", default="long_b4_h20_ctx65k_203k_bf16:0,long_b4_h20_ctx65k_203k_bf16:32,"
+                                       "fp8_mtp4_b64_h20_ctx16k:0",
+                    help="comma-separated workload[:num_splits] sub-records (decode call and attention "
+                         "kernel, eager); empty: none")
+    ap.add_argument("--extra-reps", type=int, default=10)
     ap.add_argument("--kernel", choices=["auto", "simt", "mfma"], default="auto")
     ap.add_argument("--q-abs", choices=["auto", "bf16", "f32"], default="auto",
                     help="absorbed-query dtype fed to the attention kernel; auto: f32 (hi + lo bf16 "
@@ -373,15 +504,20 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     mla.lib()
     wl = WORKLOADS[args.workload]
-    splits = wl.num_splits if args.num_splits is None else args.num_splits
+    splits = wl.num_splits if args.num_splits < 0 else args.num_splits
     kernel = {"auto": mla.MLA_KERNEL_AUTO, "simt": mla.MLA_KERNEL_SIMT, "mfma": mla.MLA_KERNEL_MFMA}[args.kernel]
-    q_abs = args.q_abs if args.q_abs != "auto" else ("bf16" if wl.kv_format == "fp8_e4m3_e8m0" else "f32")
-    qd = mla.MLA_BF16 if q_abs == "bf16" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
 
+    def q_dtype(w):
+        q = args.q_abs if args.q_abs != "auto" else ("bf16" if w.kv_format == "fp8_e4m3_e8m0" else "f32")
+        return mla.MLA_BF16 if q == "bf16" and kernel != mla.MLA_KERNEL_SIMT else mla.MLA_F32
+
+    qd = q_dtype(wl)
     log(f"[bench] generating {wl.name}")
     inp = make_inputs(wl)
+    mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
     dev = DeviceBatch.upload(inp)
-    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel)
+    flags = mla.MLA_DECODE_ALLOW_BF16_QUERIES if qd == mla.MLA_BF16 and wl.kv_format in ("bf16", "f32") else 0
+    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel, flags=flags)
     pool_bytes = dev.kv_pool.numel()
     copies = max(1, math.ceil(args.cache_bytes / pool_bytes))
     pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
@@ -447,8 +583,8 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     # Timed region 2 (the roofline): eager steps; per step the decode call
-    # (plan + attention + merge) and, recorded by the library on the launch
-    # stream, the attention kernel alone.
+    # (attention + merge) and, recorded by the library on the launch stream,
+    # the attention kernel alone.
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     for e in evs:
         for x in e:
@@ -468,6 +604,7 @@ def main() -> int:
         f"{kernel_avg_s * 1e6:.1f} us ({achieved:.0f} GB/s)")
 
     cache_write = cache_write_timing(inp, dev, args.steps)
+    log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
     sparse = None
     if args.sparse_topk > 0:
         # about 512 workgroups (measured: GLM batch best at 16 chunks, 256 sequences at 2-4)
@@ -476,16 +613,34 @@ def main() -> int:
         sparse = sparse_timing(inp, dev, step.q_abs, qd, args.sparse_topk, chunks, min(args.steps, 10))
         log(f"[bench] sparse decode over {args.sparse_topk} listed tokens per query: "
             f"{sparse['attention_kernel_us']:.1f} us ({sparse['gbs']:.0f} GB/s)")
-    log(f"[bench] mla_cache_write of {cache_write['rows']} new rows: {cache_write['us']:.1f} us")
-
     fp4 = fp4_timing(inp, dev, min(args.steps, 5))
     if fp4 is not None:
         log(f"[bench] fp4 cache copy: attention kernel {fp4['attention_kernel_us']:.1f} us ({fp4['gbs']:.0f} GB/s)")
-
     prefill = prefill_timing(inp, dev, args.prefill_chunk, 4, 3)
     if prefill is not None:
         log(f"[bench] prefill of {prefill['chunk']} new tokens on {prefill['sequences']} sequences: "
-            f"{prefill['us'] / 1e3:.2f} ms ({prefill['tflops']:.1f} TFLOP/s fp32)")
+            f"{prefill['us'] / 1e3:.2f} ms ({prefill['tflops']:.1f} TFLOP/s algorithmic, "
+            f"{prefill['frac']:.3f} of the bf16 matrix-core peak)")
+    used = mla.mla_decode_select_kernel(step.params)
+    main_cfg = {
+        "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_per_seq": wl.q_per_seq,
+        "context": list(wl.lens), "page_block": wl.page_block, "kv_format": wl.kv_format,
+        "d_latent": wl.d_latent, "d_rope": wl.d_rope, "num_splits": splits,
+        "kernel": {1: "simt", 2: "mfma"}[used], "q_abs": "f32" if qd == mla.MLA_F32 else "bf16",
+        "cache_copies": copies,
+    }
+    del graphs, step, pools, dev
+    torch.cuda.empty_cache()
+
+    extras = []
+    for name, sp in parse_extra(args.extra):
+        w = WORKLOADS[name]
+        sp = w.num_splits if sp is None else sp
+        log(f"[bench] sub-record {name} num_splits={sp}")
+        rec = decode_timing(w, sp, q_dtype(w), kernel, args.extra_reps, args.cache_bytes)
+        log(f"[bench]   attention kernel {rec['attention_kernel_us']:.1f} us ({rec['attention_frac']:.3f} of 8 TB/s), "
+            f"decode call {rec['decode_call_us']:.1f} us ({rec['decode_frac']:.3f})")
+        extras.append(rec)
 
     base = None
     if not args.no_cpu_baseline:
@@ -493,7 +648,6 @@ def main() -> int:
         base = cpu_baseline(wl, args.cpu_seconds)
 
     qtok_s = q_tokens / (ms_per_step / 1e3)
-    used = mla.mla_decode_select_kernel(step.params)
     compute = "f32" if used == mla.MLA_KERNEL_SIMT else "bf16"
     line = {
         "metric": METRIC,
@@ -508,17 +662,12 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": compute,
         "data": "synthetic",
-        "config": {
-            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_per_seq": wl.q_per_seq,
-            "context": list(wl.lens), "page_block": wl.page_block, "kv_format": wl.kv_format,
-            "d_latent": wl.d_latent, "d_rope": wl.d_rope, "num_splits": splits,
-            "kernel": {1: "simt", 2: "mfma"}[used], "q_abs": "f32" if qd == mla.MLA_F32 else "bf16",
-            "cache_copies": copies,
-        },
+        "config": main_cfg,
         "hbm_gbs": achieved_call,
         "pct_of_8tbs": 100.0 * achieved_call / HBM_PEAK_GBS,
         "decode_call_us": decode_avg_s * 1e6,
         "attention_kernel_us": kernel_avg_s * 1e6,
+        "decode_frac": achieved_call / HBM_PEAK_GBS,
         "latent_bytes": latent_bytes,
         "unique_bytes": unique_bytes,
         "roofline": {
@@ -529,7 +678,9 @@ def main() -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": counter_traffic(wl.name, splits),
         },
+        "mfma": mfma_utilisation(wl.name, splits),
         "cpu_baseline": base,
+        "configs": extras,
         "cache_write": cache_write,
         "sparse_decode": sparse,
         "fp4_decode": fp4,

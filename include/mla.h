@@ -41,7 +41,8 @@
  *    block_table entries for logical pages [0, ceil(seq_len/page_block))
  *    must lie in [0, num_pages) and seq_lens must be in
  *    [0, max_blocks_per_seq * page_block].  Entries past a sequence's last
- *    page are never read.
+ *    page are never read.  mla_validate_tables checks host copies of both
+ *    tables against these ranges.
  */
 #ifndef LIBMLA_MLA_H
 #define LIBMLA_MLA_H
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
 
@@ -67,8 +68,10 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype_t;
  *                        2i in the low nibble of byte i), then one e4m3fn
  *                        scale byte per 16 values; value = e2m1 * e4m3
  *                        (288 B at 448 + 64: the model record's fp4 variant;
- *                        its scale format is this library's reading).  Decode
- *                        runs on the vector-ALU kernel. */
+ *                        its scale format is this library's reading).  With
+ *                        bf16 q_abs it decodes on the matrix cores (the row is
+ *                        expanded to bf16 in LDS, exactly); with f32 q_abs on
+ *                        the fp32 vector-ALU kernel. */
 typedef enum {
   MLA_KV_F32 = 0,
   MLA_KV_BF16 = 1,
@@ -155,7 +158,16 @@ typedef struct {
                                after it, before the merge kernel.  Both are
                                caller-owned; they time the dominant kernel
                                alone. */
+  uint32_t flags;           /* MLA_DECODE_* bits below; 0 by default */
 } mla_decode_params_t;
+
+/* Accept bf16 q_abs with a bf16 or f32 cache.  Without this bit such calls
+ * return MLA_ERR_UNSUPPORTED: absorbed queries rounded once to bf16 (and the
+ * softmax weights with them) measure up to 1.3e-2 of the output RMS on the
+ * 256-sequence ragged batch, beyond the 1e-2 match criterion for bf16
+ * caches; f32 q_abs (split into bf16 hi + lo products) measures ~2e-5.  The
+ * fp8 and fp4 caches take bf16 q_abs without it (their criterion is 5e-2). */
+#define MLA_DECODE_ALLOW_BF16_QUERIES 0x1u
 
 /* Workspace bytes mla_decode_paged needs for these parameters.  Reads only
  * host scalars (no pointers are dereferenced, no device is touched). */
@@ -198,11 +210,11 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
  * mla_decode_sparse_workspace_size.  Kernel: a matrix-core one (rows
  * gathered through the index list) when topk_width is a multiple of 32 (the
  * pages pad the list to 128) and either the cache is bf16 with num_heads <=
- * 64, or it is fp8 / fp4 (448 + 64 row) with bf16 q_abs and num_heads <= 128
- * (padding slots then contribute exact zeros, whatever the row they are
- * pointed at holds; on the bf16 kernel they read slot 0 of page 0, which
- * must then hold finite values, as a zero weight cannot cancel a NaN);
- * unless MLA_KERNEL_SIMT is asked for.  The fp32
+ * 64, or it is fp8 / fp4 (448 + 64 row) with bf16 q_abs and num_heads <= 128;
+ * unless MLA_KERNEL_SIMT is asked for.  On every kernel a padding slot
+ * contributes exactly nothing, whatever any cache row it could point at
+ * holds (NaN bytes included): its score is masked and its value operand is
+ * zeroed, not multiplied by a zero weight.  The fp32
  * vector-ALU one otherwise (MLA_KERNEL_MFMA where none applies is
  * rejected).  Errors: see the conventions above. */
 mla_status_t mla_decode_sparse_workspace_size(const mla_decode_params_t* p, int32_t topk_width, size_t* bytes);
@@ -301,6 +313,19 @@ typedef struct {
 mla_status_t mla_prefill_workspace_size(const mla_prefill_params_t* p, size_t* bytes);
 /* Errors: see the conventions above; every check runs before any launch. */
 mla_status_t mla_prefill_paged(const mla_prefill_params_t* p, void* stream);
+
+/* Host-side check of the device-trusted tables, for callers that hold (or
+ * copy back) host copies of them: seq_lens [batch] and block_table
+ * [batch][max_blocks_per_seq] are HOST pointers here.  Checks that every
+ * seq_lens[b] lies in [0, max_blocks_per_seq * page_block] and that every
+ * block_table entry a decode reads (logical pages [0, ceil(seq_lens[b] /
+ * page_block)) of each sequence) lies in [0, num_pages).  Returns MLA_OK,
+ * or MLA_ERR_INVALID_SHAPE with a message naming the first offending entry
+ * ("block_table[3][17]: expected 0..8191, got -1").  Touches no device and
+ * launches nothing; the decode calls do not run it themselves (they take
+ * the tables as device pointers and trust them, as stated at the top). */
+mla_status_t mla_validate_tables(int32_t batch, const int32_t* seq_lens, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, int64_t num_pages, int32_t page_block);
 
 const char* mla_status_string(mla_status_t status);
 /* Message of the last failed call on this thread ("" if none). */

@@ -21,11 +21,13 @@ __all__ = [
     "mla_decode_sparse_paged", "mla_decode_sparse_workspace_size",
     "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0", "MLA_KV_FP4_E2M1_E4M3",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
+    "MLA_DECODE_ALLOW_BF16_QUERIES", "mla_validate_tables",
 ]
 
 MLA_F32, MLA_BF16 = 0, 1
 MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0, MLA_KV_FP4_E2M1_E4M3 = 0, 1, 2, 3
 MLA_KERNEL_AUTO, MLA_KERNEL_SIMT, MLA_KERNEL_MFMA = 0, 1, 2
+MLA_DECODE_ALLOW_BF16_QUERIES = 0x1
 KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0,
              "fp4_e2m1_e4m3": MLA_KV_FP4_E2M1_E4M3}
 
@@ -76,6 +78,7 @@ class DecodeParams(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("kernel_start_event", ctypes.c_void_p),
         ("kernel_stop_event", ctypes.c_void_p),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -104,7 +107,7 @@ class PrefillParams(ctypes.Structure):
 
 
 # Must equal MLA_ABI_VERSION of include/mla.h (the parameter struct layout).
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -144,6 +147,8 @@ def lib() -> ctypes.CDLL:
         L.mla_status_string.restype = ctypes.c_char_p
         L.mla_last_error_message.argtypes = []
         L.mla_last_error_message.restype = ctypes.c_char_p
+        L.mla_validate_tables.argtypes = [i32, vp, vp, i32, ctypes.c_int64, i32]
+        L.mla_validate_tables.restype = st
         L.mla_abi_version.argtypes = []
         L.mla_abi_version.restype = i32
         if L.mla_abi_version() != ABI_VERSION:
@@ -226,7 +231,7 @@ def mla_cache_write(dims, n_rows: int, rows, slots, kv_pool, kv_format: int, num
 def make_decode_params(*, dims, batch, q_per_seq, q_abs, kv_pool, kv_format, num_pages,
                        page_block, block_table, max_blocks_per_seq, seq_lens, softmax_scale,
                        num_splits=0, kernel=MLA_KERNEL_AUTO, workspace=None, workspace_bytes=0,
-                       o_latent=None, lse=None, q_abs_dtype=None) -> DecodeParams:
+                       o_latent=None, lse=None, q_abs_dtype=None, flags=0) -> DecodeParams:
     """Fill the C parameter struct (pointers from tensors or raw ints)."""
     qd = q_abs_dtype if q_abs_dtype is not None else (
         _dtype_code(q_abs) if not isinstance(q_abs, int) and q_abs is not None else MLA_F32)
@@ -238,7 +243,20 @@ def make_decode_params(*, dims, batch, q_per_seq, q_abs, kv_pool, kv_format, num
         max_blocks_per_seq=max_blocks_per_seq, seq_lens=_ptr(seq_lens),
         softmax_scale=softmax_scale, num_splits=num_splits, kernel=kernel,
         workspace=_ptr(workspace), workspace_bytes=workspace_bytes,
-        o_latent=_ptr(o_latent), o_dtype=MLA_F32, lse=_ptr(lse))
+        o_latent=_ptr(o_latent), o_dtype=MLA_F32, lse=_ptr(lse), flags=flags)
+
+
+def mla_validate_tables(seq_lens, block_table, num_pages: int, page_block: int) -> None:
+    """Host-side range check of the tables (numpy arrays or CPU tensors):
+    seq_lens [B] int32 and block_table [B][max_blocks] int32.  Raises
+    MlaError naming the first entry out of range."""
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(seq_lens), dtype=np.int32)
+    bt = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    if bt.ndim != 2 or bt.shape[0] != sl.shape[0]:
+        raise ValueError(f"block_table: expected shape [{sl.shape[0]}, max_blocks], got {bt.shape}")
+    _check(lib().mla_validate_tables(sl.shape[0], sl.ctypes.data, bt.ctypes.data, bt.shape[1],
+                                     num_pages, page_block))
 
 
 def mla_decode_workspace_size(params: DecodeParams) -> int:

@@ -92,6 +92,14 @@ mla_status_t check_decode_scalars(const mla_decode_params_t* p) {
     return fail(MLA_ERR_UNSUPPORTED, "kernel: expected 0 (auto), 1 (simt) or 2 (mfma), got %d", (int)p->kernel);
   if (!std::isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_SHAPE, "softmax_scale: expected a finite value, got %g", (double)p->softmax_scale);
+  if (p->flags & ~MLA_DECODE_ALLOW_BF16_QUERIES)
+    return fail(MLA_ERR_UNSUPPORTED, "flags: expected a subset of 0x%x, got 0x%x", MLA_DECODE_ALLOW_BF16_QUERIES,
+                p->flags);
+  if (p->q_abs_dtype == MLA_BF16 && (p->kv_format == MLA_KV_BF16 || p->kv_format == MLA_KV_F32) &&
+      !(p->flags & MLA_DECODE_ALLOW_BF16_QUERIES))
+    return fail(MLA_ERR_UNSUPPORTED,
+                "q_abs_dtype: expected 0 (f32) with a bf16 or f32 cache, got 1 (bf16): single-rounded queries "
+                "exceed the 1e-2 match bound there; set MLA_DECODE_ALLOW_BF16_QUERIES in flags to accept them");
   return MLA_OK;
 }
 
@@ -236,6 +244,31 @@ PrefillLayout prefill_workspace(const mla_prefill_params_t* p) {
 extern "C" {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+mla_status_t mla_validate_tables(int32_t batch, const int32_t* seq_lens, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, int64_t num_pages, int32_t page_block) {
+  if (batch < 0) return fail(MLA_ERR_INVALID_SHAPE, "batch: expected >= 0, got %d", batch);
+  if (page_block < 1) return fail(MLA_ERR_INVALID_SHAPE, "page_block: expected >= 1, got %d", page_block);
+  if (max_blocks_per_seq < 1)
+    return fail(MLA_ERR_INVALID_SHAPE, "max_blocks_per_seq: expected >= 1, got %d", max_blocks_per_seq);
+  if (batch == 0) return ok();
+  if (!seq_lens) return fail(MLA_ERR_NULL_POINTER, "seq_lens: expected non-null, got NULL");
+  if (!block_table) return fail(MLA_ERR_NULL_POINTER, "block_table: expected non-null, got NULL");
+  const int64_t cap = (int64_t)max_blocks_per_seq * page_block;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 0 || L > cap)
+      return fail(MLA_ERR_INVALID_SHAPE, "seq_lens[%d]: expected 0..%lld, got %lld", b, (long long)cap, (long long)L);
+    const int64_t pages = (L + page_block - 1) / page_block;
+    for (int64_t i = 0; i < pages; ++i) {
+      const int64_t pg = block_table[(int64_t)b * max_blocks_per_seq + i];
+      if (pg < 0 || pg >= num_pages)
+        return fail(MLA_ERR_INVALID_SHAPE, "block_table[%d][%lld]: expected 0..%lld, got %lld", b, (long long)i,
+                    (long long)num_pages - 1, (long long)pg);
+    }
+  }
+  return ok();
+}
 
 const char* mla_status_string(mla_status_t s) {
   switch (s) {

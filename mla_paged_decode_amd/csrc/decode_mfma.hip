@@ -661,10 +661,27 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vbase[half][r] = b0 + 32 * (r ^ (xs >> 1));
       }
+      // Sparse mode: a padding slot's row (whatever it holds, NaN bytes
+      // included) must contribute nothing, and a zero weight cannot cancel a
+      // NaN, so its values are zeroed in the operand.  Element j of the lane's
+      // operand is token 4g + j (j < 4) or 16 + 4g + j - 4 of the tile.
+      u32x4 vkeep = {~0u, ~0u, ~0u, ~0u};
+      if constexpr (SPARSE) {
+        const uint32_t msk = mask_slot[(ring + it) & 1];
+        uint32_t k[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ta = (i < 2 ? 0 : 16) + 4 * g + (2 * i) % 4;
+          k[i] = (((msk >> ta) & 1u) ? 0x0000ffffu : 0u) | (((msk >> (ta + 1)) & 1u) ? 0xffff0000u : 0u);
+        }
+        vkeep = u32x4{k[0], k[1], k[2], k[3]};
+      }
       auto tile_v = [&](int d) {
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[0][d & 3] + 128 * (d >> 2)));
         const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase[1][d & 3] + 128 * (d >> 2)));
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (SPARSE) return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) & vkeep);
+        else return v;
       };
       constexpr int kPrefetch = HILO ? 4 : 8;
       bf16x8 vq[kPrefetch];

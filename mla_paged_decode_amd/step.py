@@ -59,7 +59,7 @@ class DecodeStep:
     three calls on the stream."""
 
     def __init__(self, dev: DeviceBatch, *, q_abs_dtype: int = MLA_F32, num_splits: int = 0,
-                 kernel: int = MLA_KERNEL_AUTO, with_lse: bool = True):
+                 kernel: int = MLA_KERNEL_AUTO, with_lse: bool = True, flags: int = 0):
         d = dev.dims
         N, H = dev.n_tokens, d.num_heads
         device = dev.q.device
@@ -75,7 +75,7 @@ class DecodeStep:
             page_block=dev.page_block, block_table=dev.block_table,
             max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens,
             softmax_scale=dev.softmax_scale, num_splits=num_splits, kernel=kernel,
-            o_latent=self.o_latent, lse=self.lse, q_abs_dtype=q_abs_dtype)
+            o_latent=self.o_latent, lse=self.lse, q_abs_dtype=q_abs_dtype, flags=flags)
         nbytes = mla_decode_workspace_size(self.params)
         self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.params.workspace = self.workspace.data_ptr()

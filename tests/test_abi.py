@@ -25,11 +25,11 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert mla.mla_abi_version() == 2
+    assert mla.mla_abi_version() == 3
 
 
 def test_row_bytes_match_page_figures(golden_dir):
@@ -87,6 +87,9 @@ def expect_error(fn, status, fragment):
     (dict(seq_lens=FAKE + 2), 4, "seq_lens: expected 4-byte alignment"),
     (dict(lse=FAKE + 1), 4, "lse: expected 4-byte alignment"),
     (dict(workspace_bytes=100), 5, "workspace_bytes: expected >= "),
+    (dict(q_abs_dtype=MLA_BF16), 3, "q_abs_dtype: expected 0 (f32) with a bf16 or f32 cache, got 1 (bf16)"),
+    (dict(q_abs_dtype=MLA_BF16, kv_format=MLA_KV_F32), 3, "set MLA_DECODE_ALLOW_BF16_QUERIES"),
+    (dict(flags=0x6), 3, "flags: expected a subset of 0x1, got 0x6"),
 ])
 def test_decode_rejects_before_launch(kw, status, fragment):
     p = params(**kw)
@@ -240,3 +243,64 @@ def test_prefill_workspace_size_and_empty_batch():
     narrow = prefill_params(dims=Dims(20, 512, 64, 128, 128))
     assert mla.mla_prefill_workspace_size(narrow) == 4 * slots * 20 * 128 * 2 + 4 * slots * 64
     mla.mla_prefill_paged(prefill_params(batch=0, q=0, out=0, workspace=0), stream=0)  # no-op, no launch
+
+
+def test_bf16_queries_on_a_bf16_cache_need_the_opt_in():
+    """Single-rounded queries on a bf16 / f32 cache are refused unless the
+    caller sets MLA_DECODE_ALLOW_BF16_QUERIES; the fp8 and fp4 caches take
+    them as they are.  (The checks run before any launch, so a call that
+    passes them reaches the launch and fails there without a GPU.)"""
+    p = params(q_abs_dtype=MLA_BF16)
+    expect_error(lambda: mla.mla_decode_workspace_size(p), 3, "MLA_DECODE_ALLOW_BF16_QUERIES")
+    expect_error(lambda: mla.mla_decode_select_kernel(p), 3, "MLA_DECODE_ALLOW_BF16_QUERIES")
+    for ok in (params(q_abs_dtype=MLA_BF16, flags=mla.MLA_DECODE_ALLOW_BF16_QUERIES),
+               params(dims=FP8, kv_format=MLA_KV_FP8_E4M3_E8M0, q_abs_dtype=MLA_BF16),
+               params(dims=FP8, kv_format=mla.MLA_KV_FP4_E2M1_E4M3, q_abs_dtype=MLA_BF16)):
+        assert mla.mla_decode_workspace_size(ok) > 0
+        assert mla.mla_decode_select_kernel(ok) == mla.MLA_KERNEL_MFMA
+
+
+def test_validate_tables_accepts_valid_tables():
+    import numpy as np
+    lens = np.array([0, 1, 64, 65, 128], dtype=np.int32)
+    bt = np.full((5, 2), -1, dtype=np.int32)
+    bt[1, 0] = 0
+    bt[2, 0] = 3
+    bt[3, :] = [1, 2]
+    bt[4, :] = [4, 0]
+    mla.mla_validate_tables(lens, bt, num_pages=5, page_block=64)
+    mla.mla_validate_tables(np.zeros(0, np.int32), np.zeros((0, 1), np.int32), num_pages=1, page_block=16)
+
+
+@pytest.mark.parametrize("case,fragment", [
+    ("len_negative", "seq_lens[1]: expected 0..128, got -1"),
+    ("len_too_long", "seq_lens[2]: expected 0..128, got 129"),
+    ("page_negative", "block_table[3][1]: expected 0..4, got -1"),
+    ("page_too_big", "block_table[0][0]: expected 0..4, got 5"),
+])
+def test_validate_tables_names_the_bad_entry(case, fragment):
+    import numpy as np
+    lens = np.array([10, 5, 100, 70], dtype=np.int32)
+    bt = np.array([[0, -1], [1, -1], [2, 3], [4, 0]], dtype=np.int32)
+    if case == "len_negative":
+        lens[1] = -1
+    elif case == "len_too_long":
+        lens[2] = 129
+    elif case == "page_negative":
+        bt[3, 1] = -1
+    else:
+        bt[0, 0] = 5
+    expect_error(lambda: mla.mla_validate_tables(lens, bt, num_pages=5, page_block=64), 2, fragment)
+    # entries past a sequence's last page are never read, so they may hold anything
+    bt2 = np.array([[0, 99], [1, -7], [2, 3], [4, 0]], dtype=np.int32)
+    mla.mla_validate_tables(np.array([10, 5, 100, 70], np.int32), bt2, num_pages=5, page_block=64)
+
+
+def test_synthetic_workload_tables_are_valid():
+    """Every workload's generated tables pass the validator (the inputs the
+    GPU tests and the benchmark use)."""
+    from synth import WORKLOADS, make_inputs
+    for name, wl in WORKLOADS.items():
+        small = wl.with_(batch=min(wl.batch, 4), lens=("fixed", tuple([37, 4096, 1, 0][:min(wl.batch, 4)])))
+        inp = make_inputs(small)
+        mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], small.page_block)

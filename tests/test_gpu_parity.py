@@ -68,12 +68,12 @@ def skip_unsupported(kernel, wl):
         pytest.skip("the matrix-core kernels take bf16, fp8 and fp4 caches, not f32")
 
 
-def run_step(inp, *, kernel, num_splits=0, q_abs_dtype=None, q_abs=None):
+def run_step(inp, *, kernel, num_splits=0, q_abs_dtype=None, q_abs=None, flags=0):
     from mla_paged_decode_amd import MLA_F32
     from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
     dev = DeviceBatch.upload(inp)
     step = DecodeStep(dev, kernel=kernel, num_splits=num_splits,
-                      q_abs_dtype=MLA_F32 if q_abs_dtype is None else q_abs_dtype)
+                      q_abs_dtype=MLA_F32 if q_abs_dtype is None else q_abs_dtype, flags=flags)
     step.o_latent.fill_(float("nan"))
     step.lse.fill_(float("nan"))
     step.out.fill_(float("nan"))
@@ -372,56 +372,85 @@ def test_page_layout_invariance_and_determinism(kernel):
 # ---------------------------------------------- full-size workloads --
 
 FULL = [
-    # (workload, sequences checked against the oracle, heads checked)
-    ("glm_b32_h20_ctx4096_bf16", list(range(32)), None),
-    ("long_b4_h20_ctx65k_203k_bf16", [0, 1, 2, 3], [0, 7, 19]),
-    ("ragged_b256_h20_ctx512_8k_bf16", list(range(0, 256, 8)) + [255], None),
-    ("fp8_mtp4_b64_h20_ctx16k", list(range(0, 64, 8)) + [63], None),
+    # (workload, split mode, sequences checked against the oracle); every
+    # head of every checked sequence is compared.  The long-context workload
+    # runs both in its literal 32 chunks and in the balanced mode the
+    # benchmark times.
+    ("glm_b32_h20_ctx4096_bf16", 0, list(range(32))),
+    ("long_b4_h20_ctx65k_203k_bf16", 0, [0, 1, 2, 3]),
+    ("long_b4_h20_ctx65k_203k_bf16", 32, [0, 1, 2, 3]),
+    ("ragged_b256_h20_ctx512_8k_bf16", 0, list(range(0, 256, 8)) + [255]),
+    ("fp8_mtp4_b64_h20_ctx16k", 0, list(range(0, 64, 8)) + [63]),
 ]
+
+# Bound of the opt-in single-bf16 query mode on bf16 caches (the library
+# refuses it unless MLA_DECODE_ALLOW_BF16_QUERIES is set): queries and the
+# softmax weights are rounded once to bf16, which measured up to 1.3e-2 of
+# the output RMS on the 256-sequence batch; it is held to 2e-2 here.
+TAU_BF16_QUERIES = 2e-2
+
+_full_refs = {}
+
+
+def full_reference(name, seqs):
+    """The oracle's result for the checked sequences of a full-size workload,
+    computed once per workload and kept for the other kernel and split
+    variants (the unabsorbed definition at these sizes takes up to ~30 s)."""
+    key = (name, tuple(seqs))
+    if key not in _full_refs:
+        inp = make_inputs(WORKLOADS[name])
+        _full_refs[key] = oracle.mla_decode(inp, seqs=seqs)
+    return _full_refs[key]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("kernel,q_abs", [(SIMT, "f32"), (MFMA, "f32"), (MFMA, "bf16")])
-@pytest.mark.parametrize("name,seqs,heads", FULL)
-def test_full_size_sampled(kernel, q_abs, name, seqs, heads):
+@pytest.mark.parametrize("name,splits,seqs", FULL)
+def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
     """The whole step at full size, in the launch configuration the benchmark
-    times (matrix-core kernel, the workload's split mode, fp32 absorbed
-    queries for bf16 caches and bf16 ones for the fp8 cache), plus the
-    vector-ALU kernel."""
+    times (matrix-core kernel, balanced split mode, fp32 absorbed queries for
+    bf16 caches and bf16 ones for the fp8 cache), plus the vector-ALU kernel
+    and the workloads' literal split counts."""
+    import mla_paged_decode_amd as mla
     from mla_paged_decode_amd import MLA_BF16, MLA_F32
     wl = WORKLOADS[name]
     if kernel == MFMA and q_abs == "f32" and wl.heads * wl.q_per_seq > 64:
         pytest.skip("fp32 queries on the matrix-core kernel take at most 64 rows per sequence")
-    if q_abs == "bf16" and wl.kv_format != "fp8_e4m3_e8m0":
-        pytest.skip("single-bf16 queries are the fast mode for bf16 caches: at full size their "
-                    "rounding alone reaches ~1.3e-2 of the output RMS, beyond the 1e-2 bound")
-    say(f"[full] {name} kernel={kernel} q_abs={q_abs} splits={wl.num_splits}")
-    inp = make_inputs(wl)
-    qd = MLA_F32 if q_abs == "f32" else MLA_BF16
-    step = run_step(inp, kernel=kernel, num_splits=wl.num_splits, q_abs_dtype=qd)
-    out = step.out.cpu().numpy()
-    assert np.isfinite(out).all()
-    ref, ref_lse = oracle.mla_decode(inp, seqs=seqs, heads=heads)
-    rows = [b * wl.q_per_seq + j for b in seqs for j in range(wl.q_per_seq)]
-    hs = list(range(wl.heads)) if heads is None else heads
-    sel = np.ix_(rows, hs)
-    err = rel_err(out[sel], ref[sel])
+    flags = 0
     tau = tau_for(kernel, wl.kv_format)
+    if q_abs == "bf16" and wl.kv_format != "fp8_e4m3_e8m0":
+        # refused without the opt-in, then held to the opt-in mode's own bound
+        small = make_inputs(wl.with_(batch=1, lens=("const", 64)))
+        with pytest.raises(mla.MlaError) as ei:
+            run_step(small, kernel=kernel, num_splits=splits, q_abs_dtype=MLA_BF16)
+        assert "MLA_DECODE_ALLOW_BF16_QUERIES" in ei.value.message
+        flags, tau = mla.MLA_DECODE_ALLOW_BF16_QUERIES, TAU_BF16_QUERIES
+    say(f"[full] {name} kernel={kernel} q_abs={q_abs} splits={splits}")
+    inp = make_inputs(wl)
+    mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
+    qd = MLA_F32 if q_abs == "f32" else MLA_BF16
+    step = run_step(inp, kernel=kernel, num_splits=splits, q_abs_dtype=qd, flags=flags)
+    out = step.out.cpu().numpy()
+    lse = step.lse.cpu().numpy()
+    del step, inp
+    assert np.isfinite(out).all()
+    ref, ref_lse = full_reference(name, seqs)
+    rows = [b * wl.q_per_seq + j for b in seqs for j in range(wl.q_per_seq)]
+    err = rel_err(out[rows], ref[rows])
     say(f"  rel err {err:.3e} (tau {tau})")
     assert err <= tau
-    lse = step.lse.cpu().numpy()
-    assert np.max(np.abs(lse[sel] - ref_lse[sel])) <= 2e-3
+    assert np.max(np.abs(lse[rows] - ref_lse[rows])) <= 2e-3
 
 
 def test_graph_replay_matches_eager():
     """A whole step captured into a HIP graph gives the eager result on
     every replay, with eager work and synchronisations between replays."""
-    from mla_paged_decode_amd import MLA_BF16
+    from mla_paged_decode_amd import MLA_F32
     from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
     wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=4, lens=("const", 1000))
     inp = make_inputs(wl)
     dev = DeviceBatch.upload(inp)
-    step = DecodeStep(dev, q_abs_dtype=MLA_BF16)
+    step = DecodeStep(dev, q_abs_dtype=MLA_F32)
     eager = step.run().clone()
     lse_eager = step.lse.clone()
     side = torch.cuda.Stream()
@@ -439,6 +468,6 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(step.out, eager), rep
         assert torch.equal(step.lse, lse_eager), rep
-        other = DecodeStep(dev, q_abs_dtype=MLA_BF16)  # eager work between replays
+        other = DecodeStep(dev, q_abs_dtype=MLA_F32)  # eager work between replays
         assert torch.equal(other.run(), eager)
         torch.cuda.synchronize()

@@ -195,3 +195,35 @@ def test_sparse_full_size_sampled():
     seqs = [0, 17, 31]
     ref, rlse = oracle.mla_decode_sparse(inp, topk, seqs=seqs)
     check(got, glse, ref, rlse, rows=seqs, **BARS[MFMA])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_sparse_padding_ignores_nan_in_any_row(fmt):
+    """Padding slots (negative entries, entries past the causal limit, the
+    tail of a partly filled tile) must contribute exactly nothing, whatever
+    the pool holds.  Physical row 0 (slot 0 of page 0, where the kernels
+    point padding slots) is filled with NaN bytes (0xff: a bf16 NaN, an e4m3
+    NaN code and an e8m0 NaN scale), and no listed visible entry names it:
+    every output must stay finite and match the oracle."""
+    name = "glm_b32_h20_ctx4096_bf16" if fmt == "bf16" else "fp8_mtp4_b64_h20_ctx16k"
+    over = dict(batch=3, lens=("fixed", (300, 90, 517)))
+    if fmt == "fp8":
+        over["q_per_seq"] = 2
+    inp = make_inputs(WORKLOADS[name].with_(**over))
+    wl = inp.wl
+    P = wl.page_block
+    topk = make_lists(inp, 0.4, 160, seed=41, beyond=3)
+    for b in range(wl.batch):
+        for j in range(wl.q_per_seq):
+            for k in range(topk.shape[-1]):
+                t = int(topk[b, j, k])
+                if t >= 0 and t < int(inp.seq_lens[b]) and int(inp.block_table[b, t // P]) * P + t % P == 0:
+                    topk[b, j, k] = -1
+    inp.kv_pool[0, 0, :] = 0xFF
+    got, glse = run_step(inp, topk, 2, q_bf16=(fmt == "fp8"), kernel=MFMA)
+    assert np.isfinite(got).all()
+    ref, rlse = oracle.mla_decode_sparse(inp, topk)
+    if fmt == "fp8":
+        check(got, glse, ref, rlse, tau=5e-2, lse_tol=1e-2)
+    else:
+        check(got, glse, ref, rlse, **BARS[MFMA])

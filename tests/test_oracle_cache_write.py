@@ -176,3 +176,15 @@ def test_fp4_round_trip_error_is_at_most_half_a_step():
             step = np.where(mag < 2, 0.5, np.where(mag < 4, 1.0, 2.0))
             # half a step, plus the float32 rounding of value / scale
             assert np.all(np.abs(dec[16 * k:16 * (k + 1)] - blk) <= (0.5 * step + 1e-6 * mag) * s)
+
+
+def test_e2m1_codes_are_the_ocp_values():
+    """All 16 e2m1 codes against the OCP table written out: magnitudes 0,
+    0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7, the same negated for 8..15 (the
+    fp4 row of the model record "GLM-4.7-Flash", SERVICEABILITY JOIN)."""
+    import math as _m
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(16):
+        want = table[c & 7] * (-1.0 if c & 8 else 1.0)
+        got = oracle.e2m1_value(c)
+        assert got == want and _m.copysign(1.0, got) == _m.copysign(1.0, want), (c, got, want)
