@@ -263,7 +263,7 @@ def sparse_timing(inp, dev, q_abs, q_abs_dtype, topk_width: int, num_splits: int
         softmax_scale=dev.softmax_scale, num_splits=num_splits, o_latent=o_lat, lse=None,
         q_abs_dtype=q_abs_dtype)
     nbytes = mla.mla_decode_sparse_workspace_size(params, topk_width)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     topk_t = torch.from_numpy(topk).cuda()
     for _ in range(2):
@@ -316,7 +316,7 @@ def fp4_timing(inp, dev, reps: int):
         max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens, softmax_scale=dev.softmax_scale,
         num_splits=0, o_latent=o_lat, lse=None, q_abs_dtype=mla.MLA_BF16)
     nbytes = mla.mla_decode_workspace_size(params)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     mla.mla_decode_paged(params)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]

@@ -145,7 +145,12 @@ typedef struct {
                           tiles spread evenly over a fixed worker count */
   mla_kernel_t kernel;
   void* workspace;     /* scratch of mla_decode_workspace_size() bytes,
-                          16-B aligned; contents need no initialisation */
+                          16-B aligned.  With MLA_DECODE_DYNAMIC_SPLIT, zero-
+                          fill it once before its first use (e.g. hipMemset
+                          at allocation): its first bytes hold the run-time
+                          scheduler's counters, which every call leaves zero
+                          again.  One call at a time per workspace (calls
+                          that overlap on two streams race). */
   size_t workspace_bytes;
   void* o_latent;      /* out: [B][Sq][H][d_latent], F32 */
   mla_dtype_t o_dtype;
@@ -168,6 +173,14 @@ typedef struct {
  * caches; f32 q_abs (split into bf16 hi + lo products) measures ~2e-5.  The
  * fp8 and fp4 caches take bf16 q_abs without it (their criterion is 5e-2). */
 #define MLA_DECODE_ALLOW_BF16_QUERIES 0x1u
+/* Balanced mode (num_splits = 0) on the bf16 matrix-core kernel gives every
+ * worker one fixed, contiguous share of the tiles (the static split).  This
+ * bit hands each sequence's tiles out at run time instead, four at a time,
+ * from per-sequence counters in the workspace, to whichever worker asks
+ * next.  Both give the same result up to rounding.  (On MI355X the run-time
+ * split measures slower on the benchmark workloads: the many workers of a
+ * long sequence queue on its counter.) */
+#define MLA_DECODE_DYNAMIC_SPLIT 0x2u
 
 /* Workspace bytes mla_decode_paged needs for these parameters.  Reads only
  * host scalars (no pointers are dereferenced, no device is touched). */

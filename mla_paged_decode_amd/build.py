@@ -26,6 +26,7 @@ SOURCES = [
     "combine.hip",
     "decode_simt.hip",
     "decode_mfma.hip",
+    "decode_dyn.hip",
     "decode_fp8.hip",
     "proj_simt.hip",
     "proj_mfma.hip",
@@ -39,6 +40,10 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # LDS is laid out by hand in every kernel; do not move private arrays there
     "-mllvm", "-disable-promote-alloca-to-lds",
+    # Single-lane counter atomics stay plain atomics: the atomic optimiser
+    # would turn them into a wave reduction that waits for the result at once,
+    # where the run-time scheduler wants it a tile later.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -92,9 +92,9 @@ mla_status_t check_decode_scalars(const mla_decode_params_t* p) {
     return fail(MLA_ERR_UNSUPPORTED, "kernel: expected 0 (auto), 1 (simt) or 2 (mfma), got %d", (int)p->kernel);
   if (!std::isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_SHAPE, "softmax_scale: expected a finite value, got %g", (double)p->softmax_scale);
-  if (p->flags & ~MLA_DECODE_ALLOW_BF16_QUERIES)
-    return fail(MLA_ERR_UNSUPPORTED, "flags: expected a subset of 0x%x, got 0x%x", MLA_DECODE_ALLOW_BF16_QUERIES,
-                p->flags);
+  const uint32_t known = MLA_DECODE_ALLOW_BF16_QUERIES | MLA_DECODE_DYNAMIC_SPLIT;
+  if (p->flags & ~known)
+    return fail(MLA_ERR_UNSUPPORTED, "flags: expected a subset of 0x%x, got 0x%x", known, p->flags);
   if (p->q_abs_dtype == MLA_BF16 && (p->kv_format == MLA_KV_BF16 || p->kv_format == MLA_KV_F32) &&
       !(p->flags & MLA_DECODE_ALLOW_BF16_QUERIES))
     return fail(MLA_ERR_UNSUPPORTED,
@@ -115,6 +115,14 @@ mla_status_t select_kernel(const mla_decode_params_t* p, mla_kernel_t* chosen) {
   return MLA_OK;
 }
 
+// The run-time scheduled bf16 kernel (dense decode, balanced mode).
+bool use_dyn(const mla_decode_params_t* p, mla_kernel_t chosen) {
+  return chosen == MLA_KERNEL_MFMA && (p->flags & MLA_DECODE_DYNAMIC_SPLIT) &&
+         mla::decode_dyn_supported(p->kv_format, p->dims.d_latent, p->dims.d_rope,
+                                   p->q_per_seq * p->dims.num_heads, p->q_abs_dtype == MLA_F32, p->num_splits,
+                                   p->batch);
+}
+
 mla_status_t hip_fail(const char* what, hipError_t e) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -123,11 +131,14 @@ mla_status_t hip_fail(const char* what, hipError_t e) {
 
 namespace mla {
 
-WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits) {
+WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits, bool dyn) {
   WorkspaceLayout w{};
-  w.slots = num_splits > 0 ? (int64_t)B * num_splits : (int64_t)kBalancedWorkers + B;
-  w.tile_start_off = 0;
-  size_t off = round_up(sizeof(int32_t) * ((size_t)B + 2), 256);
+  w.slots = num_splits > 0 ? (int64_t)B * num_splits
+            : dyn          ? (int64_t)kMfmaWorkersBf16 + (int64_t)B * (1 + kDynStealParts)
+                           : (int64_t)kBalancedWorkers + B;
+  w.ctr_off = 0;
+  w.tile_start_off = kDynCounterBytes;
+  size_t off = round_up(w.tile_start_off + sizeof(int32_t) * ((size_t)B + 2), 256);
   w.part_lse_off = off;
   off = round_up(off + sizeof(float) * (size_t)w.slots * R, 256);
   w.part_o_off = off;
@@ -552,8 +563,10 @@ mla_status_t mla_decode_workspace_size(const mla_decode_params_t* p, size_t* byt
   if (!bytes) return fail(MLA_ERR_NULL_POINTER, "bytes: expected non-null, got NULL");
   mla_status_t st = check_decode_scalars(p);
   if (st) return st;
+  mla_kernel_t chosen;
+  if ((st = select_kernel(p, &chosen)) != MLA_OK) return st;
   const int R = p->q_per_seq * p->dims.num_heads;
-  *bytes = mla::workspace_layout(p->batch, R, p->dims.d_latent, p->num_splits).total;
+  *bytes = mla::workspace_layout(p->batch, R, p->dims.d_latent, p->num_splits, use_dyn(p, chosen)).total;
   return ok();
 }
 
@@ -589,7 +602,8 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
       return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
   }
   if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
-  const mla::WorkspaceLayout w = mla::workspace_layout(B, R, dc, p->num_splits);
+  const bool dyn = use_dyn(p, chosen);
+  const mla::WorkspaceLayout w = mla::workspace_layout(B, R, dc, p->num_splits, dyn);
   if (p->workspace_bytes < w.total)
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
                 p->workspace_bytes);
@@ -614,6 +628,7 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
   a.num_splits = p->num_splits;
   a.workers = mla::kBalancedWorkers;
   char* ws = static_cast<char*>(p->workspace);
+  a.ctr = reinterpret_cast<uint32_t*>(ws + w.ctr_off);
   a.tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start_off);
   a.part_lse = reinterpret_cast<float*>(ws + w.part_lse_off);
   a.part_o = reinterpret_cast<float*>(ws + w.part_o_off);
@@ -631,11 +646,12 @@ mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
     return hip_fail("plan launch", e);
   if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
     return hip_fail("kernel_start_event record", e);
-  e = use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
+  e = dyn ? mla::launch_decode_dyn(a, s) : use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
   if (e != hipSuccess) return hip_fail("decode launch", e);
   if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
     return hip_fail("kernel_stop_event record", e);
-  if ((e = mla::launch_combine(a, s)) != hipSuccess) return hip_fail("combine launch", e);
+  e = dyn ? mla::launch_combine_dyn(a, s) : mla::launch_combine(a, s);
+  if (e != hipSuccess) return hip_fail("combine launch", e);
   return ok();
 }
 

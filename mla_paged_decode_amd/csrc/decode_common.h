@@ -87,8 +87,6 @@ __device__ __forceinline__ const uint8_t* tile_row_ptr(const TileSrc& ts, int k,
   return (const uint8_t*)(uintptr_t)((kk < ts.kb ? ts.base0 : ts.base1) + (uint64_t)(kk * (int)row_bytes));
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
 // Sparse top-k mode: a tile is 32 consecutive slots of a query's index list;
 // slot k names the cached token list[tt0 + k].  Its physical rows are looked
 // up one tile ahead with scalar loads (counted by lgkmcnt, so the tile
@@ -121,10 +119,20 @@ __device__ __forceinline__ Gather gather_lookup(const DecodeArgs& a, const_i32_p
   return g;
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+// lgkmcnt[11:8], vmcnt[5:4] in bits 15:14).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
   __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | ((N >> 4) << 14));
+}
+
+// s_waitcnt vmcnt(N) alone: the scalar loads in flight (page lookups for a
+// later tile) are not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
 // s_waitcnt lgkmcnt(0): this wave's LDS reads have completed.

@@ -62,15 +62,38 @@ struct DecodeArgs {
   const int32_t* topk;
   int topk_width;
   int sparse_sq;
+  // Dynamically scheduled mode (decode_dyn.hip): the counter region at the
+  // start of the workspace (zero between calls).
+  uint32_t* ctr;
 };
+
+// Dynamically scheduled bf16 decode (decode_dyn.hip).  Workers take tiles
+// of a sequence in claims of kDynClaimTiles from a per-sequence counter; a
+// sequence accepts kDynStealParts visits beyond the workers the balanced plan
+// assigns to it.  Batches up to kDynMaxB sequences.
+constexpr int kDynClaimTiles = 4;
+constexpr int kDynStealParts = 2;
+constexpr int kDynMaxB = kMaxInKernelPlan;
+// Every decode workspace starts with this counter region (a 16-byte header
+// holding the exit counter, then 16 bytes per sequence).  Only the
+// dynamically scheduled kernel uses it; it must be zero before a workspace's
+// first use, and every call of that kernel leaves it zero again (the last
+// workgroup to finish resets it), so no clearing is needed between calls.
+constexpr size_t kDynCounterBytes = 256 + 16 * (size_t)kDynMaxB;
+bool decode_dyn_supported(int fmt, int dc, int dr, int R, int q_f32, int num_splits, int B);
+// Attention and merge: the decode kernel, then the merge kernel.
+hipError_t launch_decode_dyn(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine_dyn(const DecodeArgs& a, hipStream_t s);
 
 // Workspace layout shared by the size query and the launch.
 struct WorkspaceLayout {
-  size_t tile_start_off, part_lse_off, part_o_off, total;
+  size_t ctr_off, tile_start_off, part_lse_off, part_o_off, total;
   int64_t slots;
 };
 // Partial rows are padded to a multiple of 16 (the tiled layout's row blocks).
-WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits);
+// dyn: the dynamically scheduled kernel's slot count (workers + B * (1 +
+// kDynStealParts)) instead of the static modes'.
+WorkspaceLayout workspace_layout(int B, int R, int dc, int num_splits, bool dyn = false);
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);

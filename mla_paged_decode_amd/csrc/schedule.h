@@ -119,7 +119,7 @@ __device__ __forceinline__ int balanced_worker(int G);
 // it; the caller synchronises the workgroup afterwards.
 constexpr int kPlanPerLane = kMaxInKernelPlan / 64;
 __device__ __forceinline__ void wave_plan(const int32_t* lens, int B, int G, int32_t* ts, int32_t* lens_out,
-                                          int32_t* first) {
+                                          int32_t* first, int worker = -1) {
   const int lane = threadIdx.x & 63;
   const int per = (B + 63) / 64;
   const int b0 = lane * per;
@@ -154,7 +154,7 @@ __device__ __forceinline__ void wave_plan(const int32_t* lens, int B, int G, int
   }
   const int32_t c = __any(crossing) ? kUnitCostTiles : 0;
   const int64_t N = (int64_t)N0 + (int64_t)c * Bn;
-  const int64_t tb = worker_tile_begin(balanced_worker(G), N, G);
+  const int64_t tb = worker_tile_begin(worker >= 0 ? worker : balanced_worker(G), N, G);
   p = st - tiles;
   int32_t q = sn - ne;
   int32_t cand = -1;

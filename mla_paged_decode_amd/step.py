@@ -77,7 +77,8 @@ class DecodeStep:
             softmax_scale=dev.softmax_scale, num_splits=num_splits, kernel=kernel,
             o_latent=self.o_latent, lse=self.lse, q_abs_dtype=q_abs_dtype, flags=flags)
         nbytes = mla_decode_workspace_size(self.params)
-        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        # zero-filled once: its counter region must start at zero (calls keep it so)
+        self.workspace = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
         self.params.workspace = self.workspace.data_ptr()
         self.params.workspace_bytes = nbytes
 

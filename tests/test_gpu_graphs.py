@@ -51,7 +51,7 @@ def test_sparse_decode_graph_replays():
         block_table=dev.block_table, max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens,
         softmax_scale=dev.softmax_scale, num_splits=2, o_latent=o, lse=lse, q_abs_dtype=mla.MLA_BF16)
     nbytes = mla.mla_decode_sparse_workspace_size(params, 128)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     print("sparse decode graph (fp8 rows, matrix cores)", flush=True)
     mla.mla_decode_sparse_paged(params, topk_t, 128)
@@ -83,7 +83,7 @@ def test_prefill_graph_replays():
         block_table=dev.block_table, max_blocks_per_seq=dev.block_table.shape[1], seq_lens=dev.seq_lens,
         softmax_scale=dev.softmax_scale, out=out, lse=lse)
     nbytes = mla.mla_prefill_workspace_size(params)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     print("prefill graph (matrix cores)", flush=True)
     mla.mla_prefill_paged(params)

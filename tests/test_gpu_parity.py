@@ -349,7 +349,8 @@ def test_mtp_and_short_sequences(kernel):
 @pytest.mark.parametrize("kernel", kernels())
 def test_page_layout_invariance_and_determinism(kernel):
     """Two physical layouts of the same logical cache give identical bits,
-    and rerunning gives identical bits."""
+    and rerunning gives identical bits (static split; the run-time split
+    re-associates its sums from run to run, tests/test_gpu_dyn.py)."""
     lens = (300, 77, 1024)
     wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=3, lens=("fixed", lens))
     a = make_inputs(wl)
@@ -444,7 +445,9 @@ def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
 
 def test_graph_replay_matches_eager():
     """A whole step captured into a HIP graph gives the eager result on
-    every replay, with eager work and synchronisations between replays."""
+    every replay, with eager work and synchronisations between replays
+    (static split: bit for bit; the run-time split is replayed in
+    tests/test_gpu_dyn.py)."""
     from mla_paged_decode_amd import MLA_F32
     from mla_paged_decode_amd.step import DecodeStep, DeviceBatch
     wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=4, lens=("const", 1000))

@@ -59,7 +59,7 @@ def run_step(inp, topk, num_splits, q_bf16=False, kernel=0):
         q_abs_dtype=qd)
     width = topk.shape[-1]
     nbytes = mla.mla_decode_sparse_workspace_size(params, width)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     params.workspace, params.workspace_bytes = ws.data_ptr(), nbytes
     topk_t = torch.from_numpy(np.ascontiguousarray(topk)).cuda()
     print(f"sparse {wl.name} B={wl.batch} Sq={wl.q_per_seq} width={width} splits={num_splits} kernel={kernel}",
