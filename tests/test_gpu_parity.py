@@ -63,9 +63,22 @@ def lse_tol(kernel):
     return 1e-4 if kernel == SIMT else 1e-3
 
 
-def skip_unsupported(kernel, wl):
-    if kernel == MFMA and wl.kv_format == "f32":
-        pytest.skip("the matrix-core kernels take bf16, fp8 and fp4 caches, not f32")
+def refused(kernel, wl, q_abs_dtype=None):
+    """True, after checking that the library refuses it with
+    MLA_ERR_UNSUPPORTED, for a combination the matrix-core kernels do not
+    take: an f32 cache, or fp32 queries with more than 64 rows per
+    sequence."""
+    import mla_paged_decode_amd as mla
+    if kernel != MFMA:
+        return False
+    f32_rows = (q_abs_dtype is None or q_abs_dtype == mla.MLA_F32) and wl.heads * wl.q_per_seq > 64
+    if wl.kv_format != "f32" and not f32_rows:
+        return False
+    small = make_inputs(wl.with_(batch=1, lens=("const", 8)))
+    with pytest.raises(mla.MlaError) as ei:
+        run_step(small, kernel=kernel, q_abs_dtype=q_abs_dtype)
+    assert ei.value.status == 3 and "MFMA path does not support" in ei.value.message, ei.value
+    return True
 
 
 def run_step(inp, *, kernel, num_splits=0, q_abs_dtype=None, q_abs=None, flags=0):
@@ -191,7 +204,8 @@ def test_projections_partial_token_blocks(name, batch):
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_decode_latent_attention(kernel, name, lens, num_splits):
     wl = WORKLOADS[name].with_(batch=len(lens), lens=("fixed", lens))
-    skip_unsupported(kernel, wl)
+    if refused(kernel, wl):
+        return
     say(f"[decode] {name} lens={lens} splits={num_splits} kernel={kernel}")
     inp = make_inputs(wl, poison_tail=True)
     q_abs = make_q_abs(wl)
@@ -220,7 +234,8 @@ def test_decode_latent_attention(kernel, name, lens, num_splits):
 @pytest.mark.parametrize("kernel", kernels())
 def test_tiny_end_to_end(kernel):
     wl = WORKLOADS["tiny_b2_h4_f32"]
-    skip_unsupported(kernel, wl)
+    if refused(kernel, wl):
+        return
     say(f"[e2e] tiny kernel={kernel}")
     inp = make_inputs(wl)
     step = run_step(inp, kernel=kernel)
@@ -277,7 +292,6 @@ def test_wide_score_range(kernel, name):
     from mla_paged_decode_amd import MLA_BF16
     lens = (300, 1000)
     wl = WORKLOADS[name].with_(batch=len(lens), lens=("fixed", lens))
-    skip_unsupported(kernel, wl)
     say(f"[wide scores] {name} kernel={kernel}")
     inp = make_inputs(wl, poison_tail=True)
     q_abs = (make_q_abs(wl) * 64.0).astype(np.float32)
@@ -415,8 +429,8 @@ def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
     import mla_paged_decode_amd as mla
     from mla_paged_decode_amd import MLA_BF16, MLA_F32
     wl = WORKLOADS[name]
-    if kernel == MFMA and q_abs == "f32" and wl.heads * wl.q_per_seq > 64:
-        pytest.skip("fp32 queries on the matrix-core kernel take at most 64 rows per sequence")
+    if refused(kernel, wl, MLA_F32 if q_abs == "f32" else MLA_BF16):
+        return
     flags = 0
     tau = tau_for(kernel, wl.kv_format)
     if q_abs == "bf16" and wl.kv_format != "fp8_e4m3_e8m0":
