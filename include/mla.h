@@ -204,6 +204,24 @@ mla_status_t mla_decode_select_kernel(const mla_decode_params_t* p, mla_kernel_t
  * size and fp8 row format).  Errors: see the conventions above. */
 mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream);
 
+/* mla_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It runs the same kernels with the split
+ * partials in a scratch array inside the library, MLA_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) per GPU, which each GPU holds from the library's first use on it
+ * until the process ends.  The first call on a GPU looks the array's address
+ * up (make that call outside graph capture).  p->workspace and
+ * p->workspace_bytes are ignored; every other field means what it means for
+ * mla_decode_paged.  Errors: MLA_ERR_WORKSPACE_TOO_SMALL when the call's
+ * workspace (mla_decode_workspace_size) exceeds the scratch,
+ * MLA_ERR_UNSUPPORTED with MLA_DECODE_DYNAMIC_SPLIT; otherwise as
+ * mla_decode_paged.  All calls on one GPU share its scratch, which keeps the
+ * last call's partials: calls in one stream are ordered, calls of one
+ * process that overlap on one GPU (two streams, two threads) race.  Each
+ * process has its own copy.  Allocates nothing. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+mla_status_t mla_decode_paged_noalloc(const mla_decode_params_t* p, void* stream);
+
 /* Sparse top-k decode: each query attends only to the cached tokens its
  * index list names, as the sparse MLA path of the vLLM API page for
  * vllm.models.glm5next.common.model prepares it (a per-token buffer of top-k

@@ -17,7 +17,7 @@ from typing import Optional
 __all__ = [
     "MlaError", "Dims", "DecodeParams", "lib", "library_path",
     "mla_kv_row_bytes", "mla_absorb_q", "mla_decode_workspace_size",
-    "mla_decode_paged", "mla_decode_select_kernel", "mla_out_proj", "mla_cache_write", "mla_abi_version",
+    "mla_decode_paged", "mla_decode_paged_noalloc", "MLA_NOALLOC_SCRATCH_BYTES", "mla_decode_select_kernel", "mla_out_proj", "mla_cache_write", "mla_abi_version",
     "mla_decode_sparse_paged", "mla_decode_sparse_workspace_size",
     "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0", "MLA_KV_FP4_E2M1_E4M3",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
@@ -29,6 +29,7 @@ MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0, MLA_KV_FP4_E2M1_E4M3 = 0, 1, 2, 3
 MLA_KERNEL_AUTO, MLA_KERNEL_SIMT, MLA_KERNEL_MFMA = 0, 1, 2
 MLA_DECODE_ALLOW_BF16_QUERIES = 0x1
 MLA_DECODE_DYNAMIC_SPLIT = 0x2
+MLA_NOALLOC_SCRATCH_BYTES = 128 << 20
 KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0,
              "fp4_e2m1_e4m3": MLA_KV_FP4_E2M1_E4M3}
 
@@ -140,6 +141,8 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_sparse_paged.restype = st
         L.mla_decode_paged.argtypes = [ctypes.POINTER(DecodeParams), vp]
         L.mla_decode_paged.restype = st
+        L.mla_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeParams), vp]
+        L.mla_decode_paged_noalloc.restype = st
         L.mla_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillParams), ctypes.POINTER(ctypes.c_size_t)]
         L.mla_prefill_workspace_size.restype = st
         L.mla_prefill_paged.argtypes = [ctypes.POINTER(PrefillParams), vp]
@@ -274,6 +277,12 @@ def mla_decode_select_kernel(params: DecodeParams) -> int:
 
 def mla_decode_paged(params: DecodeParams, stream=None) -> None:
     _check(lib().mla_decode_paged(ctypes.byref(params), _stream(stream)))
+
+
+def mla_decode_paged_noalloc(params: DecodeParams, stream=None) -> None:
+    """mla_decode_paged with the library's own per-GPU scratch in place of
+    the workspace (params.workspace is ignored); allocates nothing."""
+    _check(lib().mla_decode_paged_noalloc(ctypes.byref(params), _stream(stream)))
 
 
 def mla_decode_sparse_workspace_size(params: DecodeParams, topk_width: int) -> int:

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -248,6 +249,132 @@ PrefillLayout prefill_workspace(const mla_prefill_params_t* p) {
   w.part_lse_off = w.part_o_off + up(po);
   w.total = (size_t)(w.part_lse_off + up(pl));
   return w;
+}
+
+}  // namespace
+
+namespace {
+
+// Scratch of the allocation-free decode entry point: one copy per GPU, made
+// when the library's code is loaded on that GPU and held until the process
+// ends.  Host code never uses the array's name as an address: the device
+// address of each GPU's copy is looked up once (hipGetSymbolAddress, with
+// that GPU current) and kept per device.
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mla_status_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_UNSUPPORTED, "device: expected an ordinal in 0..%d, got %d", kMaxDevices - 1, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!ptr) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// Dense decode.  The split partials go to p->workspace, or with `noalloc` to
+// the current device's scratch array (p->workspace is then ignored).
+mla_status_t decode_paged(const mla_decode_params_t* p, bool noalloc, void* stream) {
+  mla_status_t st = check_decode_scalars(p);
+  if (st) return st;
+  const int B = p->batch, H = p->dims.num_heads, R = p->q_per_seq * H;
+  const int dc = p->dims.d_latent, dr = p->dims.d_rope;
+  const int fmt = p->kv_format;
+  const int q_f32 = p->q_abs_dtype == MLA_F32;
+  mla_kernel_t chosen;
+  if ((st = select_kernel(p, &chosen)) != MLA_OK) return st;
+  const bool use_mfma = chosen == MLA_KERNEL_MFMA;
+  if (B == 0) return ok();
+  const struct {
+    const void* ptr;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{p->q_abs, "q_abs", 16},           {p->kv_pool, "kv_pool", 16},
+              {p->block_table, "block_table", 4}, {p->seq_lens, "seq_lens", 4},
+              {p->o_latent, "o_latent", 16},      {p->workspace, "workspace", 16}};
+  for (const auto& x : ptrs) {
+    if (noalloc && &x == &ptrs[5]) break;  // no workspace argument
+    if (!x.ptr) return fail(MLA_ERR_NULL_POINTER, "%s: expected non-null, got NULL", x.name);
+    if (!aligned(x.ptr, x.align))
+      return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
+  }
+  if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
+  const bool dyn = use_dyn(p, chosen);
+  if (noalloc && (p->flags & MLA_DECODE_DYNAMIC_SPLIT))
+    return fail(MLA_ERR_UNSUPPORTED, "flags: MLA_DECODE_DYNAMIC_SPLIT is not offered without a workspace");
+  const mla::WorkspaceLayout w = mla::workspace_layout(B, R, dc, p->num_splits, dyn);
+  char* ws = static_cast<char*>(p->workspace);
+  if (noalloc) {
+    if (w.total > kNoAllocScratchBytes)
+      return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace: this call needs %zu bytes, beyond the %zu-byte scratch of the allocation-free entry "
+                  "point; use mla_decode_paged with a workspace",
+                  w.total, kNoAllocScratchBytes);
+    void* sp = nullptr;
+    if ((st = scratch_for_current_device(&sp)) != MLA_OK) return st;
+    ws = static_cast<char*>(sp);
+  } else if (p->workspace_bytes < w.total) {
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
+                p->workspace_bytes);
+  }
+
+  mla::DecodeArgs a{};
+  a.B = B;
+  a.Sq = p->q_per_seq;
+  a.H = H;
+  a.R = R;
+  a.dc = dc;
+  a.dr = dr;
+  a.q_abs = p->q_abs;
+  a.q_f32 = q_f32;
+  a.pool = static_cast<const uint8_t*>(p->kv_pool);
+  a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
+  a.P = p->page_block;
+  a.P_log2 = __builtin_ctz((unsigned)p->page_block);
+  a.block_table = p->block_table;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.seq_lens = p->seq_lens;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.num_splits = p->num_splits;
+  a.workers = mla::kBalancedWorkers;
+  a.ctr = reinterpret_cast<uint32_t*>(ws + w.ctr_off);
+  a.tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start_off);
+  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse_off);
+  a.part_o = reinterpret_cast<float*>(ws + w.part_o_off);
+  a.o = static_cast<float*>(p->o_latent);
+  a.lse = p->lse;
+
+  a.plan_in_kernel = use_mfma && B <= mla::kMaxInKernelPlan;
+  a.part_tiled = use_mfma ? 1 : 0;
+  if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
+  if (use_mfma && mla::decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) a.workers = mla::fp8_rows_workers(R);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (a.num_splits == 0 && !a.plan_in_kernel && (e = mla::launch_plan(a, s)) != hipSuccess)
+    return hip_fail("plan launch", e);
+  if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
+    return hip_fail("kernel_start_event record", e);
+  e = dyn ? mla::launch_decode_dyn(a, s) : use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
+  if (e != hipSuccess) return hip_fail("decode launch", e);
+  if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
+    return hip_fail("kernel_stop_event record", e);
+  e = dyn ? mla::launch_combine_dyn(a, s) : mla::launch_combine(a, s);
+  if (e != hipSuccess) return hip_fail("combine launch", e);
+  return ok();
 }
 
 }  // namespace
@@ -579,80 +706,11 @@ mla_status_t mla_decode_select_kernel(const mla_decode_params_t* p, mla_kernel_t
 }
 
 mla_status_t mla_decode_paged(const mla_decode_params_t* p, void* stream) {
-  mla_status_t st = check_decode_scalars(p);
-  if (st) return st;
-  const int B = p->batch, H = p->dims.num_heads, R = p->q_per_seq * H;
-  const int dc = p->dims.d_latent, dr = p->dims.d_rope;
-  const int fmt = p->kv_format;
-  const int q_f32 = p->q_abs_dtype == MLA_F32;
-  mla_kernel_t chosen;
-  if ((st = select_kernel(p, &chosen)) != MLA_OK) return st;
-  const bool use_mfma = chosen == MLA_KERNEL_MFMA;
-  if (B == 0) return ok();
-  const struct {
-    const void* ptr;
-    const char* name;
-    size_t align;
-  } ptrs[] = {{p->q_abs, "q_abs", 16},           {p->kv_pool, "kv_pool", 16},
-              {p->block_table, "block_table", 4}, {p->seq_lens, "seq_lens", 4},
-              {p->workspace, "workspace", 16},    {p->o_latent, "o_latent", 16}};
-  for (const auto& x : ptrs) {
-    if (!x.ptr) return fail(MLA_ERR_NULL_POINTER, "%s: expected non-null, got NULL", x.name);
-    if (!aligned(x.ptr, x.align))
-      return fail(MLA_ERR_ALIGNMENT, "%s: expected %zu-byte alignment, got %p", x.name, x.align, x.ptr);
-  }
-  if (p->lse && !aligned(p->lse, 4)) return fail(MLA_ERR_ALIGNMENT, "lse: expected 4-byte alignment, got %p", p->lse);
-  const bool dyn = use_dyn(p, chosen);
-  const mla::WorkspaceLayout w = mla::workspace_layout(B, R, dc, p->num_splits, dyn);
-  if (p->workspace_bytes < w.total)
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace_bytes: expected >= %zu, got %zu", w.total,
-                p->workspace_bytes);
+  return decode_paged(p, false, stream);
+}
 
-  mla::DecodeArgs a{};
-  a.B = B;
-  a.Sq = p->q_per_seq;
-  a.H = H;
-  a.R = R;
-  a.dc = dc;
-  a.dr = dr;
-  a.q_abs = p->q_abs;
-  a.q_f32 = q_f32;
-  a.pool = static_cast<const uint8_t*>(p->kv_pool);
-  a.row_bytes = (int64_t)mla_kv_row_bytes(&p->dims, p->kv_format);
-  a.P = p->page_block;
-  a.P_log2 = __builtin_ctz((unsigned)p->page_block);
-  a.block_table = p->block_table;
-  a.max_blocks = p->max_blocks_per_seq;
-  a.seq_lens = p->seq_lens;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.num_splits = p->num_splits;
-  a.workers = mla::kBalancedWorkers;
-  char* ws = static_cast<char*>(p->workspace);
-  a.ctr = reinterpret_cast<uint32_t*>(ws + w.ctr_off);
-  a.tile_start = reinterpret_cast<int32_t*>(ws + w.tile_start_off);
-  a.part_lse = reinterpret_cast<float*>(ws + w.part_lse_off);
-  a.part_o = reinterpret_cast<float*>(ws + w.part_o_off);
-  a.o = static_cast<float*>(p->o_latent);
-  a.lse = p->lse;
-
-  a.plan_in_kernel = use_mfma && B <= mla::kMaxInKernelPlan;
-  a.part_tiled = use_mfma ? 1 : 0;
-  if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
-  if (use_mfma && mla::decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) a.workers = mla::fp8_rows_workers(R);
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (a.num_splits == 0 && !a.plan_in_kernel && (e = mla::launch_plan(a, s)) != hipSuccess)
-    return hip_fail("plan launch", e);
-  if (p->kernel_start_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_start_event), s)) != hipSuccess)
-    return hip_fail("kernel_start_event record", e);
-  e = dyn ? mla::launch_decode_dyn(a, s) : use_mfma ? mla::launch_decode_mfma(a, fmt, s) : mla::launch_decode_simt(a, fmt, s);
-  if (e != hipSuccess) return hip_fail("decode launch", e);
-  if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
-    return hip_fail("kernel_stop_event record", e);
-  e = dyn ? mla::launch_combine_dyn(a, s) : mla::launch_combine(a, s);
-  if (e != hipSuccess) return hip_fail("combine launch", e);
-  return ok();
+mla_status_t mla_decode_paged_noalloc(const mla_decode_params_t* p, void* stream) {
+  return decode_paged(p, true, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = mla.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -304,3 +304,20 @@ def test_synthetic_workload_tables_are_valid():
         small = wl.with_(batch=min(wl.batch, 4), lens=("fixed", tuple([37, 4096, 1, 0][:min(wl.batch, 4)])))
         inp = make_inputs(small)
         mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], small.page_block)
+
+
+def test_noalloc_entry_rejects_before_any_device_work():
+    """The allocation-free decode refuses, before touching a GPU, a call
+    whose partials would not fit its scratch and the run-time split; the
+    workspace fields are not read."""
+    assert mla.MLA_NOALLOC_SCRATCH_BYTES == 128 << 20
+    big = params(batch=4000, workspace=None, workspace_bytes=0)
+    assert mla.mla_decode_workspace_size(big) > mla.MLA_NOALLOC_SCRATCH_BYTES
+    expect_error(lambda: mla.mla_decode_paged_noalloc(big, stream=0), 5, "beyond the 134217728-byte scratch")
+    dyn = params(workspace=None, workspace_bytes=0, flags=mla.MLA_DECODE_DYNAMIC_SPLIT)
+    expect_error(lambda: mla.mla_decode_paged_noalloc(dyn, stream=0), 3, "MLA_DECODE_DYNAMIC_SPLIT")
+    # the other checks still apply
+    expect_error(lambda: mla.mla_decode_paged_noalloc(params(o_latent=None, workspace=None), stream=0), 1,
+                 "o_latent")
+    # a call with no sequences returns before looking up the scratch
+    mla.mla_decode_paged_noalloc(params(batch=0, workspace=None, workspace_bytes=0), stream=0)
