@@ -360,7 +360,7 @@ mla_status_t decode_paged(const mla_decode_params_t* p, bool noalloc, void* stre
   a.plan_in_kernel = use_mfma && B <= mla::kMaxInKernelPlan;
   a.part_tiled = use_mfma ? 1 : 0;
   if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
-  if (use_mfma && mla::decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) a.workers = mla::fp8_rows_workers(R);
+  if (use_mfma && mla::decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) a.workers = mla::fp8_rows_workers(fmt, R);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

@@ -23,9 +23,9 @@ constexpr int kBalancedWorkers = 512;
 // balanced worker count it runs with (at most kBalancedWorkers).
 constexpr int kRingBf16 = 2;
 constexpr int kMfmaWorkersBf16 = 512;
-// Balanced worker count of the fp8 / fp4 kernel for R query rows: one
-// workgroup per CU, two for at most two row blocks (fp8_rows_workers).
-int fp8_rows_workers(int R);
+// Balanced worker count of the fp8 / fp4 kernels for R query rows: one
+// workgroup per CU, two for fp4 rows with at most two row blocks.
+int fp8_rows_workers(int fmt, int R);
 // Batches up to this size are planned inside the matrix-core decode kernel
 // (each workgroup scans seq_lens itself); larger ones use the plan kernel.
 constexpr int kMaxInKernelPlan = 512;
