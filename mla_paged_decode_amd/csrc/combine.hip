@@ -167,9 +167,13 @@ constexpr int kTiledThreads = 256;
 constexpr int kTiledWaves = kTiledThreads / 64;
 constexpr int kChunk = 64;
 
-// 32-bit forms of the balanced-split worker ranges (tile counts < 2^22).
+// 32-bit forms of the balanced-split worker ranges (tile counts < 2^22,
+// workers <= 1024).
 __device__ __forceinline__ int64_t tiles_begin(int64_t g, int64_t N, int64_t G) {
   return N < (1 << 22) ? (int64_t)((uint32_t)(g * N) / (uint32_t)G) : worker_tile_begin(g, N, G);
+}
+__device__ __forceinline__ int64_t worker_of(int64_t t, int64_t N, int64_t G) {
+  return N < (1 << 22) && G <= 1024 ? (int64_t)((uint32_t)((t + 1) * G - 1) / (uint32_t)N) : worker_of_tile(t, N, G);
 }
 
 template <int DPW>
@@ -352,6 +356,225 @@ __global__ __launch_bounds__(kTiledThreads, 4) void combine_tiled_kernel(DecodeA
 }
 
 
+// Merge for the tiled partial layout when sequences have few parts.  One
+// wave per (sequence, 16-row block, kStreamCols 16-column blocks); lane l
+// holds column l % 16 of rows 4(l/16) .. +3 of every part (one float4 per
+// column block), so each lane merges its own four rows without any exchange:
+// the parts' log-sum-exps and partial rows are read kStreamBatch parts at a
+// time, all loads of a batch in flight together, and folded into a running
+// maximum, sum and weighted sum (the online form of the merge above).  No
+// LDS, no barriers.
+constexpr int kStreamBatch = 4;
+constexpr int kStreamCols = 4;
+constexpr int kStreamWaves = 4;
+constexpr int kStreamMaxParts = 12;  // average parts per sequence up to which it is used
+constexpr int kSplitMinParts = 48;   // ... and beyond which combine_split_kernel is
+
+__global__ __launch_bounds__(64 * kStreamWaves) void combine_stream_kernel(DecodeArgs a) {
+  const int b = blockIdx.x, w = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int kdb = a.dc / 16;
+  const int d0 = (blockIdx.z * kStreamWaves + wave) * kStreamCols;  // first column block
+  const int r0 = 16 * w + 4 * g;                                    // this lane's first row
+  if (d0 >= kdb || r0 >= a.R) return;                               // no barriers below
+  const int nrow = min(4, a.R - r0);
+  const bool lse4 = (a.R & 3) == 0;  // then nrow = 4 and every lane's four log-sum-exps are one aligned float4
+
+  int64_t g0 = 0, n = 0;
+  int64_t N = 0, G = a.workers;
+  if (a.num_splits > 0) {
+    n = a.num_splits;
+  } else {
+    const int64_t te = a.tile_start[b + 1];
+    const int64_t ts = a.tile_start[b] + plan_lead(a.tile_start[b], te, a.tile_start[a.B + 1]);  // first real tile
+    N = a.tile_start[a.B];
+    if (ts < te) {
+      g0 = worker_of(ts, N, G);
+      n = worker_of(te - 1, N, G) - g0 + 1;
+    }
+  }
+  const int row_blocks = (a.R + 15) / 16;
+  const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
+  const float* po = a.part_o + ((int64_t)w * kdb + d0) * 256 + lane * 4;
+
+  float m[4], z[4], acc[kStreamCols][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    m[k] = -INFINITY;
+    z[k] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kStreamCols; ++c) acc[c][k] = 0.f;
+  }
+  for (int64_t i0 = 0; i0 < n; i0 += kStreamBatch) {
+    float4 p[kStreamBatch][kStreamCols];
+    float l[kStreamBatch][4];
+#pragma unroll
+    for (int j = 0; j < kStreamBatch; ++j) {
+      const int64_t i = i0 + j;
+      int64_t slot = -1;
+      if (i < n) {
+        if (a.num_splits > 0) {
+          slot = (int64_t)b * a.num_splits + i;
+        } else {
+          const int64_t gg = g0 + i;
+          if (tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = gg + b;  // workers without tiles wrote nothing
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kStreamCols; ++c)
+        p[j][c] = slot >= 0 && d0 + c < kdb ? *reinterpret_cast<const float4*>(po + slot * slot_stride + 256 * c)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lse4) {  // four rows of a part, 16-byte aligned
+        const float4 v = slot >= 0 ? *reinterpret_cast<const float4*>(a.part_lse + slot * a.R + r0)
+                                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        l[j][0] = v.x, l[j][1] = v.y, l[j][2] = v.z, l[j][3] = v.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l[j][k] = slot >= 0 && k < nrow ? a.part_lse[slot * a.R + r0 + k] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float mb = m[k];
+#pragma unroll
+      for (int j = 0; j < kStreamBatch; ++j) mb = fmaxf(mb, l[j][k]);
+      if (mb == -INFINITY) continue;  // nothing visible so far in this row
+      const float f = m[k] == -INFINITY ? 0.f : __expf(m[k] - mb);
+      z[k] *= f;
+#pragma unroll
+      for (int c = 0; c < kStreamCols; ++c) acc[c][k] *= f;
+#pragma unroll
+      for (int j = 0; j < kStreamBatch; ++j) {
+        const float wj = l[j][k] == -INFINITY ? 0.f : __expf(l[j][k] - mb);
+        z[k] += wj;
+#pragma unroll
+        for (int c = 0; c < kStreamCols; ++c) {
+          const float pv[4] = {p[j][c].x, p[j][c].y, p[j][c].z, p[j][c].w};
+          acc[c][k] += wj != 0.f ? wj * pv[k] : 0.f;  // zero-weight parts may hold stale data: never multiplied
+        }
+      }
+      m[k] = mb;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k >= nrow) break;
+    const int64_t out_row = (int64_t)b * a.R + r0 + k;
+    const float inv = z[k] > 0.f ? 1.f / z[k] : 0.f;
+#pragma unroll
+    for (int c = 0; c < kStreamCols; ++c)
+      if (d0 + c < kdb) a.o[out_row * a.dc + 16 * (d0 + c) + li] = acc[c][k] * inv;
+    if (a.lse && d0 == 0 && li == 0) a.lse[out_row] = z[k] > 0.f ? m[k] + logf(z[k]) : -INFINITY;
+  }
+}
+
+// Merge for the tiled partial layout when sequences have many parts: one
+// workgroup of SPLIT waves per (sequence, 16-row block, 16-column block).
+// Wave k folds parts k, k + SPLIT, ... (kStreamBatch at a time, loads in
+// flight together) into per-lane running maxima, sums and weighted sums as
+// the streaming merge does; the SPLIT states are then merged through LDS.
+template <int SPLIT>
+__global__ __launch_bounds__(64 * SPLIT) void combine_split_kernel(DecodeArgs a) {
+  __shared__ float4 s_state[3][SPLIT][64];  // per wave and lane: maxima, sums, weighted sums of 4 rows
+  const int b = blockIdx.x, w = blockIdx.y, d = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
+  const int kdb = a.dc / 16;
+  const int r0 = 16 * w + 4 * g;  // this lane's first row
+  const bool active = r0 < a.R;
+  const int nrow = active ? min(4, a.R - r0) : 0;
+
+  int64_t g0 = 0, n = 0;
+  int64_t N = 0, G = a.workers;
+  if (a.num_splits > 0) {
+    n = a.num_splits;
+  } else {
+    const int64_t te = a.tile_start[b + 1];
+    const int64_t ts = a.tile_start[b] + plan_lead(a.tile_start[b], te, a.tile_start[a.B + 1]);  // first real tile
+    N = a.tile_start[a.B];
+    if (ts < te) {
+      g0 = worker_of(ts, N, G);
+      n = worker_of(te - 1, N, G) - g0 + 1;
+    }
+  }
+  const int row_blocks = (a.R + 15) / 16;
+  const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
+  const float* po = a.part_o + ((int64_t)w * kdb + d) * 256 + lane * 4;
+
+  float m[4], z[4], acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) m[k] = -INFINITY, z[k] = 0.f, acc[k] = 0.f;
+  if (active) {
+    for (int64_t i0 = wave; i0 < n; i0 += (int64_t)SPLIT * kStreamBatch) {
+      float4 p[kStreamBatch];
+      float l[kStreamBatch][4];
+#pragma unroll
+      for (int j = 0; j < kStreamBatch; ++j) {
+        const int64_t i = i0 + (int64_t)SPLIT * j;
+        int64_t slot = -1;
+        if (i < n) {
+          if (a.num_splits > 0) {
+            slot = (int64_t)b * a.num_splits + i;
+          } else {
+            const int64_t gg = g0 + i;
+            if (tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = gg + b;
+          }
+        }
+        p[j] = slot >= 0 ? *reinterpret_cast<const float4*>(po + slot * slot_stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) l[j][k] = slot >= 0 && k < nrow ? a.part_lse[slot * a.R + r0 + k] : -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float mb = m[k];
+#pragma unroll
+        for (int j = 0; j < kStreamBatch; ++j) mb = fmaxf(mb, l[j][k]);
+        if (mb == -INFINITY) continue;
+        const float f = m[k] == -INFINITY ? 0.f : __expf(m[k] - mb);
+        z[k] *= f;
+        acc[k] *= f;
+#pragma unroll
+        for (int j = 0; j < kStreamBatch; ++j) {
+          const float pv[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
+          const float wj = l[j][k] == -INFINITY ? 0.f : __expf(l[j][k] - mb);
+          z[k] += wj;
+          acc[k] += wj != 0.f ? wj * pv[k] : 0.f;  // zero-weight parts may hold stale data: never multiplied
+        }
+        m[k] = mb;
+      }
+    }
+  }
+  s_state[0][wave][lane] = make_float4(m[0], m[1], m[2], m[3]);
+  s_state[1][wave][lane] = make_float4(z[0], z[1], z[2], z[3]);
+  s_state[2][wave][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (wave != 0 || !active) return;
+  float M[4], Z[4], A[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) M[k] = -INFINITY, Z[k] = 0.f, A[k] = 0.f;
+#pragma unroll
+  for (int v = 0; v < SPLIT; ++v) {
+    const float4 mv = s_state[0][v][lane];
+    M[0] = fmaxf(M[0], mv.x), M[1] = fmaxf(M[1], mv.y), M[2] = fmaxf(M[2], mv.z), M[3] = fmaxf(M[3], mv.w);
+  }
+#pragma unroll
+  for (int v = 0; v < SPLIT; ++v) {
+    const float4 mv = s_state[0][v][lane], zv = s_state[1][v][lane], av = s_state[2][v][lane];
+    const float mm[4] = {mv.x, mv.y, mv.z, mv.w}, zz[4] = {zv.x, zv.y, zv.z, zv.w}, aa[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = mm[k] == -INFINITY ? 0.f : __expf(mm[k] - M[k]);
+      Z[k] += f * zz[k];
+      A[k] += f * aa[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (k >= nrow) break;
+    const int64_t out_row = (int64_t)b * a.R + r0 + k;
+    a.o[out_row * a.dc + 16 * d + li] = Z[k] > 0.f ? A[k] / Z[k] : 0.f;
+    if (a.lse && d == 0 && li == 0) a.lse[out_row] = Z[k] > 0.f ? M[k] + logf(Z[k]) : -INFINITY;
+  }
+}
 }  // namespace
 
 hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
@@ -362,12 +585,27 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   if ((int64_t)a.B * a.R == 0) return hipSuccess;
   if (a.part_tiled) {
-    // About 1024 workgroups: DPW column blocks per workgroup, a power of two
-    // dividing dc/16; many parts per sequence favour DPW < 4 (waves share a
-    // column block and split its parts).
     const int kdb = a.dc / 16;
     const int64_t cells = (int64_t)a.B * ((a.R + 15) / 16) * kdb;
     const int64_t parts = a.num_splits > 0 ? a.num_splits : (a.workers + a.B - 1) / a.B + 1;
+    // Few parts per sequence (on average): the streaming merge, one wave per
+    // 16 x 16 output cell.
+    if (parts <= kStreamMaxParts) {
+      const int per_block = kStreamWaves * kStreamCols;
+      const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)((kdb + per_block - 1) / per_block));
+      combine_stream_kernel<<<grid, 64 * kStreamWaves, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    // Many parts (long sequences over few workers each): the parts of each
+    // 16 x 16 output cell split over the 16 waves of a workgroup.
+    if (parts > kSplitMinParts) {
+      const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)kdb);
+      combine_split_kernel<16><<<grid, 64 * 16, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    // Otherwise about 1024 workgroups: DPW column blocks per workgroup, a
+    // power of two dividing dc/16; many parts per sequence favour DPW < 4
+    // (waves share a column block and split its parts).
     int dpw = 1;
     while (dpw < 16 && cells / (2 * dpw) >= 1024 && kdb % (2 * dpw) == 0) dpw *= 2;
     if (parts > 32 && dpw > 1) dpw = 1;
