@@ -122,6 +122,7 @@ struct ProjArgs {
   void* out;       // absorb: q_abs [N][H][dc+dr]; out_proj: [N][H][dv] (f32)
   int out_f32;
   int tok_blocks;  // matrix-core kernels: 16-token blocks per workgroup (set at launch)
+  int tok_groups;  // matrix-core kernels: workgroups per (head, column group) (set at launch)
 };
 // Dispatchers: matrix-core kernels where the dtypes and shapes allow,
 // vector-ALU kernels otherwise.

@@ -23,7 +23,7 @@
 // workgroup are chosen for about 1024 (absorb) or 512 (out_proj) workgroups,
 // one block for small batches.  Every load of a block is issued before the first one is waited
 // for, and the next block's inputs before this block's products.
-// grid = (ceil(N / (16 * tok_blocks)), out_cols / 64, H).
+// The grid is one-dimensional and XCD-aware (proj_cell below).
 #include <algorithm>
 
 #include "device_common.h"
@@ -49,6 +49,38 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// The grid is one-dimensional and every workgroup of head h lands on XCD
+// h % 8, so a head's weight slice and its tokens' inputs come from HBM once
+// and are then shared in that L2 by the head's token and column blocks (a
+// grid over (tokens, columns, heads) fetched them once per XCD that ran any
+// of them, up to 8 times).  XCDs with fewer heads get idle workgroups.
+constexpr int kXcds = 8;
+struct ProjCell {
+  int h, col_group, tok_group;
+  bool valid;
+};
+__device__ __forceinline__ ProjCell proj_cell(int col_groups, int tok_groups, int H) {
+  const int L = blockIdx.x;
+  const int x = L % kXcds, k = L / kXcds;
+  const int per_head = col_groups * tok_groups;
+  const int h = x + kXcds * (k / per_head), r = k % per_head;
+  return ProjCell{h, r % col_groups, r / col_groups, h < H};
+}
+// Grid size for proj_cell: 8 x (the most heads an XCD gets) x cells per head.
+unsigned proj_grid(int col_groups, int tok_groups, int H) {
+  return (unsigned)(kXcds * ((H + kXcds - 1) / kXcds) * col_groups * tok_groups);
+}
+// At most `per_cu` workgroups per CU on the busiest XCD (32 CUs): fewer,
+// larger token groups when the heads do not spread evenly over the XCDs.
+void cap_token_groups(ProjArgs& a, int col_groups, unsigned& gx, int per_cu) {
+  const int nblk = (a.N + kTok - 1) / kTok;
+  const int cap = std::max(1, 32 * per_cu / (((a.H + kXcds - 1) / kXcds) * col_groups));
+  if ((int)gx <= cap) return;
+  a.tok_blocks = (nblk + cap - 1) / cap;
+  gx = (unsigned)((nblk + a.tok_blocks - 1) / a.tok_blocks);
+}
+
 template <bool kOutF32, int NKS>  // NKS = d_nope / 32
 __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   constexpr int kRows = 32 * NKS;               // d_nope
@@ -57,8 +89,10 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) char w_tile[kRows * kWRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int h = blockIdx.z, c0 = blockIdx.y * kCols;
-  const int n0 = blockIdx.x * kTok * a.tok_blocks;
+  const ProjCell cell = proj_cell(a.dc / kCols, a.tok_groups, a.H);
+  if (!cell.valid) return;
+  const int h = cell.h, c0 = cell.col_group * kCols;
+  const int n0 = cell.tok_group * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + (int64_t)h * (a.dn + a.dv) * a.dc;
 
   // Weight tile W[0:dn][c0:c0+64] and the query operands: every load is
@@ -79,7 +113,7 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   // block's kTok x d_rope part, loaded with the query operands.
   constexpr int kRopePer = kTok * kMaxRope / (64 * kWaves);
   const uint16_t* qin = static_cast<const uint16_t*>(a.in);
-  const bool rope_wg = blockIdx.y == 0;
+  const bool rope_wg = cell.col_group == 0;
   auto load_q = [&](int nb, bf16x8 (&qv)[NKS], uint16_t (&rv)[kRopePer]) __attribute__((always_inline)) {
     const int n = nb + li;
     const uint16_t* q = qin + ((int64_t)(n < a.N ? n : 0) * a.H + h) * qw;
@@ -173,8 +207,10 @@ __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) 
   __shared__ __attribute__((aligned(16))) char o_tile[kTok * kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const int h = blockIdx.z, v = blockIdx.y * kCols + 16 * wave + li;
-  const int n0 = blockIdx.x * kTok * a.tok_blocks;
+  const ProjCell cell = proj_cell(a.dv / kCols, a.tok_groups, a.H);
+  if (!cell.valid) return;
+  const int h = cell.h, v = cell.col_group * kCols + 16 * wave + li;
+  const int n0 = cell.tok_group * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + ((int64_t)h * (a.dn + a.dv) + a.dn + v) * a.dc;
 
   // B operand: this lane's weight row (value column v), all of K, kept for
@@ -265,7 +301,9 @@ hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
   // fewer blocks per workgroup measured faster (at 256 tokens, 2 blocks:
   // 17.6 us; 4 blocks: 19.5 us)
   a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx, 1024);
-  const dim3 grid(gx, a.dc / kCols, a.H);
+  cap_token_groups(a, a.dc / kCols, gx, 5);
+  a.tok_groups = (int)gx;
+  const dim3 grid(proj_grid(a.dc / kCols, a.tok_groups, a.H));
   switch (a.dn / 32) {
 #define MLA_CASE(K)                                                                   \
   case K:                                                                             \
@@ -284,7 +322,9 @@ hipError_t launch_out_proj_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
   a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx, 512);
-  const dim3 grid(gx, a.dv / kCols, a.H);
+  cap_token_groups(a, a.dv / kCols, gx, 4);
+  a.tok_groups = (int)gx;
+  const dim3 grid(proj_grid(a.dv / kCols, a.tok_groups, a.H));
   switch (a.dc / 32) {
 #define MLA_CASE(K) \
   case K: out_proj_mfma_kernel<K><<<grid, 64 * kWaves, 0, s>>>(a); break;
