@@ -1136,10 +1136,14 @@ bool decode_fp8_rows_sparse_supported(int fmt, int dc, int dr, int R, int q_f32,
   return decode_fp8_rows_supported(fmt, dc, dr, R, q_f32) && topk_width % kTile == 0;
 }
 
+// Sparse units are short (one query token's list chunk), so with one or two
+// row blocks the two-workgroups-per-CU kernel keeps more of them in flight
+// than the MX kernel's one per CU (fp8 MTP batch, 512 units: 252 us against
+// 361 us).
 template <int FMT>
 hipError_t launch_rows_sparse(const DecodeArgs& a, hipStream_t s) {
   const unsigned units = (unsigned)(a.B * a.num_splits);
-  if (rows_mx(FMT, a.R)) return launch_mx<true>(a, units, s);
+  if (rows_mx(FMT, a.R) && (a.R + 15) / 16 > 2) return launch_mx<true>(a, units, s);
   switch ((a.R + 15) / 16) {
 #define MLA_CASE(N) \
   case N:           \
