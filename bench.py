@@ -392,7 +392,8 @@ def prefill_timing(inp, dev, chunk: int, n_seqs: int, reps: int):
             "frac": mfma_flops / (us * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, "kernel": "mfma"}
 
 
-def decode_timing(wl, splits: int, qd: int, kernel: int, reps: int, cache_bytes: float, warmup: int = 3):
+def decode_timing(wl, splits: int, qd: int, kernel: int, reps: int, cache_bytes: float, warmup: int = 3,
+                  extra_flags: int = 0):
     """Eager decode calls on one workload: per call, the decode call
     (mla_decode_paged: attention and merge; torch events around it) and the
     attention kernel alone (HIP events the library records on the launch
@@ -408,7 +409,7 @@ def decode_timing(wl, splits: int, qd: int, kernel: int, reps: int, cache_bytes:
     inp = make_inputs(wl)
     mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
     dev = DeviceBatch.upload(inp)
-    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel)
+    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel, flags=extra_flags)
     pool_bytes = dev.kv_pool.numel()
     copies = max(1, math.ceil(cache_bytes / pool_bytes))
     pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
@@ -472,6 +473,9 @@ def main() -> int:
                          "kernel, eager); empty: none")
     ap.add_argument("--extra-reps", type=int, default=10)
     ap.add_argument("--kernel", choices=["auto", "simt", "mfma"], default="auto")
+    ap.add_argument("--fused-merge", action="store_true",
+                    help="set MLA_DECODE_FUSED_MERGE (merge inside the attention kernel where it applies; "
+                         "measured slower on MI355X)")
     ap.add_argument("--q-abs", choices=["auto", "bf16", "f32"], default="auto",
                     help="absorbed-query dtype fed to the attention kernel; auto: f32 (hi + lo bf16 "
                          "products) for bf16 and f32 caches, bf16 for the fp8 cache")
@@ -517,7 +521,10 @@ def main() -> int:
     mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
     dev = DeviceBatch.upload(inp)
     flags = mla.MLA_DECODE_ALLOW_BF16_QUERIES if qd == mla.MLA_BF16 and wl.kv_format in ("bf16", "f32") else 0
-    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel, flags=flags)
+    # --fused-merge: the merge inside the attention kernel (the step's
+    # workspace is zero-filled once at allocation, as that mode asks).
+    fused = mla.MLA_DECODE_FUSED_MERGE if args.fused_merge else 0
+    step = DecodeStep(dev, q_abs_dtype=qd, num_splits=splits, kernel=kernel, flags=flags | fused)
     pool_bytes = dev.kv_pool.numel()
     copies = max(1, math.ceil(args.cache_bytes / pool_bytes))
     pools = [dev.kv_pool] + [dev.kv_pool.clone() for _ in range(copies - 1)]
@@ -627,7 +634,7 @@ def main() -> int:
         "context": list(wl.lens), "page_block": wl.page_block, "kv_format": wl.kv_format,
         "d_latent": wl.d_latent, "d_rope": wl.d_rope, "num_splits": splits,
         "kernel": {1: "simt", 2: "mfma"}[used], "q_abs": "f32" if qd == mla.MLA_F32 else "bf16",
-        "cache_copies": copies,
+        "cache_copies": copies, "fused_merge_flag": args.fused_merge,
     }
     del graphs, step, pools, dev
     torch.cuda.empty_cache()
@@ -637,7 +644,8 @@ def main() -> int:
         w = WORKLOADS[name]
         sp = w.num_splits if sp is None else sp
         log(f"[bench] sub-record {name} num_splits={sp}")
-        rec = decode_timing(w, sp, q_dtype(w), kernel, args.extra_reps, args.cache_bytes)
+        rec = decode_timing(w, sp, q_dtype(w), kernel, args.extra_reps, args.cache_bytes,
+                            extra_flags=mla.MLA_DECODE_FUSED_MERGE if args.fused_merge else 0)
         log(f"[bench]   attention kernel {rec['attention_kernel_us']:.1f} us ({rec['attention_frac']:.3f} of 8 TB/s), "
             f"decode call {rec['decode_call_us']:.1f} us ({rec['decode_frac']:.3f})")
         extras.append(rec)

@@ -145,12 +145,13 @@ typedef struct {
                           tiles spread evenly over a fixed worker count */
   mla_kernel_t kernel;
   void* workspace;     /* scratch of mla_decode_workspace_size() bytes,
-                          16-B aligned.  With MLA_DECODE_DYNAMIC_SPLIT, zero-
-                          fill it once before its first use (e.g. hipMemset
-                          at allocation): its first bytes hold the run-time
-                          scheduler's counters, which every call leaves zero
-                          again.  One call at a time per workspace (calls
-                          that overlap on two streams race). */
+                          16-B aligned.  With MLA_DECODE_DYNAMIC_SPLIT or
+                          MLA_DECODE_FUSED_MERGE, zero-fill it once before
+                          its first use (e.g. hipMemset at allocation): its
+                          first bytes hold per-sequence counters, which
+                          every call leaves zero again.  One call at a time
+                          per workspace (calls that overlap on two streams
+                          race). */
   size_t workspace_bytes;
   void* o_latent;      /* out: [B][Sq][H][d_latent], F32 */
   mla_dtype_t o_dtype;
@@ -160,9 +161,10 @@ typedef struct {
                                the stream right before the split-KV attention
                                kernel is launched */
   void* kernel_stop_event;  /* optional hipEvent_t (NULL = none): recorded right
-                               after it, before the merge kernel.  Both are
-                               caller-owned; they time the dominant kernel
-                               alone. */
+                               after it, before the merge kernel (if the merge
+                               runs inside the attention kernel, after both).
+                               Both are caller-owned; they time the dominant
+                               kernel alone. */
   uint32_t flags;           /* MLA_DECODE_* bits below; 0 by default */
 } mla_decode_params_t;
 
@@ -181,6 +183,20 @@ typedef struct {
  * split measures slower on the benchmark workloads: the many workers of a
  * long sequence queue on its counter.) */
 #define MLA_DECODE_DYNAMIC_SPLIT 0x2u
+/* The caller keeps the workspace's counter region zero (zero-filled once at
+ * allocation; every call leaves it zero), which lets balanced mode merge the
+ * partial results inside the attention kernel instead of in a second kernel:
+ * the last workgroup to finish a part of a sequence merges that sequence,
+ * and a sequence held by one worker is written out directly.  Applies to the
+ * bf16 matrix-core kernel with up to 32 query rows (q_per_seq * num_heads)
+ * and batches with few parts per sequence (at least a fifth as many
+ * sequences as workers); otherwise the bit changes nothing.  Same result up
+ * to rounding.  Ignored by mla_decode_paged_noalloc.  (On MI355X it measures
+ * slower than the separate merge kernel on the 256-sequence ragged batch:
+ * making every partial visible across the XCDs' L2 caches before its
+ * arrival is counted, and the merges left to the last workgroups, each cost
+ * more than the merge kernel saves.) */
+#define MLA_DECODE_FUSED_MERGE 0x4u
 
 /* Workspace bytes mla_decode_paged needs for these parameters.  Reads only
  * host scalars (no pointers are dereferenced, no device is touched). */

@@ -21,7 +21,7 @@ __all__ = [
     "mla_decode_sparse_paged", "mla_decode_sparse_workspace_size",
     "MLA_F32", "MLA_BF16", "MLA_KV_F32", "MLA_KV_BF16", "MLA_KV_FP8_E4M3_E8M0", "MLA_KV_FP4_E2M1_E4M3",
     "MLA_KERNEL_AUTO", "MLA_KERNEL_SIMT", "MLA_KERNEL_MFMA", "KV_FORMAT",
-    "MLA_DECODE_ALLOW_BF16_QUERIES", "MLA_DECODE_DYNAMIC_SPLIT", "mla_validate_tables",
+    "MLA_DECODE_ALLOW_BF16_QUERIES", "MLA_DECODE_DYNAMIC_SPLIT", "MLA_DECODE_FUSED_MERGE", "mla_validate_tables",
 ]
 
 MLA_F32, MLA_BF16 = 0, 1
@@ -29,6 +29,7 @@ MLA_KV_F32, MLA_KV_BF16, MLA_KV_FP8_E4M3_E8M0, MLA_KV_FP4_E2M1_E4M3 = 0, 1, 2, 3
 MLA_KERNEL_AUTO, MLA_KERNEL_SIMT, MLA_KERNEL_MFMA = 0, 1, 2
 MLA_DECODE_ALLOW_BF16_QUERIES = 0x1
 MLA_DECODE_DYNAMIC_SPLIT = 0x2
+MLA_DECODE_FUSED_MERGE = 0x4
 MLA_NOALLOC_SCRATCH_BYTES = 128 << 20
 KV_FORMAT = {"f32": MLA_KV_F32, "bf16": MLA_KV_BF16, "fp8_e4m3_e8m0": MLA_KV_FP8_E4M3_E8M0,
              "fp4_e2m1_e4m3": MLA_KV_FP4_E2M1_E4M3}

@@ -93,7 +93,7 @@ mla_status_t check_decode_scalars(const mla_decode_params_t* p) {
     return fail(MLA_ERR_UNSUPPORTED, "kernel: expected 0 (auto), 1 (simt) or 2 (mfma), got %d", (int)p->kernel);
   if (!std::isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_SHAPE, "softmax_scale: expected a finite value, got %g", (double)p->softmax_scale);
-  const uint32_t known = MLA_DECODE_ALLOW_BF16_QUERIES | MLA_DECODE_DYNAMIC_SPLIT;
+  const uint32_t known = MLA_DECODE_ALLOW_BF16_QUERIES | MLA_DECODE_DYNAMIC_SPLIT | MLA_DECODE_FUSED_MERGE;
   if (p->flags & ~known)
     return fail(MLA_ERR_UNSUPPORTED, "flags: expected a subset of 0x%x, got 0x%x", known, p->flags);
   if (p->q_abs_dtype == MLA_BF16 && (p->kv_format == MLA_KV_BF16 || p->kv_format == MLA_KV_F32) &&
@@ -361,6 +361,8 @@ mla_status_t decode_paged(const mla_decode_params_t* p, bool noalloc, void* stre
   a.part_tiled = use_mfma ? 1 : 0;
   if (use_mfma && fmt == MLA_KV_BF16) a.workers = mla::kMfmaWorkersBf16;
   if (use_mfma && mla::decode_fp8_rows_supported(fmt, dc, dr, R, q_f32)) a.workers = mla::fp8_rows_workers(fmt, R);
+  a.fuse_merge = !noalloc && !dyn && use_mfma && (p->flags & MLA_DECODE_FUSED_MERGE) && a.plan_in_kernel &&
+                 mla::decode_fused_merge_supported(fmt, dc, dr, R, a.num_splits, B, a.workers);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -372,8 +374,10 @@ mla_status_t decode_paged(const mla_decode_params_t* p, bool noalloc, void* stre
   if (e != hipSuccess) return hip_fail("decode launch", e);
   if (p->kernel_stop_event && (e = hipEventRecord(static_cast<hipEvent_t>(p->kernel_stop_event), s)) != hipSuccess)
     return hip_fail("kernel_stop_event record", e);
-  e = dyn ? mla::launch_combine_dyn(a, s) : mla::launch_combine(a, s);
-  if (e != hipSuccess) return hip_fail("combine launch", e);
+  if (!a.fuse_merge) {
+    e = dyn ? mla::launch_combine_dyn(a, s) : mla::launch_combine(a, s);
+    if (e != hipSuccess) return hip_fail("combine launch", e);
+  }
   return ok();
 }
 

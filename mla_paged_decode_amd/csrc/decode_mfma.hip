@@ -43,6 +43,7 @@
 #include "staging_bf16.h"
 #include "device_common.h"
 #include "internal.h"
+#include "merge_fused.h"
 #include "schedule.h"
 
 namespace mla {
@@ -149,13 +150,18 @@ struct Staging<kFP8, NW, NBUF> {
   __device__ __forceinline__ void wait(int) { wait_vmcnt_lgkm0<0>(); }
 };
 
-template <int FMT, bool HILO, int NW, int NBUF, bool SPARSE = false>
+// FUSE: balanced plan computed in the kernel, with the merge done by the
+// last workgroup to finish each sequence (merge_fused.h): sequences with one
+// part are written to o and lse directly.
+template <int FMT, bool HILO, int NW, int NBUF, bool SPARSE = false, bool FUSE = false>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
   using G = Geo<FMT>;
+  static_assert(!FUSE || (FMT == kBF16 && !SPARSE), "the fused merge is built for the dense bf16 kernel");
   __shared__ __attribute__((aligned(16))) char tiles_mem[NBUF * G::kTileBytes];
   __shared__ int32_t s_ts[kMaxInKernelPlan + 2];
   __shared__ int32_t s_lens[kMaxInKernelPlan];
   __shared__ int32_t s_first;
+  __shared__ int32_t s_last[2];
   __shared__ int32_t s_sink[64];  // destination of L2 prefetch loads, never read
   lds_char* const tiles = (lds_char*)tiles_mem;
 
@@ -182,7 +188,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     if (blockIdx.x == 0)  // publish the plan for the merge kernel
       for (int i = threadIdx.x; i <= a.B + 1; i += 64 * NW) a.tile_start[i] = s_ts[i];
     ts = s_ts;
+    if constexpr (FUSE) zero_empty_sequences(a, s_lens, a.workers);
   }
+  // FUSE: sequences of this worker with several parts whose arrival is
+  // counted at the end (only the first and the last unit can be such: a
+  // sequence between them lies wholly in this worker's range).
+  int pend0 = -1, pend1 = -1;
   using St = Staging<FMT, NW, NBUF>;
   constexpr int D = St::kDepth;
   St st;
@@ -592,17 +603,38 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     float inv_r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) inv_r[i] = __shfl(inv, 4 * g + i);
-    if (g == 0 && row_ok)
-      a.part_lse[slot * a.R + row] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
-    // Tiled partial layout: the lane's four rows of column block d are one
-    // 16-byte store, and a wave's store instruction writes 1 KB contiguously.
+    const float lse_row = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
     const int row_blocks = (a.R + 15) / 16;
-    if (wave < row_blocks && wave * 16 + 4 * g < a.R) {  // lanes with only padding rows skip
-      float* dst = a.part_o + ((slot * row_blocks + wave) * G::kDb * 64 + lane) * 4;
+    bool direct = false;
+    if constexpr (FUSE) {
+      direct = uniform(part_range(ts, a.B, a.workers, b).n) == 1;
+      if (!direct) {
+        if (pend0 < 0) pend0 = b;
+        else pend1 = b;
+      }
+    }
+    if (direct) {  // the only part: the result itself, rows of o
+      if (a.lse && g == 0 && row_ok) a.lse[(int64_t)b * a.R + row] = lse_row;
 #pragma unroll
-      for (int d = 0; d < G::kDb; ++d)
-        *reinterpret_cast<float4*>(dst + 256 * d) =
-            make_float4(acc[d][0] * inv_r[0], acc[d][1] * inv_r[1], acc[d][2] * inv_r[2], acc[d][3] * inv_r[3]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = wave * 16 + 4 * g + i;
+        if (r < a.R) {
+          float* dst = a.o + ((int64_t)b * a.R + r) * a.dc + li;
+#pragma unroll
+          for (int d = 0; d < G::kDb; ++d) dst[16 * d] = acc[d][i] * inv_r[i];
+        }
+      }
+    } else {
+      if (g == 0 && row_ok) a.part_lse[slot * a.R + row] = lse_row;
+      // Tiled partial layout: the lane's four rows of column block d are one
+      // 16-byte store, and a wave's store instruction writes 1 KB contiguously.
+      if (wave < row_blocks && wave * 16 + 4 * g < a.R) {  // lanes with only padding rows skip
+        float* dst = a.part_o + ((slot * row_blocks + wave) * G::kDb * 64 + lane) * 4;
+#pragma unroll
+        for (int d = 0; d < G::kDb; ++d)
+          *reinterpret_cast<float4*>(dst + 256 * d) =
+              make_float4(acc[d][0] * inv_r[0], acc[d][1] * inv_r[1], acc[d][2] * inv_r[2], acc[d][3] * inv_r[3]);
+      }
     }
     ring = uniform((ring + ntiles) % NBUF);
     pre = uniform(ahead_done);
@@ -612,12 +644,51 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeArgs a) {
     have_next = have && uniform(unit_it.next(a, nxt));
   }
   wait_vmcnt_lgkm0<0>();  // no transfer into LDS outlives the workgroup
+  if constexpr (FUSE) {
+    if (pend0 >= 0) {
+      const int pend[2] = {pend0, pend1};
+      // Every wave's partial stores are visible at agent scope before the
+      // arrival is counted.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          s_last[k] = 0;
+          if (pend[k] >= 0) {
+            const int n = part_range(ts, a.B, a.workers, pend[k]).n;
+            s_last[k] = __hip_atomic_fetch_add(arrival_counter(a, pend[k]), 1u, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(n - 1);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (s_last[k]) {  // this workgroup completed the sequence: merge it
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+          merge_sequence<G::kDb>(a, ts, pend[k], NW, wave, lane);
+          if (threadIdx.x == 0)
+            __hip_atomic_store(arrival_counter(a, pend[k]), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
 }
 
 template <int FMT, bool HILO>
 hipError_t launch_nw(const DecodeArgs& a, int nw, hipStream_t s) {
   const unsigned units = a.num_splits > 0 ? (unsigned)(a.B * a.num_splits) : (unsigned)a.workers;
   constexpr int NBUF = FMT == kBF16 ? kRingBf16 : 2;
+  if (a.fuse_merge) {
+    if constexpr (FMT == kBF16) {
+      if (nw == 2 && a.num_splits == 0 && a.plan_in_kernel && a.ctr) {
+        decode_mfma_kernel<FMT, HILO, 2, NBUF, false, true><<<units, 128, 0, s>>>(a);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   switch (nw) {
 #define MLA_CASE(N) \
   case N: decode_mfma_kernel<FMT, HILO, N, NBUF><<<units, 64 * N, 0, s>>>(a); break;
@@ -655,6 +726,14 @@ bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32) {
   if (!((fmt == kBF16 && dc == 512) || (fmt == kFP8 && dc == 448))) return false;
   const int nw = waves_for(R);
   return nw <= (q_f32 ? 4 : 8);
+}
+
+// The fused merge is offered where sequences have few parts: its merging
+// workgroup reads every other part itself (a merge kernel spreads that over
+// the chip), so it needs at least one sequence per five workers.
+bool decode_fused_merge_supported(int fmt, int dc, int dr, int R, int num_splits, int B, int workers) {
+  return fmt == kBF16 && dc == 512 && dr == kDr && waves_for(R) == 2 && num_splits == 0 && B >= 1 &&
+         B <= kMaxInKernelPlan && 5 * B >= workers;
 }
 
 bool decode_mfma_sparse_supported(int fmt, int dc, int dr, int R, int topk_width) {

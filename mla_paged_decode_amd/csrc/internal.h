@@ -62,9 +62,12 @@ struct DecodeArgs {
   const int32_t* topk;
   int topk_width;
   int sparse_sq;
-  // Dynamically scheduled mode (decode_dyn.hip): the counter region at the
-  // start of the workspace (zero between calls).
+  // Dynamically scheduled mode (decode_dyn.hip) and the fused merge: the
+  // counter region at the start of the workspace (zero between calls).
   uint32_t* ctr;
+  // 1: the bf16 matrix-core kernel merges the partials itself (merge_fused.h)
+  // and no merge kernel runs.
+  int fuse_merge;
 };
 
 // Dynamically scheduled bf16 decode (decode_dyn.hip).  Workers take tiles
@@ -99,6 +102,9 @@ hipError_t launch_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_simt(const DecodeArgs& a, int fmt, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int fmt, hipStream_t s);
 bool decode_mfma_supported(int fmt, int dc, int dr, int R, int q_f32);
+// Whether the bf16 matrix-core kernel merges in-kernel for this call shape
+// (balanced mode, plan in the kernel, one workgroup shape, few parts).
+bool decode_fused_merge_supported(int fmt, int dc, int dr, int R, int num_splits, int B, int workers);
 // fp8 or fp4 cache with bf16 queries: one 16-row block per wave
 // (decode_fp8.hip); launch_decode_mfma dispatches to it when it applies.
 bool decode_fp8_rows_supported(int fmt, int dc, int dr, int R, int q_f32);

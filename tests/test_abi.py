@@ -89,7 +89,7 @@ def expect_error(fn, status, fragment):
     (dict(workspace_bytes=100), 5, "workspace_bytes: expected >= "),
     (dict(q_abs_dtype=MLA_BF16), 3, "q_abs_dtype: expected 0 (f32) with a bf16 or f32 cache, got 1 (bf16)"),
     (dict(q_abs_dtype=MLA_BF16, kv_format=MLA_KV_F32), 3, "set MLA_DECODE_ALLOW_BF16_QUERIES"),
-    (dict(flags=0x5), 3, "flags: expected a subset of 0x3, got 0x5"),
+    (dict(flags=0x9), 3, "flags: expected a subset of 0x7, got 0x9"),
 ])
 def test_decode_rejects_before_launch(kw, status, fragment):
     p = params(**kw)
