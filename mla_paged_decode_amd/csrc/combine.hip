@@ -473,7 +473,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void combine_stream_kernel(Decod
 // Wave k folds parts k, k + SPLIT, ... (kStreamBatch at a time, loads in
 // flight together) into per-lane running maxima, sums and weighted sums as
 // the streaming merge does; the SPLIT states are then merged through LDS.
-template <int SPLIT>
+template <int SPLIT, int BATCH>
 __global__ __launch_bounds__(64 * SPLIT) void combine_split_kernel(DecodeArgs a) {
   __shared__ float4 s_state[3][SPLIT][64];  // per wave and lane: maxima, sums, weighted sums of 4 rows
   const int b = blockIdx.x, w = blockIdx.y, d = blockIdx.z;
@@ -503,37 +503,45 @@ __global__ __launch_bounds__(64 * SPLIT) void combine_split_kernel(DecodeArgs a)
   float m[4], z[4], acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) m[k] = -INFINITY, z[k] = 0.f, acc[k] = 0.f;
+  const bool lse4 = (a.R & 3) == 0;  // then nrow = 4 and every lane's four log-sum-exps are one aligned float4
   if (active) {
-    for (int64_t i0 = wave; i0 < n; i0 += (int64_t)SPLIT * kStreamBatch) {
-      float4 p[kStreamBatch];
-      float l[kStreamBatch][4];
+    for (int64_t i0 = wave; i0 < n; i0 += (int64_t)SPLIT * BATCH) {
+      float4 p[BATCH];
+      float l[BATCH][4];
 #pragma unroll
-      for (int j = 0; j < kStreamBatch; ++j) {
+      for (int j = 0; j < BATCH; ++j) {
         const int64_t i = i0 + (int64_t)SPLIT * j;
         int64_t slot = -1;
         if (i < n) {
           if (a.num_splits > 0) {
             slot = (int64_t)b * a.num_splits + i;
           } else {
+            // every worker has tiles when there are at least as many tiles as workers
             const int64_t gg = g0 + i;
-            if (tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = gg + b;
+            if (N >= G || tiles_begin(gg, N, G) < tiles_begin(gg + 1, N, G)) slot = gg + b;
           }
         }
         p[j] = slot >= 0 ? *reinterpret_cast<const float4*>(po + slot * slot_stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (lse4) {
+          const float4 v = slot >= 0 ? *reinterpret_cast<const float4*>(a.part_lse + slot * a.R + r0)
+                                     : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          l[j][0] = v.x, l[j][1] = v.y, l[j][2] = v.z, l[j][3] = v.w;
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) l[j][k] = slot >= 0 && k < nrow ? a.part_lse[slot * a.R + r0 + k] : -INFINITY;
+          for (int k = 0; k < 4; ++k) l[j][k] = slot >= 0 && k < nrow ? a.part_lse[slot * a.R + r0 + k] : -INFINITY;
+        }
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         float mb = m[k];
 #pragma unroll
-        for (int j = 0; j < kStreamBatch; ++j) mb = fmaxf(mb, l[j][k]);
+        for (int j = 0; j < BATCH; ++j) mb = fmaxf(mb, l[j][k]);
         if (mb == -INFINITY) continue;
         const float f = m[k] == -INFINITY ? 0.f : __expf(m[k] - mb);
         z[k] *= f;
         acc[k] *= f;
 #pragma unroll
-        for (int j = 0; j < kStreamBatch; ++j) {
+        for (int j = 0; j < BATCH; ++j) {
           const float pv[4] = {p[j].x, p[j].y, p[j].z, p[j].w};
           const float wj = l[j][k] == -INFINITY ? 0.f : __expf(l[j][k] - mb);
           z[k] += wj;
@@ -556,8 +564,8 @@ __global__ __launch_bounds__(64 * SPLIT) void combine_split_kernel(DecodeArgs a)
     const float4 mv = s_state[0][v][lane];
     M[0] = fmaxf(M[0], mv.x), M[1] = fmaxf(M[1], mv.y), M[2] = fmaxf(M[2], mv.z), M[3] = fmaxf(M[3], mv.w);
   }
-#pragma unroll
-  for (int v = 0; v < SPLIT; ++v) {
+#pragma unroll 4
+  for (int v = 0; v < SPLIT; ++v) {  // (4 at a time: 16 states in registers at once would spill)
     const float4 mv = s_state[0][v][lane], zv = s_state[1][v][lane], av = s_state[2][v][lane];
     const float mm[4] = {mv.x, mv.y, mv.z, mv.w}, zz[4] = {zv.x, zv.y, zv.z, zv.w}, aa[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
@@ -598,9 +606,13 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
     }
     // Many parts (long sequences over few workers each): the parts of each
     // 16 x 16 output cell split over the 16 waves of a workgroup.
+    // Each wave reads its parts in one batch up to 12 per wave (192 parts).
     if (parts > kSplitMinParts) {
       const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)kdb);
-      combine_split_kernel<16><<<grid, 64 * 16, 0, s>>>(a);
+      const int64_t per_wave = (parts + 15) / 16;
+      if (per_wave <= 4) combine_split_kernel<16, 4><<<grid, 64 * 16, 0, s>>>(a);
+      else if (per_wave <= 8) combine_split_kernel<16, 8><<<grid, 64 * 16, 0, s>>>(a);
+      else combine_split_kernel<16, 12><<<grid, 64 * 16, 0, s>>>(a);
       return hipGetLastError();
     }
     // Otherwise about 1024 workgroups: DPW column blocks per workgroup, a

@@ -9,8 +9,9 @@
 //
 // absorb: the weight's contiguous dimension is the output column, so the
 // workgroup's d_nope x 64 weight tile is staged in LDS (all loads issued
-// before the first store) and read k-major with ds_read_b64_tr_b16.  bf16 q
-// times bf16 W is exact in fp32.
+// before the first store) and read k-major with ds_read_b64_tr_b16; the
+// queries (the A operand all four waves share) are staged in LDS too.  bf16
+// q times bf16 W is exact in fp32.
 // out_proj: weight rows are contiguous along K and load straight from
 // memory into the B operand.  The fp32 latent input is split into hi + lo
 // bf16 parts, so the products are exact to ~16 significant bits;
@@ -19,10 +20,10 @@
 // Decode batches are small (tens to hundreds of tokens): the weights are
 // read once per step and the cost is memory latency.  A workgroup covers one
 // head, 64 output columns (one wave per 16) and one or more 16-token blocks,
-// keeping its weight slice (LDS or registers) across its blocks; blocks per
-// workgroup are chosen for about 1024 (absorb) or 512 (out_proj) workgroups,
-// one block for small batches.  Every load of a block is issued before the first one is waited
-// for, and the next block's inputs before this block's products.
+// keeping its weight slice (LDS or registers) across its blocks.  The grid is
+// one round of workgroups (three per CU), and a workgroup requests its
+// weights and the inputs of up to four (absorb) or two (out_proj) token
+// blocks before it waits for any of them: one memory round trip.
 // The grid is one-dimensional and XCD-aware (proj_cell below).
 #include <algorithm>
 
@@ -86,7 +87,14 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   constexpr int kRows = 32 * NKS;               // d_nope
   constexpr int kChunks = kRows * (kCols / 8);  // 16-B chunks of the weight tile
   constexpr int kPer = (kChunks + 64 * kWaves - 1) / (64 * kWaves);
+  // Token blocks whose queries are staged together (fewer for wide d_nope,
+  // to keep the LDS of three workgroups per CU).
+  constexpr int kBlk = NKS <= 8 ? 4 : 2;
+  constexpr int kQRow = kRows * 2 + 16;          // LDS row stride (bytes) of the query tile
+  constexpr int kQChunks = kBlk * kTok * (kRows / 8);
+  constexpr int kQPer = (kQChunks + 64 * kWaves - 1) / (64 * kWaves);
   __shared__ __attribute__((aligned(16))) char w_tile[kRows * kWRow];
+  __shared__ __attribute__((aligned(16))) char q_tile[kBlk * kTok * kQRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
   const ProjCell cell = proj_cell(a.dc / kCols, a.tok_groups, a.H);
@@ -94,111 +102,110 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
   const int h = cell.h, c0 = cell.col_group * kCols;
   const int n0 = cell.tok_group * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + (int64_t)h * (a.dn + a.dv) * a.dc;
+  const int qw = a.dn + a.dr, ow = a.dc + a.dr;
+  const uint16_t* qin = static_cast<const uint16_t*>(a.in);
+  const bool rope_wg = cell.col_group == 0;
+  constexpr int kRopePer = kTok * kMaxRope / (64 * kWaves);
+  const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
 
-  // Weight tile W[0:dn][c0:c0+64] and the query operands: every load is
-  // issued before the first one is waited for.
-  // (Indices past the tile are clamped, not branched around, so that the
-  // loads are issued back to back.)
+  // The weight tile W[0:dn][c0:c0+64] and the d_nope part of kBlk token
+  // blocks' queries (the A operand every wave shares) go through LDS: the
+  // workgroup loads each once, and every load is issued before the first one
+  // is waited for, so the workgroup waits one memory round trip.  Indices
+  // past a tile are clamped, not branched around (padding tokens read the
+  // last token; their products are never stored).
   u32x4 wt[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int i = min(j * 64 * kWaves + (int)threadIdx.x, kChunks - 1);
     wt[j] = *reinterpret_cast<const u32x4*>(w + (int64_t)(i >> 3) * a.dc + c0 + 8 * (i & 7));
   }
-  const int qw = a.dn + a.dr, ow = a.dc + a.dr;
-  const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-  // Query operands of a token block (padding tokens read token 0, no branch
-  // around the loads, and use zeros).  The first column block also copies
-  // the RoPE part of the query: thread t holds values t, t + 256, ... of the
-  // block's kTok x d_rope part, loaded with the query operands.
-  constexpr int kRopePer = kTok * kMaxRope / (64 * kWaves);
-  const uint16_t* qin = static_cast<const uint16_t*>(a.in);
-  const bool rope_wg = cell.col_group == 0;
-  auto load_q = [&](int nb, bf16x8 (&qv)[NKS], uint16_t (&rv)[kRopePer]) __attribute__((always_inline)) {
-    const int n = nb + li;
-    const uint16_t* q = qin + ((int64_t)(n < a.N ? n : 0) * a.H + h) * qw;
+  bool first = true;
+  for (int nc = n0; nc < nb_end; nc += kTok * kBlk) {
+    u32x4 qt[kQPer];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qv[ks] = load_bf16x8(q + 32 * ks + 8 * g);
+    for (int j = 0; j < kQPer; ++j) {
+      const int i = min(j * 64 * kWaves + (int)threadIdx.x, kQChunks - 1);
+      const int n = min(nc + i / (kRows / 8), a.N - 1);  // token (block-major, 16 per block)
+      qt[j] = *reinterpret_cast<const u32x4*>(qin + ((int64_t)n * a.H + h) * qw + 8 * (i % (kRows / 8)));
+    }
+    // The RoPE part of the query is copied by the first column group: thread
+    // t holds values t, t + 256, ... of each block's kTok x d_rope part.
+    uint16_t ra[kBlk][kRopePer];
     if (rope_wg) {
 #pragma unroll
-      for (int u = 0; u < kRopePer; ++u) {
-        const int i = min(u * 64 * kWaves + (int)threadIdx.x, kTok * a.dr - 1);
-        const int nn = min(nb + i / a.dr, a.N - 1);
-        rv[u] = qin[((int64_t)nn * a.H + h) * qw + a.dn + i % a.dr];
+      for (int k = 0; k < kBlk; ++k)
+#pragma unroll
+        for (int u = 0; u < kRopePer; ++u) {
+          const int i = min(u * 64 * kWaves + (int)threadIdx.x, kTok * a.dr - 1);
+          const int nn = min(nc + k * kTok + i / a.dr, a.N - 1);
+          ra[k][u] = qin[((int64_t)nn * a.H + h) * qw + a.dn + i % a.dr];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first is waited for
+    if (!first) __syncthreads();        // the previous blocks' readers of q_tile are done
+    if (first) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = j * 64 * kWaves + threadIdx.x;
+        if (i < kChunks) *reinterpret_cast<u32x4*>(w_tile + (i >> 3) * kWRow + 16 * (i & 7)) = wt[j];
       }
-    }
-  };
-  bf16x8 qa[NKS];
-  uint16_t ra[kRopePer];
-  load_q(n0, qa, ra);
-  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first is waited for
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = j * 64 * kWaves + threadIdx.x;
-    if (i < kChunks) *reinterpret_cast<u32x4*>(w_tile + (i >> 3) * kWRow + 16 * (i & 7)) = wt[j];
-  }
-  __syncthreads();
-
-  // The workgroup's token blocks share the weight tile; the next block's
-  // queries are requested before this block's products.
-  const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
-  for (int nb = n0; nb < nb_end; nb += kTok) {
-    bf16x8 qn[NKS];
-    uint16_t rn[kRopePer];
-    if (nb + kTok < nb_end) load_q(nb + kTok, qn, rn);
-    if (nb + li >= a.N) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qa[ks] = zero;
-    }
-    // This wave's 16 columns c0 + 16 * wave + li.
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const char* rows = w_tile + (32 * ks + 8 * g + (li >> 2)) * kWRow + 32 * wave + 8 * (li & 3);
-      const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)rows);
-      const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + 4 * kWRow));
-      const bf16x8 wb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], wb, acc, 0, 0, 0);
+      first = false;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nn = nb + 4 * g + i;
-      if (nn >= a.N) continue;
-      const int64_t o = ((int64_t)nn * a.H + h) * ow + c0 + 16 * wave + li;
-      if (kOutF32) static_cast<float*>(a.out)[o] = acc[i];
-      else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
+    for (int j = 0; j < kQPer; ++j) {
+      const int i = j * 64 * kWaves + threadIdx.x;
+      if (i < kQChunks)
+        *reinterpret_cast<u32x4*>(q_tile + (i / (kRows / 8)) * kQRow + 16 * (i % (kRows / 8))) = qt[j];
     }
-    if (rope_wg) {
+    __syncthreads();
 #pragma unroll
-      for (int u = 0; u < kRopePer; ++u) {
-        const int i = u * 64 * kWaves + threadIdx.x;
-        const int nn = nb + i / a.dr, k = i % a.dr;
-        if (i >= kTok * a.dr || nn >= a.N) continue;
-        const int64_t r = (int64_t)nn * a.H + h;
-        if (kOutF32) static_cast<float*>(a.out)[r * ow + a.dc + k] = bf16_bits_to_f32(ra[u]);
-        else static_cast<uint16_t*>(a.out)[r * ow + a.dc + k] = ra[u];
+    for (int k = 0; k < kBlk; ++k) {
+      const int nb = nc + k * kTok;
+      if (nb >= nb_end) break;
+      // This wave's 16 columns c0 + 16 * wave + li; A rows are tokens.
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* qrow = q_tile + (k * kTok + li) * kQRow + 16 * g;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 64 * ks));
+        const char* rows = w_tile + (32 * ks + 8 * g + (li >> 2)) * kWRow + 32 * wave + 8 * (li & 3);
+        const bf16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)rows);
+        const bf16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(rows + 4 * kWRow));
+        const bf16x8 wb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, wb, acc, 0, 0, 0);
       }
-    }
-    if (nb + kTok < nb_end) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qa[ks] = qn[ks];
+      for (int i = 0; i < 4; ++i) {
+        const int nn = nb + 4 * g + i;
+        if (nn >= a.N) continue;
+        const int64_t o = ((int64_t)nn * a.H + h) * ow + c0 + 16 * wave + li;
+        if (kOutF32) static_cast<float*>(a.out)[o] = acc[i];
+        else static_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[i]);
+      }
       if (rope_wg) {
 #pragma unroll
-        for (int u = 0; u < kRopePer; ++u) ra[u] = rn[u];
+        for (int u = 0; u < kRopePer; ++u) {
+          const int i = u * 64 * kWaves + threadIdx.x;
+          const int nn = nb + i / a.dr, kk = i % a.dr;
+          if (i >= kTok * a.dr || nn >= a.N) continue;
+          const int64_t r = (int64_t)nn * a.H + h;
+          if (kOutF32) static_cast<float*>(a.out)[r * ow + a.dc + kk] = bf16_bits_to_f32(ra[k][u]);
+          else static_cast<uint16_t*>(a.out)[r * ow + a.dc + kk] = ra[k][u];
+        }
       }
     }
   }
 }
 
 constexpr int kMaxLatent = 512;
+constexpr int kOutBlocks = 2;  // out_proj: token blocks whose rows are loaded together
 
 template <int NKS>  // NKS = d_latent / 32
-__global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 3) void out_proj_mfma_kernel(ProjArgs a) {
   // The token block's fp32 latent rows (16 x d_latent) are the A operand of
   // all four waves.  They are staged once per workgroup in LDS and read back
-  // per k-step, instead of each wave holding all of them in registers: that
-  // keeps the kernel near 120 VGPRs, four workgroups per CU.  The next
-  // block's rows are requested before this block's products.
+  // per k-step, instead of each wave holding all of them in registers.
   constexpr int kDc = 32 * NKS;
   constexpr int kRow = kDc * 4 + 16;  // LDS row stride: rows start 16 B apart in the bank cycle
   constexpr int kQuads = kDc / 4;     // float4 per row
@@ -221,54 +228,62 @@ __global__ __launch_bounds__(64 * kWaves) void out_proj_mfma_kernel(ProjArgs a) 
 
   // Latent rows of token block nb: thread t loads quads t, t + 256, ...
   // (indices clamped, not branched around; padding tokens read token 0).
-  float4 st[kPer];
-  auto load_rows = [&](int nb) __attribute__((always_inline)) {
+  // The rows of kOutBlocks blocks are requested together with the weights,
+  // so the workgroup waits one memory round trip for all of them.
+  float4 st[kOutBlocks][kPer];
+  auto load_rows = [&](int nb, float4 (&dst)[kPer]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int i = min(j * 64 * kWaves + (int)threadIdx.x, kChunks - 1);
       const int n = nb + i / kQuads;
-      st[j] = reinterpret_cast<const float4*>(static_cast<const float*>(a.in) +
-                                              ((int64_t)(n < a.N ? n : 0) * a.H + h) * a.dc)[i % kQuads];
+      dst[j] = reinterpret_cast<const float4*>(static_cast<const float*>(a.in) +
+                                               ((int64_t)(n < a.N ? n : 0) * a.H + h) * a.dc)[i % kQuads];
     }
   };
-  load_rows(n0);
-  __builtin_amdgcn_sched_barrier(0);  // weights and rows requested before the first wait
 
   float* out = static_cast<float*>(a.out);
   const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
-  for (int nb = n0; nb < nb_end; nb += kTok) {
+  for (int nc = n0; nc < nb_end; nc += kTok * kOutBlocks) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = j * 64 * kWaves + threadIdx.x;
-      if (i < kChunks) {
-        const int r = i / kQuads;
-        *reinterpret_cast<float4*>(o_tile + r * kRow + 16 * (i % kQuads)) =
-            nb + r < a.N ? st[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < kOutBlocks; ++k)
+      if (nc + k * kTok < nb_end) load_rows(nc + k * kTok, st[k]);
+    __builtin_amdgcn_sched_barrier(0);  // weights and rows requested before the first wait
+#pragma unroll
+    for (int k = 0; k < kOutBlocks; ++k) {
+      const int nb = nc + k * kTok;
+      if (nb >= nb_end) break;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = j * 64 * kWaves + threadIdx.x;
+        if (i < kChunks) {
+          const int r = i / kQuads;
+          *reinterpret_cast<float4*>(o_tile + r * kRow + 16 * (i % kQuads)) =
+              nb + r < a.N ? st[k][j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
-    }
-    __syncthreads();
-    if (nb + kTok < nb_end) load_rows(nb + kTok);
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const char* arow = o_tile + li * kRow + 32 * g;
+      __syncthreads();
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* arow = o_tile + li * kRow + 32 * g;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const float4 x0 = *reinterpret_cast<const float4*>(arow + 128 * ks);
-      const float4 x1 = *reinterpret_cast<const float4*>(arow + 128 * ks + 16);
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint32_t hw[4], lw[4];
+      for (int ks = 0; ks < NKS; ++ks) {
+        const float4 x0 = *reinterpret_cast<const float4*>(arow + 128 * ks);
+        const float4 x1 = *reinterpret_cast<const float4*>(arow + 128 * ks + 16);
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) split_bf16x2(x[2 * i], x[2 * i + 1], hw[i], lw[i]);
-      const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-      const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[ks], acc, 0, 0, 0);
-    }
+        for (int i = 0; i < 4; ++i) split_bf16x2(x[2 * i], x[2 * i + 1], hw[i], lw[i]);
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[ks], acc, 0, 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int nn = nb + 4 * g + i;
-      if (nn < a.N) out[((int64_t)nn * a.H + h) * a.dv + v] = acc[i];
+      for (int i = 0; i < 4; ++i) {
+        const int nn = nb + 4 * g + i;
+        if (nn < a.N) out[((int64_t)nn * a.H + h) * a.dv + v] = acc[i];
+      }
+      __syncthreads();  // the tile is rewritten for the next block
     }
-    __syncthreads();  // the tile is rewritten for the next block
   }
 }
 
@@ -297,11 +312,11 @@ bool out_proj_mfma_supported(const ProjArgs& a) {
 hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
-  // about 1024 workgroups: at 88 VGPRs and 27 KB of LDS five fit per CU, and
-  // fewer blocks per workgroup measured faster (at 256 tokens, 2 blocks:
-  // 17.6 us; 4 blocks: 19.5 us)
-  a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx, 1024);
-  cap_token_groups(a, a.dc / kCols, gx, 5);
+  // One round of workgroups: three fit per CU (53 KB of LDS and 160 VGPRs
+  // with d_nope = 192), and a workgroup's token blocks (up to four) cost one
+  // memory round trip together.
+  a.tok_blocks = token_blocks(a.N, a.dc / kCols, a.H, gx, 768);
+  cap_token_groups(a, a.dc / kCols, gx, 3);
   a.tok_groups = (int)gx;
   const dim3 grid(proj_grid(a.dc / kCols, a.tok_groups, a.H));
   switch (a.dn / 32) {
@@ -321,8 +336,10 @@ hipError_t launch_absorb_mfma(const ProjArgs& args, hipStream_t s) {
 hipError_t launch_out_proj_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
-  a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx, 512);
-  cap_token_groups(a, a.dv / kCols, gx, 4);
+  // One round of workgroups (three per CU at 164 VGPRs); a workgroup's rows
+  // of two token blocks cost one memory round trip together.
+  a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx, 768);
+  cap_token_groups(a, a.dv / kCols, gx, 3);
   a.tok_groups = (int)gx;
   const dim3 grid(proj_grid(a.dv / kCols, a.tok_groups, a.H));
   switch (a.dc / 32) {

@@ -170,11 +170,13 @@ def test_out_proj(name):
 
 @pytest.mark.parametrize("name,batch", [("ragged_b256_h20_ctx512_8k_bf16", 100),
                                         ("ragged_b256_h20_ctx512_8k_bf16", 200),
+                                        ("ragged_b256_h20_ctx512_8k_bf16", 700),
                                         ("fp8_mtp4_b64_h20_ctx16k", 25)])
 def test_projections_partial_token_blocks(name, batch):
-    """Token counts (100, 200) that end in a partial 16-token block and split
-    unevenly over the workgroups that each keep one weight slice for several
-    token blocks."""
+    """Token counts (100, 200, 700) that end in a partial 16-token block and
+    split unevenly over the workgroups that each keep one weight slice for
+    several token blocks (700: more blocks per workgroup than it loads at
+    once, so the staging tiles are reused)."""
     import mla_paged_decode_amd as mla
     from mla_paged_decode_amd.step import DeviceBatch
     wl = WORKLOADS[name].with_(batch=batch, lens=("const", 16))
