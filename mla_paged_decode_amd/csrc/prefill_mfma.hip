@@ -162,17 +162,32 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
   __shared__ __attribute__((aligned(16))) char pl[kWaves][kAQ * kPRowB];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
-  const int h = blockIdx.y;
   const int nqb = (a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves);
-  const int split = blockIdx.x % a.splits, qblk = blockIdx.x / a.splits;
-  const int b = qblk / nqb, qb = qblk % nqb;
+  // XCD-aware order (workgroups go round-robin over the 8 XCDs, each with its
+  // own L2): the nqb query blocks of one (sequence, head, key split) read the
+  // same keys and values, so they run on one XCD, one after another in its
+  // dispatch order, and share its L2.  Unit u = (b * H + h) * splits + split
+  // goes to XCD u % 8.
+  int h, split, b, qb;
+  {
+    const int x8 = blockIdx.x % 8, k = blockIdx.x / 8;
+    const int u = 8 * (k / nqb) + x8;
+    if (u >= a.B * a.H * a.splits) return;  // no barrier precedes this
+    qb = k % nqb;
+    split = u % a.splits;
+    h = (u / a.splits) % a.H;
+    b = u / (a.splits * a.H);
+  }
   const int iw = qb * kAQ * kWaves + kAQ * wave;  // the wave's first query
   const int L = (int)min((int64_t)max(a.seq_lens[b], 0), a.Lcap);
   const int ig_end = min(a.Sq, (qb + 1) * kAQ * kWaves);
   // Keys the workgroup's queries see: [0, n_keys); this split takes
-  // [k_begin, blk_last] of them, a whole number of key blocks.
+  // [k_begin, blk_last] of them, a whole number of key blocks.  The split
+  // boundaries come from the sequence's L keys (what its last query sees),
+  // so every query block of the sequence cuts the keys at the same places
+  // and the blocks' reads of a split coincide in L2.
   const int n_keys = max(0, min(L, L - a.Sq + ig_end));
-  const int chunk = ((n_keys + a.splits - 1) / a.splits + kAKeys - 1) / kAKeys * kAKeys;
+  const int chunk = ((L + a.splits - 1) / a.splits + kAKeys - 1) / kAKeys * kAKeys;
   const int k_begin = split * chunk;
   const int blk_last = min(n_keys, k_begin + chunk) - 1;  // this split's last key
 
@@ -416,8 +431,11 @@ int prefill_attn_splits(int B, int Sq, int H, int64_t Lcap, int dn, int dr, int 
 hipError_t launch_prefill_attn_mfma(const PrefillArgs& a, hipStream_t s) {
   if (!prefill_attn_mfma_supported(a) || a.splits < 1 || (a.splits > 1 && (!a.part_o || !a.part_lse)))
     return hipErrorInvalidValue;
-  const unsigned qb = (unsigned)((a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves));
-  prefill_attn_mfma_kernel<<<dim3((unsigned)a.B * qb * (unsigned)a.splits, (unsigned)a.H), 64 * kWaves, 0, s>>>(a);
+  const int64_t qb = (a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves);
+  const int64_t units = (int64_t)a.B * a.H * a.splits;
+  const int64_t grid = 8 * qb * ((units + 7) / 8);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  prefill_attn_mfma_kernel<<<dim3((unsigned)grid), 64 * kWaves, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   prefill_merge_kernel<<<dim3((unsigned)(a.B * a.Sq), (unsigned)a.H), kAD, 0, s>>>(a);
