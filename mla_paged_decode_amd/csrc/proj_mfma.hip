@@ -199,24 +199,26 @@ __global__ __launch_bounds__(64 * kWaves) void absorb_mfma_kernel(ProjArgs a) {
 }
 
 constexpr int kMaxLatent = 512;
-constexpr int kOutBlocks = 2;  // out_proj: token blocks whose rows are loaded together
 
-template <int NKS>  // NKS = d_latent / 32
-__global__ __launch_bounds__(64 * kWaves, 3) void out_proj_mfma_kernel(ProjArgs a) {
+// out_proj: NW waves of 16 value columns each, NB token blocks whose rows
+// are requested together with the weights (one memory round trip).
+template <int NKS, int NW, int NB>  // NKS = d_latent / 32
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void out_proj_mfma_kernel(ProjArgs a) {
   // The token block's fp32 latent rows (16 x d_latent) are the A operand of
-  // all four waves.  They are staged once per workgroup in LDS and read back
+  // all the waves.  They are staged once per workgroup in LDS and read back
   // per k-step, instead of each wave holding all of them in registers.
+  constexpr int kC = 16 * NW;  // value columns per workgroup
   constexpr int kDc = 32 * NKS;
   constexpr int kRow = kDc * 4 + 16;  // LDS row stride: rows start 16 B apart in the bank cycle
   constexpr int kQuads = kDc / 4;     // float4 per row
   constexpr int kChunks = kTok * kQuads;
-  constexpr int kPer = (kChunks + 64 * kWaves - 1) / (64 * kWaves);
+  constexpr int kPer = (kChunks + 64 * NW - 1) / (64 * NW);
   __shared__ __attribute__((aligned(16))) char o_tile[kTok * kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, li = lane & 15;
-  const ProjCell cell = proj_cell(a.dv / kCols, a.tok_groups, a.H);
+  const ProjCell cell = proj_cell(a.dv / kC, a.tok_groups, a.H);
   if (!cell.valid) return;
-  const int h = cell.h, v = cell.col_group * kCols + 16 * wave + li;
+  const int h = cell.h, v = cell.col_group * kC + 16 * wave + li;
   const int n0 = cell.tok_group * kTok * a.tok_blocks;
   const uint16_t* w = static_cast<const uint16_t*>(a.w) + ((int64_t)h * (a.dn + a.dv) + a.dn + v) * a.dc;
 
@@ -226,15 +228,13 @@ __global__ __launch_bounds__(64 * kWaves, 3) void out_proj_mfma_kernel(ProjArgs 
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) wb[ks] = load_bf16x8(w + 32 * ks + 8 * g);
 
-  // Latent rows of token block nb: thread t loads quads t, t + 256, ...
+  // Latent rows of token block nb: thread t loads quads t, t + 64 NW, ...
   // (indices clamped, not branched around; padding tokens read token 0).
-  // The rows of kOutBlocks blocks are requested together with the weights,
-  // so the workgroup waits one memory round trip for all of them.
-  float4 st[kOutBlocks][kPer];
+  float4 st[NB][kPer];
   auto load_rows = [&](int nb, float4 (&dst)[kPer]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int i = min(j * 64 * kWaves + (int)threadIdx.x, kChunks - 1);
+      const int i = min(j * 64 * NW + (int)threadIdx.x, kChunks - 1);
       const int n = nb + i / kQuads;
       dst[j] = reinterpret_cast<const float4*>(static_cast<const float*>(a.in) +
                                                ((int64_t)(n < a.N ? n : 0) * a.H + h) * a.dc)[i % kQuads];
@@ -243,18 +243,18 @@ __global__ __launch_bounds__(64 * kWaves, 3) void out_proj_mfma_kernel(ProjArgs 
 
   float* out = static_cast<float*>(a.out);
   const int nb_end = min(a.N, n0 + kTok * a.tok_blocks);
-  for (int nc = n0; nc < nb_end; nc += kTok * kOutBlocks) {
+  for (int nc = n0; nc < nb_end; nc += kTok * NB) {
 #pragma unroll
-    for (int k = 0; k < kOutBlocks; ++k)
+    for (int k = 0; k < NB; ++k)
       if (nc + k * kTok < nb_end) load_rows(nc + k * kTok, st[k]);
     __builtin_amdgcn_sched_barrier(0);  // weights and rows requested before the first wait
 #pragma unroll
-    for (int k = 0; k < kOutBlocks; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const int nb = nc + k * kTok;
       if (nb >= nb_end) break;
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
-        const int i = j * 64 * kWaves + threadIdx.x;
+        const int i = j * 64 * NW + threadIdx.x;
         if (i < kChunks) {
           const int r = i / kQuads;
           *reinterpret_cast<float4*>(o_tile + r * kRow + 16 * (i % kQuads)) =
@@ -337,14 +337,16 @@ hipError_t launch_out_proj_mfma(const ProjArgs& args, hipStream_t s) {
   ProjArgs a = args;
   unsigned gx;
   // One round of workgroups (three per CU at 164 VGPRs); a workgroup's rows
-  // of two token blocks cost one memory round trip together.
+  // of two token blocks cost one memory round trip together.  (Eight-wave
+  // workgroups with four blocks, one per CU, halve the L2 traffic but
+  // measured slower at 256 tokens: 18.2-20.9 us against 15.9-18.7 us.)
   a.tok_blocks = token_blocks(a.N, a.dv / kCols, a.H, gx, 768);
   cap_token_groups(a, a.dv / kCols, gx, 3);
   a.tok_groups = (int)gx;
   const dim3 grid(proj_grid(a.dv / kCols, a.tok_groups, a.H));
   switch (a.dc / 32) {
 #define MLA_CASE(K) \
-  case K: out_proj_mfma_kernel<K><<<grid, 64 * kWaves, 0, s>>>(a); break;
+  case K: out_proj_mfma_kernel<K, kWaves, 2><<<grid, 64 * kWaves, 0, s>>>(a); break;
     MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7) MLA_CASE(8)
     MLA_CASE(9) MLA_CASE(10) MLA_CASE(11) MLA_CASE(12) MLA_CASE(13) MLA_CASE(14) MLA_CASE(15) MLA_CASE(16)
 #undef MLA_CASE
