@@ -94,7 +94,8 @@ def cpu_baseline(wl, target_s: float):
     }
 
 
-COUNTER_SOURCES = ["decode_mfma.hip", "decode_fp8.hip", "decode_common.h", "schedule.h", "internal.h", "device_common.h"]
+COUNTER_SOURCES = ["decode_mfma.hip", "decode_fp8.hip", "decode_common.h", "staging_bf16.h", "merge_fused.h",
+                   "schedule.h", "internal.h", "device_common.h"]
 
 
 def code_without_comments(text: str) -> str:

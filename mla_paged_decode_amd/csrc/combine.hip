@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void combine_stream_kernel(Decod
 
 // Merge for the tiled partial layout when sequences have many parts: one
 // workgroup of SPLIT waves per (sequence, 16-row block, 16-column block).
-// Wave k folds parts k, k + SPLIT, ... (kStreamBatch at a time, loads in
+// Wave k folds parts k, k + SPLIT, ... (BATCH at a time, loads in
 // flight together) into per-lane running maxima, sums and weighted sums as
 // the streaming merge does; the SPLIT states are then merged through LDS.
 template <int SPLIT, int BATCH>
@@ -606,13 +606,12 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
     }
     // Many parts (long sequences over few workers each): the parts of each
     // 16 x 16 output cell split over the 16 waves of a workgroup.
-    // Each wave reads its parts in one batch up to 12 per wave (192 parts).
+    // Four parts per wave at a time: larger batches spill at the 128
+    // registers a 16-wave workgroup leaves each wave (129 parts: 8 per wave
+    // 14.3-17.2 us, 12 per wave 28.4-31 us, 4 per wave 13.2-16.3 us).
     if (parts > kSplitMinParts) {
       const dim3 grid((unsigned)a.B, (unsigned)((a.R + 15) / 16), (unsigned)kdb);
-      const int64_t per_wave = (parts + 15) / 16;
-      if (per_wave <= 4) combine_split_kernel<16, 4><<<grid, 64 * 16, 0, s>>>(a);
-      else if (per_wave <= 8) combine_split_kernel<16, 8><<<grid, 64 * 16, 0, s>>>(a);
-      else combine_split_kernel<16, 12><<<grid, 64 * 16, 0, s>>>(a);
+      combine_split_kernel<16, 4><<<grid, 64 * 16, 0, s>>>(a);
       return hipGetLastError();
     }
     // Otherwise about 1024 workgroups: DPW column blocks per workgroup, a
