@@ -423,12 +423,17 @@ def decode_timing(wl, splits: int, qd: int, kernel: int, reps: int, cache_bytes:
         for x in e:
             x.record()
     torch.cuda.synchronize()
+    # the decode calls, then the attention kernels (events between the
+    # attention and merge kernels would delay the merge)
     for i, e in enumerate(evs):
         step.params.kv_pool = pools[i % copies].data_ptr()
         e[0].record()
-        step.params.kernel_start_event, step.params.kernel_stop_event = e[2].cuda_event, e[3].cuda_event
         step.decode()
         e[1].record()
+    for i, e in enumerate(evs):
+        step.params.kv_pool = pools[i % copies].data_ptr()
+        step.params.kernel_start_event, step.params.kernel_stop_event = e[2].cuda_event, e[3].cuda_event
+        step.decode()
     step.params.kernel_start_event = step.params.kernel_stop_event = None
     torch.cuda.synchronize()
     call_us = sum(e[0].elapsed_time(e[1]) for e in evs) / reps * 1e3
@@ -544,18 +549,23 @@ def main() -> int:
     unique_bytes = pool_bytes  # every page of the pool is referenced once or more
     q_tokens = wl.n_tokens
 
-    def one_step(i, ev=None):
+    def one_step(i, ev=None, kernel_ev=None):
+        """One step; ev = (start, stop) events around the decode call, or
+        kernel_ev = (start, stop) events the library records around the
+        attention kernel (never both: events between the attention and merge
+        kernels delay the merge and would inflate the call's time)."""
         step.params.kv_pool = pools[i % copies].data_ptr()
         step.absorb()
         if ev is not None:
             ev[0].record()
-            step.params.kernel_start_event = ev[2].cuda_event
-            step.params.kernel_stop_event = ev[3].cuda_event
+        if kernel_ev is not None:
+            step.params.kernel_start_event = kernel_ev[0].cuda_event
+            step.params.kernel_stop_event = kernel_ev[1].cuda_event
         step.decode()
         if ev is not None:
             ev[1].record()
-            step.params.kernel_start_event = None
-            step.params.kernel_stop_event = None
+        step.params.kernel_start_event = None
+        step.params.kernel_stop_event = None
         step.project()
 
     for i in range(args.warmup):
@@ -590,16 +600,19 @@ def main() -> int:
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
-    # Timed region 2 (the roofline): eager steps; per step the decode call
-    # (attention + merge) and, recorded by the library on the launch stream,
-    # the attention kernel alone.
+    # Timed region 2 (the roofline): eager steps, twice: first with events
+    # around each decode call (attention + merge), then with the events the
+    # library records on the launch stream around the attention kernel alone.
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(args.steps)]
     for e in evs:
         for x in e:
             x.record()  # creates the underlying HIP event
     torch.cuda.synchronize()
     for i in range(args.steps):
-        one_step(i, evs[i])
+        one_step(i, ev=evs[i][:2])
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        one_step(i, kernel_ev=evs[i][2:])
     torch.cuda.synchronize()
     decode_ms = [e[0].elapsed_time(e[1]) for e in evs]
     kernel_ms = [e[2].elapsed_time(e[3]) for e in evs]
