@@ -69,6 +69,76 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_expand_mfma_kernel(Prefil
   for (int ks = 0; ks < NKS; ++ks)
     wb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(w + 32 * ks + 8 * g));
 
+  // bf16 cache: the rows of the next two blocks are in flight while a block
+  // is computed.  A 16-token block (its start is a multiple of 16, and
+  // page_block is a power of two >= 16) lies in one page: one scalar page
+  // lookup per block, all made up front.  Thread t carries 16-byte chunk
+  // t % (kDc / 8) of rows t / (kDc / 8) + (256 / (kDc / 8)) j of each block.
+  constexpr int kChunksPerRow = kDc / 8;
+  constexpr int kRowsPerPass = 64 * kWaves / kChunksPerRow;
+  constexpr int kRawPer = kTokBlk / kRowsPerPass;  // chunks per thread and block
+  constexpr int kAhead = 2;
+  const bool pipelined = FMT == kBF16 && (64 * kWaves) % kChunksPerRow == 0 && kRowsPerPass <= kTokBlk;
+  if constexpr (FMT == kBF16) {
+    if (pipelined) {
+      const int nblk = (t_end - t_begin + kTokBlk - 1) / kTokBlk;
+      const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+      int pg[kBlocks];
+#pragma unroll
+      for (int k = 0; k < kBlocks; ++k) pg[k] = k < nblk ? bt[(t_begin + k * kTokBlk) / a.P] : 0;
+      const int c8 = tid % kChunksPerRow, r0 = tid / kChunksPerRow;
+      uint4 raw[kAhead + 1][kRawPer];
+      auto load = [&](int k, uint4 (&dst)[kRawPer]) __attribute__((always_inline)) {
+        const int t0 = t_begin + k * kTokBlk;
+        const uint8_t* base = a.pool + ((int64_t)pg[k] * a.P + (t0 & (a.P - 1))) * a.row_bytes + 16 * c8;
+#pragma unroll
+        for (int j = 0; j < kRawPer; ++j)  // rows past the sequence stay inside the block's page
+          dst[j] = *reinterpret_cast<const uint4*>(base + (int64_t)(r0 + kRowsPerPass * j) * a.row_bytes);
+      };
+#pragma unroll
+      for (int k = 0; k < kAhead; ++k)
+        if (k < nblk) load(k, raw[k]);
+#pragma unroll
+      for (int k = 0; k < kBlocks; ++k) {
+        if (k >= nblk) break;
+        const int t0 = t_begin + k * kTokBlk;
+        if (k + kAhead < nblk) load(k + kAhead, raw[(k + kAhead) % (kAhead + 1)]);
+#pragma unroll
+        for (int j = 0; j < kRawPer; ++j) {
+          const int r = r0 + kRowsPerPass * j;
+          *reinterpret_cast<uint4*>(hi_tile + r * kRowB + 16 * c8) =
+              t0 + r < t_end ? raw[k % (kAhead + 1)][j] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (h == 0 && blockIdx.y == 0)  // the shared RoPE keys, once per token
+          for (int idx = tid; idx < kTokBlk * a.dr; idx += 64 * kWaves) {
+            const int r = idx / a.dr, i = idx % a.dr, t = t0 + r;
+            if (t < t_end) {
+              const uint8_t* row = a.pool + ((int64_t)pg[k] * a.P + (t & (a.P - 1))) * a.row_bytes;
+              a.kr[((int64_t)b * a.Lcap + t) * a.dr + i] = any_value<FMT>(row, a.dc + i, nv);
+            }
+          }
+        __syncthreads();
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* hrow = hi_tile + li * kRowB + 16 * g;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(hrow + 64 * ks));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[ks], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 4 * g + i;
+          if (t < t_end) {
+            const int64_t tok = ((int64_t)b * a.Lcap + t) * a.H + h;
+            if (col < a.dn) a.kn[tok * a.dn + col] = acc[i];
+            else a.v[tok * a.dv + (col - a.dn)] = acc[i];
+          }
+        }
+        __syncthreads();  // the tile is rewritten by the next block
+      }
+      return;
+    }
+  }
   for (int t0 = t_begin; t0 < t_end; t0 += kTokBlk) {
     // bf16 tile of the block's latent rows (rows past the end are zero)
     for (int idx = tid; idx < kTokBlk * (kDc / 8); idx += 64 * kWaves) {
