@@ -46,6 +46,25 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return bf16x
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Maximum and sum over the four 16-lane rows of a wave at each lane's
+// position in its row (what x op shfl_xor(x, 16) op shfl_xor(x, 32) gives),
+// with gfx950's row-swap permutes: VALU operations instead of LDS permutes.
+// After a swap of x with itself, every lane holds its own row's value and
+// its partner row's (rows r and r ^ 1, then halves h and h ^ 1), so the
+// results equal the shuffle forms exactly (both operations commute).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Source of one tile: tokens [tt0, tt0 + n) of the current sequence.  Work
 // units start at multiples of kTile tokens and page_block is a power of two
 // >= 16, so the tile lies in one page (page_block >= 32) or two (16).  Tile

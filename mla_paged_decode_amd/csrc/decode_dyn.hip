@@ -467,8 +467,7 @@ __global__ __launch_bounds__(64 * NW) void decode_dyn_kernel(DecodeArgs a) {
           sv[tb2][i] = ok ? s[tb2][i] * a.scale_log2 : -INFINITY;
           mx = fmaxf(mx, sv[tb2][i]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_rows(mx);
       if constexpr (kRescale) {
         const bool raise = mx > m + 8.f;
         if (__any(raise)) {
@@ -500,8 +499,7 @@ __global__ __launch_bounds__(64 * NW) void decode_dyn_kernel(DecodeArgs a) {
           if constexpr (HILO) split_bf16x2(e0, e1, pk[2 * tb2 + i / 2], pl[2 * tb2 + i / 2]);
           else pk[2 * tb2 + i / 2] = bf16x2_bits(e0, e1);
         }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
+      psum = sum_over_rows(psum);
       lsum += psum;
       const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
       bf16x8 pa_lo = pa;

@@ -572,8 +572,7 @@ __global__ __launch_bounds__(64 * NW, raw_depth<RB>() == 2 ? 2 : 1) void decode_
             sv[tb][i] = ok ? s[tb][i] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[tb][i]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_rows(mx);
         int flag = 0;
         if constexpr (kRescale) {
           const bool raise = mx > m + 8.f;  // also true when m = -inf < mx
@@ -601,8 +600,7 @@ __global__ __launch_bounds__(64 * NW, raw_depth<RB>() == 2 ? 2 : 1) void decode_
               psum += e0 + e1;
               pk[2 * tb + i / 2] = pack_bf16(e0, e1);
             }
-          psum += __shfl_xor(psum, 16);
-          psum += __shfl_xor(psum, 32);
+          psum = sum_over_rows(psum);
           lsum += psum;
           *(lds_u32x4*)(pbuf + (wave * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
         }
@@ -939,8 +937,7 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
             sv[tb][i] = ok ? s[tb][i] * a.scale_log2 : -INFINITY;
             mx = fmaxf(mx, sv[tb][i]);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_over_rows(mx);
         const bool raise = mx > m + 8.f;  // also true when m = -inf < mx
         const int flag = __any(raise) ? 1 : 0;
         float alpha = 1.f;
@@ -961,8 +958,7 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
             psum += e0 + e1;
             pk[2 * tb + i / 2] = pack_bf16(e0, e1);
           }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
+        psum = sum_over_rows(psum);
         lsum += psum;
         *(lds_u32x4*)((lds_char*)p_mem[pb] + (wave * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
         if (g == 0) s_alpha[pb][wave][li] = alpha;
