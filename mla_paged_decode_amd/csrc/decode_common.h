@@ -58,6 +58,28 @@ __device__ __forceinline__ float max_over_rows(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Maximum and sum over the 16 lanes of each row, every lane of the row
+// getting the row's result, with DPP lane moves on the VALU instead of LDS
+// permutes: swaps within quads (lanes 1 0 3 2, then 2 3 0 1), then the
+// half-row mirror (lane i of 8 takes 7 - i) and the row mirror (i of 16
+// takes 15 - i), each pairing two already-reduced groups.  The sum's order
+// of additions differs from a xor butterfly's.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float max_in_row(float x) {
+  x = fmaxf(x, dpp_move<0xB1>(x));
+  x = fmaxf(x, dpp_move<0x4E>(x));
+  x = fmaxf(x, dpp_move<0x141>(x));
+  return fmaxf(x, dpp_move<0x140>(x));
+}
+__device__ __forceinline__ float sum_in_row(float x) {
+  x += dpp_move<0xB1>(x);
+  x += dpp_move<0x4E>(x);
+  x += dpp_move<0x141>(x);
+  return x + dpp_move<0x140>(x);
+}
 __device__ __forceinline__ float sum_over_rows(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);

@@ -372,7 +372,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       float s0 = t0 + li <= last ? sc[0][r] * a.scale_log2 : -INFINITY;
       float s1 = t0 + 16 + li <= last ? sc[1][r] * a.scale_log2 : -INFINITY;
       float mx = fmaxf(s0, s1);
-      for (int o2 = 8; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+      mx = mfma::max_in_row(mx);
       const float m_new = fmaxf(m[r], mx);
       float al = 1.f, p0 = 0.f, p1 = 0.f;
       if (m_new != -INFINITY) {
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
         p1 = s1 == -INFINITY ? 0.f : exp2f(s1 - m_new);
       }
       float ps = p0 + p1;
-      for (int o2 = 8; o2 >= 1; o2 >>= 1) ps += __shfl_xor(ps, o2);
+      ps = mfma::sum_in_row(ps);
       l[r] = l[r] * al + ps;
       m[r] = m_new;
       alpha[r] = al;
