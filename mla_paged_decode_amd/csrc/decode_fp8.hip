@@ -1037,14 +1037,18 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
             else pages_next = tile_pages(a, bt, t0 + (xn + 1) * kTile, t1);
           }
         }
+        // Owners score first (their scores gate the next step), the other
+        // waves accumulate first (their V decode is needed only next step):
+        // measured 2% faster than both roles accumulating last.
         if constexpr (kOwner) {
           if (x < ntiles) score(x);
+          if (s >= 0) pv(s);
         } else {
+          if (s >= 0) pv(s);
           if (x < ntiles)
             decode_v_fp8<SPARSE, 64 * kWk>(raws + (x % kRaw) * kRawBuf, (lds_char*)v_mem[x & 1],
                                           SPARSE ? s_mask[x % kRaw] : ~0u, threadIdx.x - 64 * RB);
         }
-        if (s >= 0) pv(s);
       }
 
       // ---- normalise and write this unit's partials (tiled layout) ----
