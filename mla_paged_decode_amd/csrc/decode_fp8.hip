@@ -901,22 +901,28 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
           return i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         };
         // S^T = K . Q^T, one accumulation chain per token block.  The next
-        // step's K rows are read while this step's products run; the empty
-        // asm statements keep that order (the compiler would otherwise read
-        // all K rows first and run out of registers).
+        // step's K rows are requested before this step's products, so they
+        // arrive while those run; the empty asm statements keep the steps
+        // apart (the compiler would otherwise read all K rows first and run
+        // out of registers).
         f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         i32x8 ka[2] = {load_k(0, 0), load_k(0, 1)};
 #pragma unroll
         for (int ks = 0; ks < kSteps; ++ks) {
+          i32x8 kn[2];
+          if (ks + 1 < kSteps) {
+            kn[0] = load_k(ks + 1, 0);
+            kn[1] = load_k(ks + 1, 1);
+          }
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             s[tb] = mfma_mx(ks, ka[tb], mq.hi[ks], s[tb], ska[tb], mq.sh);
             s[tb] = mfma_mx(ks, ka[tb], mq.lo[ks], s[tb], ska[tb], mq.sl);
           }
           if (ks + 1 < kSteps) {
-            ka[0] = load_k(ks + 1, 0);
-            ka[1] = load_k(ks + 1, 1);
             asm volatile("" ::"v"(s[0]), "v"(s[1]) : "memory");
+            ka[0] = kn[0];
+            ka[1] = kn[1];
           }
         }
         // online softmax of the owned rows
@@ -970,6 +976,11 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
       // transposed (ds_read_tr16_b64), as the B operand.
       auto pv = [&](int x) __attribute__((always_inline)) {
         const int pb = x & 1;
+        // P is requested before the branches on the rescale flags, so its
+        // LDS round trip overlaps theirs.
+        bf16x8 pa[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) pa[r] = *(const lds_bf16x8*)((const lds_char*)p_mem[pb] + (r * 64 + lane) * 16);
 #pragma unroll
         for (int r = 0; r < RB; ++r)
           if (uniform(s_flag[pb][r])) {
@@ -982,9 +993,6 @@ __global__ __launch_bounds__(64 * kMxWaves, 1) void decode_fp8_mx_kernel(DecodeA
               acc[r][d][3] *= al4[3];
             }
           }
-        bf16x8 pa[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) pa[r] = *(const lds_bf16x8*)((const lds_char*)p_mem[pb] + (r * 64 + lane) * 16);
         const int tok = 4 * g + (li >> 2);  // and tok + 16 (same swizzle)
         const int xs = swz(tok);
         const lds_char* const vb0 =
