@@ -216,7 +216,7 @@ constexpr int kAQ = 16;        // queries per wave
 constexpr int kAKeys = 32;     // keys per block
 constexpr int kAD = 256;       // key and value width
 constexpr int kKRowB = kAD * 2 + 16;      // K tile row stride (bytes)
-constexpr int kVRowB = kAKeys * 2 + 16;   // transposed V tile row stride (bytes)
+constexpr int kVRowB = kAD * 2 + 32;      // V tile row stride (bytes): 4 rows land 32 B apart in the banks
 constexpr int kPRowB = kAKeys * 2 + 16;   // P tile row stride (bytes)
 
 __device__ __forceinline__ bf16x8 lds_b8(const char* p) {
@@ -226,8 +226,8 @@ __device__ __forceinline__ bf16x8 lds_b8(const char* p) {
 __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char kh[kAKeys * kKRowB];
   __shared__ __attribute__((aligned(16))) char kl[kAKeys * kKRowB];
-  __shared__ __attribute__((aligned(16))) char vth[kAD * kVRowB];
-  __shared__ __attribute__((aligned(16))) char vtl[kAD * kVRowB];
+  __shared__ __attribute__((aligned(16))) char vh_t[kAKeys * kVRowB];
+  __shared__ __attribute__((aligned(16))) char vl_t[kAKeys * kVRowB];
   __shared__ __attribute__((aligned(16))) char ph[kWaves][kAQ * kPRowB];
   __shared__ __attribute__((aligned(16))) char pl[kWaves][kAQ * kPRowB];
   const int tid = threadIdx.x;
@@ -295,8 +295,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
   // holds K chunks (key r, dims 4c .. 4c + 3) for idx = tid + 256 j and V
   // chunks (keys 2 rp, 2 rp + 1, dims 4c .. 4c + 3) likewise.
   constexpr int kKPer = kAKeys * (kAD / 4) / (64 * kWaves);        // 8
-  constexpr int kVPer = (kAKeys / 2) * (kAD / 4) / (64 * kWaves);  // 4
-  float4 kx[kKPer], vx0[kVPer], vx1[kVPer];
+  float4 kx[kKPer], vx[kKPer];
   auto load_block = [&](int t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kKPer; ++j) {
@@ -306,12 +305,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
                            : reinterpret_cast<const float4*>(a.kr + ((int64_t)b * a.Lcap + t) * a.dr)[c - a.dn / 4];
     }
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
+    for (int j = 0; j < kKPer; ++j) {
       const int idx = tid + 64 * kWaves * j;
-      const int rp = idx / (kAD / 4), c = idx % (kAD / 4);
-      const int t = min(t0 + 2 * rp, blk_last), t1 = min(t0 + 2 * rp + 1, blk_last);
-      vx0[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c];
-      vx1[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t1) * a.H + h) * a.dv)[c];
+      const int r = idx / (kAD / 4), c = idx % (kAD / 4), t = min(t0 + r, blk_last);
+      vx[j] = reinterpret_cast<const float4*>(a.v + (((int64_t)b * a.Lcap + t) * a.H + h) * a.dv)[c];
     }
   };
   if (k_begin <= blk_last) load_block(k_begin);
@@ -332,19 +329,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       *reinterpret_cast<uint2*>(kl + r * kKRowB + 8 * c) = make_uint2(l0, l1);
     }
 #pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
+    for (int j = 0; j < kKPer; ++j) {
       const int idx = tid + 64 * kWaves * j;
-      const int rp = idx / (kAD / 4), c = idx % (kAD / 4);
-      const float4 x0 = t0 + 2 * rp <= blk_last ? vx0[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 x1 = t0 + 2 * rp + 1 <= blk_last ? vx1[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float v0[4] = {x0.x, x0.y, x0.z, x0.w}, v1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t hw, lw;
-        split_bf16x2(v0[q], v1[q], hw, lw);
-        *reinterpret_cast<uint32_t*>(vth + (4 * c + q) * kVRowB + 4 * rp) = hw;
-        *reinterpret_cast<uint32_t*>(vtl + (4 * c + q) * kVRowB + 4 * rp) = lw;
-      }
+      const int r = idx / (kAD / 4), c = idx % (kAD / 4);
+      const float4 x = t0 + r <= blk_last ? vx[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      uint32_t h0, l0, h1, l1;
+      split_bf16x2(x.x, x.y, h0, l0);
+      split_bf16x2(x.z, x.w, h1, l1);
+      *reinterpret_cast<uint2*>(vh_t + r * kVRowB + 8 * c) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(vl_t + r * kVRowB + 8 * c) = make_uint2(l0, l1);
     }
     __syncthreads();
     if (t0 + kAKeys <= blk_last) load_block(t0 + kAKeys);  // in flight during this block's products
@@ -405,13 +398,31 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       for (int r = 0; r < 4; ++r) o[d][r] *= alpha[r];
     __syncthreads();  // P tiles written
 
-    // O += P V: A = P (row li, keys 8 g ..), B = V^T rows (dim 16 d + li)
-    const bf16x8 pah = lds_b8(ph[wave] + li * kPRowB + 16 * g);
-    const bf16x8 pal = lds_b8(pl[wave] + li * kPRowB + 16 * g);
+    // O += P V.  B operand of column block d: V is key-major in LDS and read
+    // transposed (ds_read_b64_tr_b16): lane li of group g reads the 4 values
+    // of row 4 g + li / 4 (and 16 rows on), columns 16 d + 4 (li % 4) .. + 3,
+    // and the 16-lane transpose hands it column 16 d + li of keys 4 g .. 4 g + 3
+    // and 16 + 4 g .. 16 + 4 g + 3.  The A operand (P, row li) takes its
+    // keys in the same order.
+    auto p8 = [&](const char* t) {
+      const uint2 x0 = *reinterpret_cast<const uint2*>(t + li * kPRowB + 8 * g);
+      const uint2 x1 = *reinterpret_cast<const uint2*>(t + li * kPRowB + 32 + 8 * g);
+      return __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
+    };
+    const bf16x8 pah = p8(ph[wave]);
+    const bf16x8 pal = p8(pl[wave]);
+    const int vrow = 4 * g + (li >> 2), vcol = 8 * (li & 3);  // bytes within the column block
+    auto v8 = [&](const char* t, int d) {
+      const char* p0 = t + vrow * kVRowB + 32 * d + vcol;
+      typedef __attribute__((address_space(3))) mfma::bf16x4 lds_b4;
+      const mfma::bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p0));
+      const mfma::bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p0 + 16 * kVRowB));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 #pragma unroll
     for (int d = 0; d < kAD / 16; ++d) {
-      const bf16x8 vh = lds_b8(vth + (16 * d + li) * kVRowB + 16 * g);
-      const bf16x8 vl = lds_b8(vtl + (16 * d + li) * kVRowB + 16 * g);
+      const bf16x8 vh = v8(vh_t, d);
+      const bf16x8 vl = v8(vl_t, d);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vh, o[d], 0, 0, 0);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vl, o[d], 0, 0, 0);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vh, o[d], 0, 0, 0);
