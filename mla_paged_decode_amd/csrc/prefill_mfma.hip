@@ -209,15 +209,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_expand_mfma_kernel(Prefil
 // keys in blocks of 32 staged in LDS once for all of them.  Every fp32
 // operand is split into bf16 hi + lo and each product takes three MFMAs
 // (hi.hi + hi.lo + lo.hi), which keeps the result at fp32-level accuracy:
-//   S = Q K^T: A = the wave's queries (registers), B = K rows (LDS);
-//   online softmax per query row in the S layout (lane = key, 4 rows);
-//   P goes through LDS to the A layout; O += P V with V transposed in LDS.
+//   S^T = K Q^T: A = K rows (LDS), B = the wave's queries (registers);
+//   online softmax per query (lane li = query, 8 keys per lane);
+//   O += P V with P from registers (the S^T layout is PV's A layout) and V
+//   read from its key-major LDS tile with transposing loads.
 constexpr int kAQ = 16;        // queries per wave
 constexpr int kAKeys = 32;     // keys per block
 constexpr int kAD = 256;       // key and value width
 constexpr int kKRowB = kAD * 2 + 16;      // K tile row stride (bytes)
 constexpr int kVRowB = kAD * 2 + 32;      // V tile row stride (bytes): 4 rows land 32 B apart in the banks
-constexpr int kPRowB = kAKeys * 2 + 16;   // P tile row stride (bytes)
 
 __device__ __forceinline__ bf16x8 lds_b8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -228,8 +228,6 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
   __shared__ __attribute__((aligned(16))) char kl[kAKeys * kKRowB];
   __shared__ __attribute__((aligned(16))) char vh_t[kAKeys * kVRowB];
   __shared__ __attribute__((aligned(16))) char vl_t[kAKeys * kVRowB];
-  __shared__ __attribute__((aligned(16))) char ph[kWaves][kAQ * kPRowB];
-  __shared__ __attribute__((aligned(16))) char pl[kWaves][kAQ * kPRowB];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
   const int nqb = (a.Sq + kAQ * kWaves - 1) / (kAQ * kWaves);
@@ -286,9 +284,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
   f32x4 o[kAD / 16];
 #pragma unroll
   for (int d = 0; d < kAD / 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];  // per query row 4 g + r, base 2
-#pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = -INFINITY, l[r] = 0.f;
+  float m = -INFINITY, l = 0.f;  // query iw + li's running maximum and sum (base 2)
 
   // A block's K and V rows are loaded into registers one block ahead, so
   // that their transfer overlaps the previous block's products: thread tid
@@ -342,7 +338,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
     __syncthreads();
     if (t0 + kAKeys <= blk_last) load_block(t0 + kAKeys);  // in flight during this block's products
 
-    // S = Q K^T for keys t0 + 16 nt + li (lane) and queries iw + 4 g + r
+    // S^T = K Q^T: K rows are the A operand (LDS), the wave's queries the B
+    // operand (registers), so lane (li, g) gets query iw + li's scores for
+    // keys t0 + 16 nt + 4 g + r.  Those are exactly PV's A operand (P, row li)
+    // in the key order the transposing V reads use, so P stays in registers.
     f32x4 sc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -352,65 +351,62 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
 #pragma unroll
       for (int ks = 0; ks < kAD / 32; ++ks) {
         const bf16x8 bh = lds_b8(krh + 64 * ks), bl = lds_b8(krl + 64 * ks);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[ks], bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[ks], bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, qh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, qh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, ql[ks], acc, 0, 0, 0);
       }
       sc[nt] = acc;
     }
-    float pv[2][4], alpha[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int last = L - a.Sq + iw + 4 * g + r;  // query's last visible key
-      float s0 = t0 + li <= last ? sc[0][r] * a.scale_log2 : -INFINITY;
-      float s1 = t0 + 16 + li <= last ? sc[1][r] * a.scale_log2 : -INFINITY;
-      float mx = fmaxf(s0, s1);
-      mx = mfma::max_in_row(mx);
-      const float m_new = fmaxf(m[r], mx);
-      float al = 1.f, p0 = 0.f, p1 = 0.f;
-      if (m_new != -INFINITY) {
-        al = m[r] == -INFINITY ? 0.f : exp2f(m[r] - m_new);
-        p0 = s0 == -INFINITY ? 0.f : exp2f(s0 - m_new);
-        p1 = s1 == -INFINITY ? 0.f : exp2f(s1 - m_new);
-      }
-      float ps = p0 + p1;
-      ps = mfma::sum_in_row(ps);
-      l[r] = l[r] * al + ps;
-      m[r] = m_new;
-      alpha[r] = al;
-      pv[0][r] = p0;
-      pv[1][r] = p1;
-    }
-    // P (hi, lo) into the wave's tile: row 4 g + r, keys li and 16 + li
+    // Online softmax of query iw + li (base 2; every lane group holds the
+    // query's m and l, the reductions run over the 4 groups).
+    const int last = L - a.Sq + iw + li;  // the query's last visible key
+    float sv[2][4], mx = -INFINITY;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t hb = f32_to_bf16_bits(pv[nt][r]);
-        const uint32_t lb = f32_to_bf16_bits(pv[nt][r] - __uint_as_float(hb << 16));
-        const int off = (4 * g + r) * kPRowB + 2 * (16 * nt + li);
-        *reinterpret_cast<uint16_t*>(ph[wave] + off) = (uint16_t)hb;
-        *reinterpret_cast<uint16_t*>(pl[wave] + off) = (uint16_t)lb;
+        sv[nt][r] = t0 + 16 * nt + 4 * g + r <= last ? sc[nt][r] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[nt][r]);
       }
+    mx = mfma::max_over_rows(mx);
+    const float m_new = fmaxf(m, mx);
+    float al = 1.f, ps = 0.f;
+    uint32_t pkh[4], pkl[4];
 #pragma unroll
-    for (int d = 0; d < kAD / 16; ++d)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[d][r] *= alpha[r];
-    __syncthreads();  // P tiles written
+      for (int r = 0; r < 4; r += 2) {
+        float e0 = 0.f, e1 = 0.f;
+        if (m_new != -INFINITY) {
+          e0 = sv[nt][r] == -INFINITY ? 0.f : exp2f(sv[nt][r] - m_new);
+          e1 = sv[nt][r + 1] == -INFINITY ? 0.f : exp2f(sv[nt][r + 1] - m_new);
+        }
+        ps += e0 + e1;
+        split_bf16x2(e0, e1, pkh[2 * nt + r / 2], pkl[2 * nt + r / 2]);
+      }
+    if (m_new != -INFINITY) al = m == -INFINITY ? 0.f : exp2f(m - m_new);
+    ps = mfma::sum_over_rows(ps);
+    l = l * al + ps;
+    m = m_new;
+    // O's rows are queries 4 g + r: their rescale factors come from lanes
+    // 4 g + r (only when some query's maximum moved).
+    if (__any(al != 1.f)) {
+      float alr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) alr[r] = __shfl(al, 4 * g + r);
+#pragma unroll
+      for (int d = 0; d < kAD / 16; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[d][r] *= alr[r];
+    }
+    const bf16x8 pah = __builtin_bit_cast(bf16x8, make_uint4(pkh[0], pkh[1], pkh[2], pkh[3]));
+    const bf16x8 pal = __builtin_bit_cast(bf16x8, make_uint4(pkl[0], pkl[1], pkl[2], pkl[3]));
 
     // O += P V.  B operand of column block d: V is key-major in LDS and read
     // transposed (ds_read_b64_tr_b16): lane li of group g reads the 4 values
     // of row 4 g + li / 4 (and 16 rows on), columns 16 d + 4 (li % 4) .. + 3,
     // and the 16-lane transpose hands it column 16 d + li of keys 4 g .. 4 g + 3
-    // and 16 + 4 g .. 16 + 4 g + 3.  The A operand (P, row li) takes its
-    // keys in the same order.
-    auto p8 = [&](const char* t) {
-      const uint2 x0 = *reinterpret_cast<const uint2*>(t + li * kPRowB + 8 * g);
-      const uint2 x1 = *reinterpret_cast<const uint2*>(t + li * kPRowB + 32 + 8 * g);
-      return __builtin_bit_cast(bf16x8, make_uint4(x0.x, x0.y, x1.x, x1.y));
-    };
-    const bf16x8 pah = p8(ph[wave]);
-    const bf16x8 pal = p8(pl[wave]);
+    // and 16 + 4 g .. 16 + 4 g + 3: the order of P's keys above.
     const int vrow = 4 * g + (li >> 2), vcol = 8 * (li & 3);  // bytes within the column block
     auto v8 = [&](const char* t, int d) {
       const char* p0 = t + vrow * kVRowB + 32 * d + vcol;
@@ -431,12 +427,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
 
   // out[query iw + 4 g + r][16 d + li] = O / l and its lse (lane li = 0);
   // with several splits, this split's normalised partial and lse instead.
+  // Query q's m and l live in lane q (every group).
+  const float inv_q = l > 0.f ? 1.f / l : 0.f;
+  const float ls_q = l > 0.f ? (m + log2f(l)) * 0.693147180559945309f : -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = iw + 4 * g + r;
+    const float inv = __shfl(inv_q, 4 * g + r);
+    const float ls = __shfl(ls_q, 4 * g + r);
     if (i >= a.Sq) continue;
-    const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
-    const float ls = l[r] > 0.f ? (m[r] + log2f(l[r])) * 0.693147180559945309f : -INFINITY;
     const int64_t row = ((int64_t)b * a.Sq + i) * a.H + h;
     if (a.splits == 1) {
       float* dst = a.out + row * a.dv;
