@@ -342,20 +342,38 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
     // operand (registers), so lane (li, g) gets query iw + li's scores for
     // keys t0 + 16 nt + 4 g + r.  Those are exactly PV's A operand (P, row li)
     // in the key order the transposing V reads use, so P stays in registers.
-    f32x4 sc[2];
+    // The two key halves' products alternate (two independent accumulation
+    // chains), and each k-step's K operands are read two steps ahead.
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      constexpr int kAhead = 2;
+      const char* krh[2] = {kh + li * kKRowB + 16 * g, kh + (16 + li) * kKRowB + 16 * g};
+      const char* krl[2] = {kl + li * kKRowB + 16 * g, kl + (16 + li) * kKRowB + 16 * g};
+      bf16x8 kbh[kAhead][2], kbl[kAhead][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      const char* krh = kh + (16 * nt + li) * kKRowB + 16 * g;
-      const char* krl = kl + (16 * nt + li) * kKRowB + 16 * g;
+      for (int k = 0; k < kAhead; ++k)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) kbh[k][nt] = lds_b8(krh[nt] + 64 * k), kbl[k][nt] = lds_b8(krl[nt] + 64 * k);
 #pragma unroll
       for (int ks = 0; ks < kAD / 32; ++ks) {
-        const bf16x8 bh = lds_b8(krh + 64 * ks), bl = lds_b8(krl + 64 * ks);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, qh[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, qh[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, ql[ks], acc, 0, 0, 0);
+        bf16x8 bh[2], bl[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) bh[nt] = kbh[ks % kAhead][nt], bl[nt] = kbl[ks % kAhead][nt];
+        if (ks + kAhead < kAD / 32) {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            kbh[ks % kAhead][nt] = lds_b8(krh[nt] + 64 * (ks + kAhead));
+            kbl[ks % kAhead][nt] = lds_b8(krl[nt] + 64 * (ks + kAhead));
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[nt], qh[ks], sc[nt], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[nt], qh[ks], sc[nt], 0, 0, 0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[nt], ql[ks], sc[nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sc[nt] = acc;
     }
     // Online softmax of query iw + li (base 2; every lane group holds the
     // query's m and l, the reductions run over the 4 groups).
@@ -378,13 +396,13 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       for (int r = 0; r < 4; r += 2) {
         float e0 = 0.f, e1 = 0.f;
         if (m_new != -INFINITY) {
-          e0 = sv[nt][r] == -INFINITY ? 0.f : exp2f(sv[nt][r] - m_new);
-          e1 = sv[nt][r + 1] == -INFINITY ? 0.f : exp2f(sv[nt][r + 1] - m_new);
+          e0 = sv[nt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[nt][r] - m_new);
+          e1 = sv[nt][r + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[nt][r + 1] - m_new);
         }
         ps += e0 + e1;
         split_bf16x2(e0, e1, pkh[2 * nt + r / 2], pkl[2 * nt + r / 2]);
       }
-    if (m_new != -INFINITY) al = m == -INFINITY ? 0.f : exp2f(m - m_new);
+    if (m_new != -INFINITY) al = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
     ps = mfma::sum_over_rows(ps);
     l = l * al + ps;
     m = m_new;
@@ -415,13 +433,19 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       const mfma::bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p0 + 16 * kVRowB));
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
+    // (V operands read two column blocks ahead)
+    constexpr int kVAhead = 2;
+    bf16x8 vbh[kVAhead], vbl[kVAhead];
+#pragma unroll
+    for (int d = 0; d < kVAhead; ++d) vbh[d] = v8(vh_t, d), vbl[d] = v8(vl_t, d);
 #pragma unroll
     for (int d = 0; d < kAD / 16; ++d) {
-      const bf16x8 vh = v8(vh_t, d);
-      const bf16x8 vl = v8(vl_t, d);
+      const bf16x8 vh = vbh[d % kVAhead], vl = vbl[d % kVAhead];
+      if (d + kVAhead < kAD / 16) vbh[d % kVAhead] = v8(vh_t, d + kVAhead), vbl[d % kVAhead] = v8(vl_t, d + kVAhead);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vh, o[d], 0, 0, 0);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pah, vl, o[d], 0, 0, 0);
       o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pal, vh, o[d], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
