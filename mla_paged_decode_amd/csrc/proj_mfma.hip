@@ -262,7 +262,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void out_proj_mfma_kernel
         }
       }
       __syncthreads();
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      // hi and lo products in two accumulation chains, added at the end
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, acl = f32x4{0.f, 0.f, 0.f, 0.f};
       const char* arow = o_tile + li * kRow + 32 * g;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -275,8 +276,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void out_proj_mfma_kernel
         const bf16x8 ah = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
         const bf16x8 al = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, wb[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[ks], acc, 0, 0, 0);
+        acl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, wb[ks], acl, 0, 0, 0);
       }
+      acc += acl;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int nn = nb + 4 * g + i;
