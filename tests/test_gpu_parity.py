@@ -389,15 +389,17 @@ def test_page_layout_invariance_and_determinism(kernel):
 # ---------------------------------------------- full-size workloads --
 
 FULL = [
-    # (workload, split mode, sequences checked against the oracle); every
-    # head of every checked sequence is compared.  The long-context workload
-    # runs both in its literal 32 chunks and in the balanced mode the
-    # benchmark times.
-    ("glm_b32_h20_ctx4096_bf16", 0, list(range(32))),
-    ("long_b4_h20_ctx65k_203k_bf16", 0, [0, 1, 2, 3]),
-    ("long_b4_h20_ctx65k_203k_bf16", 32, [0, 1, 2, 3]),
-    ("ragged_b256_h20_ctx512_8k_bf16", 0, list(range(0, 256, 8)) + [255]),
-    ("fp8_mtp4_b64_h20_ctx16k", 0, list(range(0, 64, 8)) + [63]),
+    # (workload, split mode, sequences checked against the oracle, changes to
+    # the workload); every head of every checked sequence is compared.  The
+    # long-context workload runs both in its literal 32 chunks and in the
+    # balanced mode the benchmark times; the fp8 batch also runs with one
+    # query token per sequence (two row blocks on the MX kernel).
+    ("glm_b32_h20_ctx4096_bf16", 0, list(range(32)), {}),
+    ("long_b4_h20_ctx65k_203k_bf16", 0, [0, 1, 2, 3], {}),
+    ("long_b4_h20_ctx65k_203k_bf16", 32, [0, 1, 2, 3], {}),
+    ("ragged_b256_h20_ctx512_8k_bf16", 0, list(range(0, 256, 8)) + [255], {}),
+    ("fp8_mtp4_b64_h20_ctx16k", 0, list(range(0, 64, 8)) + [63], {}),
+    ("fp8_mtp4_b64_h20_ctx16k", 0, list(range(0, 64, 8)) + [63], {"q_per_seq": 1}),
 ]
 
 # Bound of the opt-in single-bf16 query mode on bf16 caches (the library
@@ -409,28 +411,28 @@ TAU_BF16_QUERIES = 2e-2
 _full_refs = {}
 
 
-def full_reference(name, seqs):
+def full_reference(name, seqs, over):
     """The oracle's result for the checked sequences of a full-size workload,
     computed once per workload and kept for the other kernel and split
     variants (the unabsorbed definition at these sizes takes up to ~30 s)."""
-    key = (name, tuple(seqs))
+    key = (name, tuple(seqs), tuple(sorted(over.items())))
     if key not in _full_refs:
-        inp = make_inputs(WORKLOADS[name])
+        inp = make_inputs(WORKLOADS[name].with_(**over))
         _full_refs[key] = oracle.mla_decode(inp, seqs=seqs)
     return _full_refs[key]
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("kernel,q_abs", [(SIMT, "f32"), (MFMA, "f32"), (MFMA, "bf16")])
-@pytest.mark.parametrize("name,splits,seqs", FULL)
-def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
+@pytest.mark.parametrize("name,splits,seqs,over", FULL)
+def test_full_size_sampled(kernel, q_abs, name, splits, seqs, over):
     """The whole step at full size, in the launch configuration the benchmark
     times (matrix-core kernel, balanced split mode, fp32 absorbed queries for
     bf16 caches and bf16 ones for the fp8 cache), plus the vector-ALU kernel
     and the workloads' literal split counts."""
     import mla_paged_decode_amd as mla
     from mla_paged_decode_amd import MLA_BF16, MLA_F32
-    wl = WORKLOADS[name]
+    wl = WORKLOADS[name].with_(**over)
     if refused(kernel, wl, MLA_F32 if q_abs == "f32" else MLA_BF16):
         return
     flags = 0
@@ -442,7 +444,7 @@ def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
             run_step(small, kernel=kernel, num_splits=splits, q_abs_dtype=MLA_BF16)
         assert "MLA_DECODE_ALLOW_BF16_QUERIES" in ei.value.message
         flags, tau = mla.MLA_DECODE_ALLOW_BF16_QUERIES, TAU_BF16_QUERIES
-    say(f"[full] {name} kernel={kernel} q_abs={q_abs} splits={splits}")
+    say(f"[full] {name} {over} kernel={kernel} q_abs={q_abs} splits={splits}")
     inp = make_inputs(wl)
     mla.mla_validate_tables(inp.seq_lens, inp.block_table, inp.kv_pool.shape[0], wl.page_block)
     qd = MLA_F32 if q_abs == "f32" else MLA_BF16
@@ -451,7 +453,7 @@ def test_full_size_sampled(kernel, q_abs, name, splits, seqs):
     lse = step.lse.cpu().numpy()
     del step, inp
     assert np.isfinite(out).all()
-    ref, ref_lse = full_reference(name, seqs)
+    ref, ref_lse = full_reference(name, seqs, over)
     rows = [b * wl.q_per_seq + j for b in seqs for j in range(wl.q_per_seq)]
     err = rel_err(out[rows], ref[rows])
     say(f"  rel err {err:.3e} (tau {tau})")
