@@ -36,10 +36,10 @@ e8m0 scale per 32 values (model record "GLM-4.7-Flash", ENGINE KERNEL
 CONSTRAINTS item (2): 528 bytes per token).  Decoded value = e4m3fn(code) *
 2^(E - 127), with both codes decoded below from their format definitions.
 
-Parity pins live in tests/test_oracle_pins.py.  Absolute output values are
-"parity unpinned" in the sense that the pages print no numeric MLA output; the
-function is pinned by closed forms, invariances and a reduction to a library
-attention routine instead.
+Parity pins live in tests/test_oracle_pins.py.  The pages print no numeric
+MLA output for any input, so no stored value comes from them; the function is
+pinned by closed forms, invariances, brute force on tiny inputs and a
+reduction to a library attention routine.
 """
 from __future__ import annotations
 
