@@ -3,12 +3,17 @@
 //   [k_t ; v_t] = W[h] c_t,   W[h] = [W_UK[h] ; W_UV[h]]  ((d_nope + d_v) x d_latent),
 // as v_mfma_f32_16x16x32_bf16 products with fp32 accumulation.
 //
-// Workgroup = 4 waves over one (sequence, head), 64 output rows of W[h]
-// (16 per wave, held in registers as the B operand for the whole
-// workgroup) and up to 8 blocks of 16 tokens.  Per block the latent rows
-// are decoded from the cache row into a bf16 tile in LDS (the A operand).
-// bf16, fp8 and fp4 latents are exact in bf16; an f32 latent is split into
-// bf16 hi + lo parts, two products per k-step, as the fp32 projections do.
+// Two kernels.  prefill_expand_gemm_kernel (bf16 cache, 512-wide latent,
+// d_nope + d_v a multiple of 64 up to 448) tiles the product as a GEMM over
+// 128 tokens x all output rows; it is defined further down.  Otherwise
+// prefill_expand_mfma_kernel: a workgroup of 4 waves over one (sequence,
+// head), 64 output rows of W[h] (16 per wave, held in registers as the B
+// operand for the whole workgroup) and up to 8 blocks of 16 tokens.  Per
+// block the latent rows are decoded from the cache row into a bf16 tile in
+// LDS (the A operand).  bf16, fp8 and fp4 latents are exact in bf16; an f32
+// latent is split into bf16 hi + lo parts, two products per k-step, as the
+// fp32 projections do.  Both accumulate over the latent in the same order,
+// so on a bf16 cache they give the same bits.
 #include <algorithm>
 #include <cmath>
 
@@ -222,6 +227,141 @@ constexpr int kVRowB = kAD * 2 + 32;      // V tile row stride (bytes): 4 rows l
 __device__ __forceinline__ bf16x8 lds_b8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
+
+// The rebuild for a bf16 cache with a 512-wide latent, tiled as a GEMM per
+// (sequence, head): a workgroup of 8 waves computes 128 tokens x all
+// N = d_nope + d_v output rows of W[h], so each latent row is read once per
+// head (the kernel above reads it once per 64 output rows) and W[h] once per
+// 128 tokens.  K = d_latent goes in chunks of 64: the chunk's latent rows
+// (128 x 64) and W rows (N x 64) are staged in LDS (rows padded to 144 B, so
+// the 16 lanes of an operand read hit distinct banks), the next chunk's are
+// loaded into registers meanwhile.  Wave w takes tokens 64 (w % 2) .. +63
+// (four 16-row blocks) and output rows (w / 2) N / 4 .. +N / 4 (NCB 16-row
+// blocks).  XCD-aware order: the tiles of one (sequence, head) are
+// consecutive on one XCD, which keeps W[h] in its L2.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t gemm_u4;  // a native vector, kept in registers
+constexpr int kGTok = 128;              // tokens per workgroup
+constexpr int kGKc = 64;                // K chunk
+constexpr int kGRowB = kGKc * 2 + 16;   // LDS row stride (bytes)
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+
+template <int NCB>  // 16-row blocks of W per wave: N = 64 NCB
+__global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillArgs a, int tiles) {
+  constexpr int N = 64 * NCB;
+  constexpr int kDc = 512;
+  constexpr int kChunks = kDc / kGKc;
+  constexpr int kAUnits = kGTok * (kGKc / 8);               // 16-B units of a latent chunk
+  constexpr int kWUnits = N * (kGKc / 8);                   // ... of a W chunk
+  static_assert(kAUnits == 2 * kGThreads, "two latent units per thread");
+  constexpr int kWPer = kWUnits / kGThreads;
+  static_assert(kAUnits % kGThreads == 0 && kWUnits % kGThreads == 0, "staging");
+  __shared__ __attribute__((aligned(16))) char a_tile[kGTok * kGRowB];
+  __shared__ __attribute__((aligned(16))) char w_tile[N * kGRowB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
+  const int x8 = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int u = 8 * (k / tiles) + x8;  // (sequence, head) unit
+  if (u >= a.B * a.H) return;
+  const int b = u / a.H, h = u % a.H;
+  const int L = (int)min((int64_t)max(a.seq_lens[b], 0), a.Lcap);
+  const int t0 = (k % tiles) * kGTok;
+  if (t0 >= L) return;  // uniform
+
+  // Latent rows of this thread's staging units (tokens past L read the
+  // sequence's first row and are zeroed in LDS).
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+  auto row_of = [&](int un, uint32_t& m) __attribute__((always_inline)) {
+    const int t = t0 + un / (kGKc / 8);
+    m = t < L ? 0xffffffffu : 0u;
+    const int tt = t < L ? t : 0;
+    return a.pool + ((int64_t)bt[tt / a.P] * a.P + (tt & (a.P - 1))) * a.row_bytes + 16 * (un % (kGKc / 8));
+  };
+  uint32_t am0, am1;
+  const uint8_t* const arow0 = row_of(tid, am0);
+  const uint8_t* const arow1 = row_of(tid + kGThreads, am1);
+  const uint16_t* wh = static_cast<const uint16_t*>(a.w) + (int64_t)h * (a.dn + a.dv) * kDc;
+  gemm_u4 ra0, ra1, rw[kWPer];
+  // The shared RoPE keys, once per token (head 0).
+  if (h == 0)
+    for (int idx = tid; idx < kGTok * a.dr; idx += kGThreads) {
+      const int r = idx / a.dr, i = idx % a.dr, t = t0 + r;
+      if (t < L) {
+        const uint8_t* row = a.pool + ((int64_t)bt[t / a.P] * a.P + (t & (a.P - 1))) * a.row_bytes;
+        a.kr[((int64_t)b * a.Lcap + t) * a.dr + i] =
+            bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[kDc + i]);
+      }
+    }
+
+  const int th = wave & 1, cq = wave >> 1;
+  f32x4 acc[4][NCB];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  ra0 = *reinterpret_cast<const gemm_u4*>(arow0);
+  ra1 = *reinterpret_cast<const gemm_u4*>(arow1);
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) {
+    const int un = tid + kGThreads * j;
+    rw[j] = *reinterpret_cast<const gemm_u4*>(wh + (int64_t)(un / (kGKc / 8)) * kDc + 8 * (un % (kGKc / 8)));
+  }
+  for (int c = 0; c < kChunks; ++c) {
+    if (c > 0) __syncthreads();  // the previous chunk's readers are done
+    {  // tokens past L are zeros
+      const int u0 = tid, u1 = tid + kGThreads;
+      *reinterpret_cast<gemm_u4*>(a_tile + (u0 / (kGKc / 8)) * kGRowB + 16 * (u0 % (kGKc / 8))) = ra0 & am0;
+      *reinterpret_cast<gemm_u4*>(a_tile + (u1 / (kGKc / 8)) * kGRowB + 16 * (u1 % (kGKc / 8))) = ra1 & am1;
+    }
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const int un = tid + kGThreads * j;  // kWUnits is a multiple of the thread count
+      *reinterpret_cast<gemm_u4*>(w_tile + (un / (kGKc / 8)) * kGRowB + 16 * (un % (kGKc / 8))) = rw[j];
+    }
+    __syncthreads();
+    if (c + 1 < kChunks) {  // the next chunk is in flight during this chunk's products
+      ra0 = *reinterpret_cast<const gemm_u4*>(arow0 + 2 * kGKc * (c + 1));
+      ra1 = *reinterpret_cast<const gemm_u4*>(arow1 + 2 * kGKc * (c + 1));
+#pragma unroll
+      for (int j = 0; j < kWPer; ++j) {
+        const int un = tid + kGThreads * j;
+        rw[j] = *reinterpret_cast<const gemm_u4*>(wh + (int64_t)(un / (kGKc / 8)) * kDc + kGKc * (c + 1) +
+                                                8 * (un % (kGKc / 8)));
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < kGKc / 32; ++ks) {
+      bf16x8 av[4], bv[NCB];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        av[r] = lds_b8(a_tile + (64 * th + 16 * r + li) * kGRowB + 64 * ks + 16 * g);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        bv[cb] = lds_b8(w_tile + (N / 4 * cq + 16 * cb + li) * kGRowB + 64 * ks + 16 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[r], bv[cb], acc[r][cb], 0, 0, 0);
+    }
+  }
+  // C layout: lane (li, g) holds output row (of W) 16 cb + li for tokens 4g .. 4g + 3.
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 64 * th + 16 * r + 4 * g + i;
+      if (t >= L) continue;
+      const int64_t tok = ((int64_t)b * a.Lcap + t) * a.H + h;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int n = N / 4 * cq + 16 * cb + li;
+        if (n < a.dn) a.kn[tok * a.dn + n] = acc[r][cb][i];
+        else a.v[tok * a.dv + (n - a.dn)] = acc[r][cb][i];
+      }
+    }
+}
+
 
 __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char kh[kAKeys * kKRowB];
@@ -552,6 +692,20 @@ bool prefill_expand_mfma_supported(const PrefillArgs& a) {
 
 hipError_t launch_prefill_expand_mfma(const PrefillArgs& a, int fmt, hipStream_t s) {
   if (!prefill_expand_mfma_supported(a)) return hipErrorInvalidValue;
+  const int n = a.dn + a.dv;
+  if (fmt == kBF16 && a.dc == 512 && a.dr % 4 == 0 && n % 64 == 0 && n / 64 >= 1 && n / 64 <= 7) {
+    const int64_t tiles = (a.Lcap + kGTok - 1) / kGTok;
+    const int64_t units = (int64_t)a.B * a.H;
+    const int64_t grid = 8 * tiles * ((units + 7) / 8);
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    switch (n / 64) {
+#define MLA_CASE(K) \
+  case K: prefill_expand_gemm_kernel<K><<<dim3((unsigned)grid), kGThreads, 0, s>>>(a, (int)tiles); break;
+      MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7)
+#undef MLA_CASE
+    }
+    return hipGetLastError();
+  }
   switch (fmt) {
     case kF32: return launch_fmt<kF32>(a, s);
     case kBF16: return launch_fmt<kBF16>(a, s);
