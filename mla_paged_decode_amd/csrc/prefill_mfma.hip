@@ -154,6 +154,31 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_expand_mfma_kernel(Prefil
         const uint8_t* row = a.pool + ((int64_t)page * a.P + (t % a.P)) * a.row_bytes;
         if constexpr (FMT == kBF16) {
           hv = *reinterpret_cast<const uint4*>(row + 16 * c8);
+        } else if constexpr (FMT == kFP8) {
+          // 8 e4m3 codes and their block's e8m0 scale: one scaled conversion
+          // per pair, exact in bf16 (the decode kernels use the same one)
+          const uint2 raw = *reinterpret_cast<const uint2*>(row + 8 * c8);
+          const float sc = e8m0_to_f32(row[nv + c8 / 4]);
+          hv = make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, sc, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, sc, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, sc, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, sc, true)));
+        } else if constexpr (FMT == kFP4) {
+          // 8 e2m1 codes (value 2i in the low nibble of byte i) and their
+          // block's e4m3 scale: an e2m1 value times an e4m3 scale has at most
+          // 6 significant bits, so the bf16 value is the upper half of the
+          // exact fp32 product
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * c8);
+          const float sc = e4m3fn_to_f32(row[nv / 2 + c8 / 2]);
+          const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+          const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+          const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+          const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+          auto hi2 = [&](float x0, float x1) {
+            return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, x1 * sc), __builtin_bit_cast(uint32_t, x0 * sc),
+                                         0x07060302u);
+          };
+          hv = make_uint4(hi2(p0[0], p0[1]), hi2(p1[0], p1[1]), hi2(p2[0], p2[1]), hi2(p3[0], p3[1]));
         } else {
           float x[8];
 #pragma unroll
