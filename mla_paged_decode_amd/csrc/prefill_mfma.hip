@@ -243,6 +243,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_expand_mfma_kernel(Prefil
 //   online softmax per query (lane li = query, 8 keys per lane);
 //   O += P V with P from registers (the S^T layout is PV's A layout) and V
 //   read from its key-major LDS tile with transposing loads.
+// Two workgroups share a CU (69 KB of LDS and at most 256 registers each),
+// so that each SIMD has a second wave to run while the first one waits.
 constexpr int kAQ = 16;        // queries per wave
 constexpr int kAKeys = 32;     // keys per block
 constexpr int kAD = 256;       // key and value width
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillA
 }
 
 
-__global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void prefill_attn_mfma_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char kh[kAKeys * kKRowB];
   __shared__ __attribute__((aligned(16))) char kl[kAKeys * kKRowB];
   __shared__ __attribute__((aligned(16))) char vh_t[kAKeys * kVRowB];
@@ -508,10 +510,10 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
     // keys t0 + 16 nt + 4 g + r.  Those are exactly PV's A operand (P, row li)
     // in the key order the transposing V reads use, so P stays in registers.
     // The two key halves' products alternate (two independent accumulation
-    // chains), and each k-step's K operands are read two steps ahead.
+    // chains), and each k-step's K operands are read one step ahead.
     f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     {
-      constexpr int kAhead = 2;
+      constexpr int kAhead = 1;
       const char* krh[2] = {kh + li * kKRowB + 16 * g, kh + (16 + li) * kKRowB + 16 * g};
       const char* krl[2] = {kl + li * kKRowB + 16 * g, kl + (16 + li) * kKRowB + 16 * g};
       bf16x8 kbh[kAhead][2], kbl[kAhead][2];
@@ -598,8 +600,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_mfma_kernel(PrefillA
       const mfma::bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p0 + 16 * kVRowB));
       return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    // (V operands read two column blocks ahead)
-    constexpr int kVAhead = 2;
+    // (V operands read one column block ahead)
+    constexpr int kVAhead = 1;
     bf16x8 vbh[kVAhead], vbl[kVAhead];
 #pragma unroll
     for (int d = 0; d < kVAhead; ++d) vbh[d] = v8(vh_t, d), vbl[d] = v8(vl_t, d);
@@ -680,9 +682,12 @@ bool prefill_attn_mfma_supported(const PrefillArgs& a) {
   return a.dn + a.dr == kAD && a.dv == kAD && a.dn % 4 == 0;
 }
 
-// One 85-KB workgroup per CU: 256 run at once on MI355X.  The split count
-// minimises the rounds of the grid per unit of work (ties go to fewer
-// splits), with at least 128 keys of capacity per split.
+// The split count minimises the rounds of the grid per unit of work over
+// 256 slots (ties go to fewer splits), with at least 128 keys of capacity
+// per split.  Two workgroups run per CU (512 at once on MI355X), but the
+// per-split costs (partials, the merge) make a 256-slot model pick better
+// on the benchmark's chunks: 4 splits of 4 x 4,096 keys measured 933-937 us
+// for the call, against 995-1,002 us with 2 and 963-982 us with 8.
 int prefill_attn_splits(int B, int Sq, int H, int64_t Lcap, int dn, int dr, int dv) {
   if (dn + dr != kAD || dv != kAD || dn % 4) return 1;
   constexpr int kSlots = 256;
