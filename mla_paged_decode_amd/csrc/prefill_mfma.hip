@@ -3,8 +3,9 @@
 //   [k_t ; v_t] = W[h] c_t,   W[h] = [W_UK[h] ; W_UV[h]]  ((d_nope + d_v) x d_latent),
 // as v_mfma_f32_16x16x32_bf16 products with fp32 accumulation.
 //
-// Two kernels.  prefill_expand_gemm_kernel (bf16 cache, 512-wide latent,
-// d_nope + d_v a multiple of 64 up to 448) tiles the product as a GEMM over
+// Two kernels.  prefill_expand_gemm_kernel (bf16 cache with a 512-wide
+// latent or fp8 cache with a 448-wide one, d_nope + d_v a multiple of 64 up
+// to 448) tiles the product as a GEMM over
 // 128 tokens x all output rows; it is defined further down.  Otherwise
 // prefill_expand_mfma_kernel: a workgroup of 4 waves over one (sequence,
 // head), 64 output rows of W[h] (16 per wave, held in registers as the B
@@ -255,7 +256,8 @@ __device__ __forceinline__ bf16x8 lds_b8(const char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-// The rebuild for a bf16 cache with a 512-wide latent, tiled as a GEMM per
+// The rebuild for a bf16 cache with a 512-wide latent (or an fp8 cache with
+// a 448-wide one, decoded exactly to bf16 when staged), tiled as a GEMM per
 // (sequence, head): a workgroup of 8 waves computes 128 tokens x all
 // N = d_nope + d_v output rows of W[h], so each latent row is read once per
 // head (the kernel above reads it once per 64 output rows) and W[h] once per
@@ -273,10 +275,12 @@ constexpr int kGRowB = kGKc * 2 + 16;   // LDS row stride (bytes)
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
 
-template <int NCB>  // 16-row blocks of W per wave: N = 64 NCB
+template <int FMT, int NCB>  // bf16 or fp8 rows; 16-row blocks of W per wave: N = 64 NCB
 __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillArgs a, int tiles) {
+  static_assert(FMT == kBF16 || FMT == kFP8, "row formats");
   constexpr int N = 64 * NCB;
-  constexpr int kDc = 512;
+  constexpr int kDc = FMT == kBF16 ? 512 : 448;  // the latent width of the row format
+  constexpr int kVB = FMT == kBF16 ? 2 : 1;      // stored bytes per value
   constexpr int kChunks = kDc / kGKc;
   constexpr int kAUnits = kGTok * (kGKc / 8);               // 16-B units of a latent chunk
   constexpr int kWUnits = N * (kGKc / 8);                   // ... of a W chunk
@@ -295,28 +299,58 @@ __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillA
   const int t0 = (k % tiles) * kGTok;
   if (t0 >= L) return;  // uniform
 
-  // Latent rows of this thread's staging units (tokens past L read the
-  // sequence's first row and are zeroed in LDS).
+  // Latent rows of this thread's two staging units: tokens t0 + tid / 8 and
+  // 64 more, values 8 (tid % 8) .. + 7 of each chunk (tokens past L read the
+  // sequence's first row and are zeroed in LDS).  fp8 values are decoded
+  // exactly to bf16 when staged, with their block's e8m0 scale.
   const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks;
+  const int u8 = tid % (kGKc / 8);
   auto row_of = [&](int un, uint32_t& m) __attribute__((always_inline)) {
     const int t = t0 + un / (kGKc / 8);
     m = t < L ? 0xffffffffu : 0u;
     const int tt = t < L ? t : 0;
-    return a.pool + ((int64_t)bt[tt / a.P] * a.P + (tt & (a.P - 1))) * a.row_bytes + 16 * (un % (kGKc / 8));
+    return a.pool + ((int64_t)bt[tt / a.P] * a.P + (tt & (a.P - 1))) * a.row_bytes;
   };
   uint32_t am0, am1;
   const uint8_t* const arow0 = row_of(tid, am0);
   const uint8_t* const arow1 = row_of(tid + kGThreads, am1);
   const uint16_t* wh = static_cast<const uint16_t*>(a.w) + (int64_t)h * (a.dn + a.dv) * kDc;
-  gemm_u4 ra0, ra1, rw[kWPer];
+  // A unit of chunk c: 8 values (16 B of bf16, or 8 fp8 codes and the scale
+  // code of their 32-value block).
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t gemm_u2;
+  struct AUnit {
+    gemm_u4 v;       // bf16
+    gemm_u2 q;       // fp8 codes
+    uint32_t sc;     // fp8 scale code
+  };
+  auto load_a = [&](const uint8_t* row, int c, AUnit& x) __attribute__((always_inline)) {
+    if constexpr (FMT == kBF16) {
+      x.v = *reinterpret_cast<const gemm_u4*>(row + kVB * (kGKc * c + 8 * u8));
+    } else {
+      x.q = *reinterpret_cast<const gemm_u2*>(row + kGKc * c + 8 * u8);
+      x.sc = row[a.dc + a.dr + (kGKc * c + 8 * u8) / 32];
+    }
+  };
+  auto bf16_of = [&](const AUnit& x) __attribute__((always_inline)) -> gemm_u4 {
+    if constexpr (FMT == kBF16) {
+      return x.v;
+    } else {
+      const float sc = e8m0_to_f32(x.sc);
+      return gemm_u4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.q[0], sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.q[0], sc, true)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.q[1], sc, false)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.q[1], sc, true))};
+    }
+  };
+  AUnit ra0, ra1;
+  gemm_u4 rw[kWPer];
   // The shared RoPE keys, once per token (head 0).
   if (h == 0)
     for (int idx = tid; idx < kGTok * a.dr; idx += kGThreads) {
       const int r = idx / a.dr, i = idx % a.dr, t = t0 + r;
       if (t < L) {
         const uint8_t* row = a.pool + ((int64_t)bt[t / a.P] * a.P + (t & (a.P - 1))) * a.row_bytes;
-        a.kr[((int64_t)b * a.Lcap + t) * a.dr + i] =
-            bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[kDc + i]);
+        a.kr[((int64_t)b * a.Lcap + t) * a.dr + i] = any_value<FMT>(row, kDc + i, kDc + a.dr);
       }
     }
 
@@ -326,8 +360,8 @@ __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillA
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < NCB; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  ra0 = *reinterpret_cast<const gemm_u4*>(arow0);
-  ra1 = *reinterpret_cast<const gemm_u4*>(arow1);
+  load_a(arow0, 0, ra0);
+  load_a(arow1, 0, ra1);
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     const int un = tid + kGThreads * j;
@@ -337,8 +371,8 @@ __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillA
     if (c > 0) __syncthreads();  // the previous chunk's readers are done
     {  // tokens past L are zeros
       const int u0 = tid, u1 = tid + kGThreads;
-      *reinterpret_cast<gemm_u4*>(a_tile + (u0 / (kGKc / 8)) * kGRowB + 16 * (u0 % (kGKc / 8))) = ra0 & am0;
-      *reinterpret_cast<gemm_u4*>(a_tile + (u1 / (kGKc / 8)) * kGRowB + 16 * (u1 % (kGKc / 8))) = ra1 & am1;
+      *reinterpret_cast<gemm_u4*>(a_tile + (u0 / (kGKc / 8)) * kGRowB + 16 * (u0 % (kGKc / 8))) = bf16_of(ra0) & am0;
+      *reinterpret_cast<gemm_u4*>(a_tile + (u1 / (kGKc / 8)) * kGRowB + 16 * (u1 % (kGKc / 8))) = bf16_of(ra1) & am1;
     }
 #pragma unroll
     for (int j = 0; j < kWPer; ++j) {
@@ -347,8 +381,8 @@ __global__ __launch_bounds__(kGThreads) void prefill_expand_gemm_kernel(PrefillA
     }
     __syncthreads();
     if (c + 1 < kChunks) {  // the next chunk is in flight during this chunk's products
-      ra0 = *reinterpret_cast<const gemm_u4*>(arow0 + 2 * kGKc * (c + 1));
-      ra1 = *reinterpret_cast<const gemm_u4*>(arow1 + 2 * kGKc * (c + 1));
+      load_a(arow0, c + 1, ra0);
+      load_a(arow1, c + 1, ra1);
 #pragma unroll
       for (int j = 0; j < kWPer; ++j) {
         const int un = tid + kGThreads * j;
@@ -723,14 +757,18 @@ bool prefill_expand_mfma_supported(const PrefillArgs& a) {
 hipError_t launch_prefill_expand_mfma(const PrefillArgs& a, int fmt, hipStream_t s) {
   if (!prefill_expand_mfma_supported(a)) return hipErrorInvalidValue;
   const int n = a.dn + a.dv;
-  if (fmt == kBF16 && a.dc == 512 && a.dr % 4 == 0 && n % 64 == 0 && n / 64 >= 1 && n / 64 <= 7) {
+  const bool gemm_rows = (fmt == kBF16 && a.dc == 512) || (fmt == kFP8 && a.dc == 448 && a.dr == 64);
+  if (gemm_rows && a.dr % 4 == 0 && n % 64 == 0 && n / 64 >= 1 && n / 64 <= 7) {
     const int64_t tiles = (a.Lcap + kGTok - 1) / kGTok;
     const int64_t units = (int64_t)a.B * a.H;
     const int64_t grid = 8 * tiles * ((units + 7) / 8);
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     switch (n / 64) {
-#define MLA_CASE(K) \
-  case K: prefill_expand_gemm_kernel<K><<<dim3((unsigned)grid), kGThreads, 0, s>>>(a, (int)tiles); break;
+#define MLA_CASE(K)                                                                                          \
+  case K:                                                                                                    \
+    if (fmt == kBF16) prefill_expand_gemm_kernel<kBF16, K><<<dim3((unsigned)grid), kGThreads, 0, s>>>(a, (int)tiles); \
+    else prefill_expand_gemm_kernel<kFP8, K><<<dim3((unsigned)grid), kGThreads, 0, s>>>(a, (int)tiles);              \
+    break;
       MLA_CASE(1) MLA_CASE(2) MLA_CASE(3) MLA_CASE(4) MLA_CASE(5) MLA_CASE(6) MLA_CASE(7)
 #undef MLA_CASE
     }
