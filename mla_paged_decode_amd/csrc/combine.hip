@@ -374,9 +374,14 @@ __global__ __launch_bounds__(64 * kStreamWaves) void combine_stream_kernel(Decod
   const int b = blockIdx.x, w = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, li = lane & 15;
   const int kdb = a.dc / 16;
-  const int d0 = (blockIdx.z * kStreamWaves + wave) * kStreamCols;  // first column block
-  const int r0 = 16 * w + 4 * g;                                    // this lane's first row
-  if (d0 >= kdb || r0 >= a.R) return;                               // no barriers below
+  // A last row block with at most four rows has data in lane group 0 only;
+  // there the four lane groups take four different sets of column blocks of
+  // those rows, so every lane of the wave loads.
+  const bool thin = a.R - 16 * w <= 4;
+  const int cell = blockIdx.z * kStreamWaves + wave;
+  const int d0 = (thin ? 4 * cell + g : cell) * kStreamCols;  // first column block
+  const int r0 = thin ? 16 * w : 16 * w + 4 * g;              // this lane's first row
+  if (d0 >= kdb || r0 >= a.R) return;                         // no barriers below
   const int nrow = min(4, a.R - r0);
   const bool lse4 = (a.R & 3) == 0;  // then nrow = 4 and every lane's four log-sum-exps are one aligned float4
 
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void combine_stream_kernel(Decod
   }
   const int row_blocks = (a.R + 15) / 16;
   const int64_t slot_stride = (int64_t)row_blocks * kdb * 256;
-  const float* po = a.part_o + ((int64_t)w * kdb + d0) * 256 + lane * 4;
+  const float* po = a.part_o + ((int64_t)w * kdb + d0) * 256 + (thin ? li : lane) * 4;
 
   float m[4], z[4], acc[kStreamCols][4];
 #pragma unroll
