@@ -51,11 +51,16 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
-// The grid is one-dimensional and every workgroup of head h lands on XCD
-// h % 8, so a head's weight slice and its tokens' inputs come from HBM once
-// and are then shared in that L2 by the head's token and column blocks (a
-// grid over (tokens, columns, heads) fetched them once per XCD that ran any
-// of them, up to 8 times).  XCDs with fewer heads get idle workgroups.
+// The grid is one-dimensional.  The H x col_groups (head, column group)
+// pairs are dealt to the XCDs in contiguous runs of equal length (XCD x takes
+// pairs [x U / 8, (x + 1) U / 8), U = H col_groups, a head's pairs being
+// consecutive), and an XCD's workgroups take its pairs one after another, the
+// token groups of a pair together.  A head's weight slice and its tokens'
+// inputs thus come from HBM once per XCD holding one of its pairs (one or
+// two XCDs once a run is at least a head long) and are then shared in that
+// L2, and no XCD holds more than ceil(U / 8) pairs.  (Whole heads per XCD,
+// head h on XCD h % 8, left 3 heads on some XCDs and 2 on others at 20
+// heads, and the launch took as long as the busiest XCD.)
 constexpr int kXcds = 8;
 struct ProjCell {
   int h, col_group, tok_group;
@@ -64,19 +69,21 @@ struct ProjCell {
 __device__ __forceinline__ ProjCell proj_cell(int col_groups, int tok_groups, int H) {
   const int L = blockIdx.x;
   const int x = L % kXcds, k = L / kXcds;
-  const int per_head = col_groups * tok_groups;
-  const int h = x + kXcds * (k / per_head), r = k % per_head;
-  return ProjCell{h, r % col_groups, r / col_groups, h < H};
+  const int U = H * col_groups;
+  const int u = x * U / kXcds + k / tok_groups;
+  return ProjCell{u / col_groups, u % col_groups, k % tok_groups, u < (x + 1) * U / kXcds};
 }
-// Grid size for proj_cell: 8 x (the most heads an XCD gets) x cells per head.
+// The most (head, column group) pairs an XCD holds.
+int pairs_per_xcd(int col_groups, int H) { return (H * col_groups + kXcds - 1) / kXcds; }
+// Grid size for proj_cell: 8 x (the most pairs an XCD holds) x token groups.
 unsigned proj_grid(int col_groups, int tok_groups, int H) {
-  return (unsigned)(kXcds * ((H + kXcds - 1) / kXcds) * col_groups * tok_groups);
+  return (unsigned)(kXcds * pairs_per_xcd(col_groups, H) * tok_groups);
 }
 // At most `per_cu` workgroups per CU on the busiest XCD (32 CUs): fewer,
-// larger token groups when the heads do not spread evenly over the XCDs.
+// larger token groups when an XCD holds many pairs.
 void cap_token_groups(ProjArgs& a, int col_groups, unsigned& gx, int per_cu) {
   const int nblk = (a.N + kTok - 1) / kTok;
-  const int cap = std::max(1, 32 * per_cu / (((a.H + kXcds - 1) / kXcds) * col_groups));
+  const int cap = std::max(1, 32 * per_cu / pairs_per_xcd(col_groups, a.H));
   if ((int)gx <= cap) return;
   a.tok_blocks = (nblk + cap - 1) / cap;
   gx = (unsigned)((nblk + a.tok_blocks - 1) / a.tok_blocks);

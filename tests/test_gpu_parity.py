@@ -197,6 +197,32 @@ def test_projections_partial_token_blocks(name, batch):
     assert e1 <= 1e-5 and e2 <= 1e-4
 
 
+@pytest.mark.parametrize("heads,batch", [(1, 40), (3, 40), (7, 100), (12, 256), (33, 30)])
+def test_projections_head_counts(heads, batch):
+    """The matrix-core projections deal (head, column group) pairs to the
+    eight XCDs in contiguous runs: head counts whose runs split a head over two
+    XCDs, give an XCD no pair (1 head, 4 column groups of out_proj), or part of
+    one head only."""
+    import mla_paged_decode_amd as mla
+    from mla_paged_decode_amd.step import DeviceBatch
+    wl = WORKLOADS["glm_b32_h20_ctx4096_bf16"].with_(batch=batch, heads=heads, lens=("const", 16))
+    say(f"[projections] heads={heads} tokens={wl.n_tokens}")
+    inp = make_inputs(wl)
+    dev = DeviceBatch.upload(inp)
+    N, H = wl.n_tokens, wl.heads
+    q_abs = torch.full((N, H, wl.d_latent + wl.d_rope), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_absorb_q(dev.dims, N, dev.q, dev.w_kv_b, q_abs)
+    o_lat = make_o_latent(wl)
+    out = torch.full((N, H, wl.d_v), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_out_proj(dev.dims, N, torch.from_numpy(o_lat).cuda(), dev.w_kv_b, out)
+    torch.cuda.synchronize()
+    w = oracle.to_f64(inp.w_kv_b, wl.w_dtype)
+    e1 = rel_err(q_abs.cpu().numpy(), oracle.absorb_q(oracle.to_f64(inp.q, wl.q_dtype), w, wl.d_nope))
+    e2 = rel_err(out.cpu().numpy(), oracle.out_proj(o_lat.astype(np.float64), w, wl.d_nope))
+    say(f"  rel err absorb {e1:.3e} out_proj {e2:.3e}")
+    assert e1 <= 1e-5 and e2 <= 1e-4
+
+
 @pytest.mark.parametrize("kernel", kernels())
 @pytest.mark.parametrize("name,lens", [
     ("tiny_b2_h4_f32", (37, 64)),
