@@ -27,7 +27,7 @@ _lib = None
 
 def build(verbose: bool = False) -> str:
     """Compile libmla_oracle.so with g++ (every call)."""
-    tmp = LIBRARY + ".tmp"
+    tmp = f"{LIBRARY}.{os.getpid()}.tmp"  # one per process: concurrent builds each rename a whole file
     r = subprocess.run(["g++", *FLAGS, SOURCE, "-o", tmp], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"g++ failed on {SOURCE}:\n{r.stderr}")
